@@ -1,0 +1,237 @@
+"""Python side of the CPU oracle (test infrastructure only).
+
+Thin ctypes marshalling over ``mixq_oracle.c`` plus the decode-step driver,
+which chains the oracle's steps in the order the MixQ article gives them
+(section "MixQ的解决方案": gate on the amax, re-detect only when it fires,
+concatenate the outlier channels in order, quantize, two products, fused
+dequantize/scale/add).  Arrays are NumPy; fp16 data is passed as its bit
+pattern.  Nothing here is imported by the product path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mixq_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
+          "-fPIC", "-shared", "-Wall", "-Wno-unknown-pragmas"]
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP over rows)."""
+    cmd = ["gcc", *CFLAGS, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def _bind(lib):
+    lib.orc_half_to_float.argtypes = [ctypes.c_uint16]
+    lib.orc_half_to_float.restype = ctypes.c_float
+    lib.orc_update_outlier_set.argtypes = [_P, _I64, _I64, _I64, ctypes.c_float, _I32, _P, _P]
+    lib.orc_update_outlier_set.restype = _I32
+    lib.orc_outlier_list.argtypes = [_P, _I64, _P]
+    lib.orc_outlier_list.restype = _I32
+    lib.orc_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64]
+    lib.orc_quantize_act.restype = None
+    lib.orc_quantize_weight.argtypes = [_P, _I64, _I64, ctypes.c_int, _P, _P]
+    lib.orc_quantize_weight.restype = None
+    lib.orc_gather_weight_cols.argtypes = [_P, _I64, _I64, _P, _P, _I64]
+    lib.orc_gather_weight_cols.restype = None
+    lib.orc_int_gemm.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+    lib.orc_int_gemm.restype = ctypes.c_int
+    lib.orc_output.argtypes = [_P, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]
+    lib.orc_output.restype = None
+    lib.orc_sampled_output.argtypes = [_P, _P, _I64, _P, _P, _P, _I64, _P, _I64, _I64,
+                                       _P, _P, _I64, _P, _P]
+    lib.orc_sampled_output.restype = ctypes.c_int
+    return lib
+
+
+_LIBS: dict[str, ctypes.CDLL] = {}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (building first if absent) an oracle library; cached per path."""
+    if path not in _LIBS:
+        if not os.path.exists(path):
+            if path != LIB_PATH:
+                raise FileNotFoundError(path)
+            build()
+        _LIBS[path] = _bind(ctypes.CDLL(path))
+    return _LIBS[path]
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    assert x.dtype == np.uint16
+    return np.ascontiguousarray(x)
+
+
+class Oracle:
+    """Oracle entry points over one loaded library (the default build, or a
+    deliberately altered copy in the tests that check the pins bite)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        self.lib = load(path)
+
+    # -- scalar helper -------------------------------------------------------
+    def half_to_float(self, bits: int) -> float:
+        return float(self.lib.orc_half_to_float(int(bits)))
+
+    # -- gate / detection / union -------------------------------------------
+    def update_outlier_set(self, X, tau: float, in_set: np.ndarray, k_cap: int):
+        """Returns (new_set, count, flag); ``in_set`` is not modified."""
+        Xb = _bits(X)
+        M, K = Xb.shape
+        s = np.ascontiguousarray(in_set.astype(np.uint8).copy())
+        flag = np.zeros(1, np.int32)
+        cnt = self.lib.orc_update_outlier_set(_ptr(Xb), M, K, K, float(tau), int(k_cap),
+                                              _ptr(s), _ptr(flag))
+        return s, int(cnt), int(flag[0])
+
+    def outlier_list(self, in_set: np.ndarray) -> np.ndarray:
+        s = np.ascontiguousarray(in_set.astype(np.uint8))
+        idx = np.zeros(max(1, s.size), np.int32)
+        n = self.lib.orc_outlier_list(_ptr(s), s.size, _ptr(idx))
+        return idx[:n].copy()
+
+    # -- quantization ----------------------------------------------------------
+    def quantize_act(self, X, in_set: np.ndarray, ldo: int):
+        Xb = _bits(X)
+        M, K = Xb.shape
+        s = np.ascontiguousarray(in_set.astype(np.uint8))
+        Xq = np.zeros((M, K), np.int8)
+        s_x = np.zeros(M, np.float32)
+        X_out = np.zeros((M, max(ldo, 0)), np.uint16)
+        self.lib.orc_quantize_act(_ptr(Xb), M, K, K, _ptr(s), _ptr(Xq), _ptr(s_x),
+                                  _ptr(X_out), int(ldo))
+        return Xq, s_x, X_out
+
+    def quantize_weight(self, W, bits: int):
+        Wb = _bits(W)
+        N, K = Wb.shape
+        Wq = np.zeros((N, K), np.int8)
+        s_w = np.zeros(N, np.float32)
+        self.lib.orc_quantize_weight(_ptr(Wb), N, K, int(bits), _ptr(Wq), _ptr(s_w))
+        return Wq, s_w
+
+    def gather_weight_cols(self, W, in_set: np.ndarray, ldo: int):
+        Wb = _bits(W)
+        N, K = Wb.shape
+        s = np.ascontiguousarray(in_set.astype(np.uint8))
+        W_out = np.zeros((N, max(ldo, 0)), np.uint16)
+        self.lib.orc_gather_weight_cols(_ptr(Wb), N, K, _ptr(s), _ptr(W_out), int(ldo))
+        return W_out
+
+    # -- products ----------------------------------------------------------------
+    def int_gemm(self, Xq: np.ndarray, Wq: np.ndarray) -> np.ndarray:
+        M, K = Xq.shape
+        N, K2 = Wq.shape
+        assert K == K2
+        acc = np.zeros((M, N), np.int32)
+        rc = self.lib.orc_int_gemm(_ptr(np.ascontiguousarray(Xq)),
+                                   _ptr(np.ascontiguousarray(Wq)), M, N, K, _ptr(acc))
+        if rc != 0:
+            raise OverflowError("integer accumulator exceeds int32")
+        return acc
+
+    def output(self, acc, s_x, s_w, X_out, W_out, k: int) -> np.ndarray:
+        M, N = acc.shape
+        Y = np.zeros((M, N), np.float64)
+        Xo = _bits(X_out)
+        Wo = _bits(W_out)
+        self.lib.orc_output(_ptr(np.ascontiguousarray(acc)), _ptr(np.ascontiguousarray(s_x)),
+                            _ptr(np.ascontiguousarray(s_w)), _ptr(Xo), Xo.shape[1],
+                            _ptr(Wo), Wo.shape[1], M, N, int(k), _ptr(Y))
+        return Y
+
+    def sampled_output(self, Xq, Wq, s_x, s_w, X_out, W_out, k, rows, cols):
+        """acc and Y at the (rows[i], cols[i]) pairs only."""
+        rows = np.ascontiguousarray(rows, np.int64)
+        cols = np.ascontiguousarray(cols, np.int64)
+        S = rows.size
+        acc = np.zeros(S, np.int32)
+        Y = np.zeros(S, np.float64)
+        Xo = _bits(X_out)
+        Wo = _bits(W_out)
+        K = Xq.shape[1]
+        rc = self.lib.orc_sampled_output(
+            _ptr(np.ascontiguousarray(Xq)), _ptr(np.ascontiguousarray(Wq)), K,
+            _ptr(np.ascontiguousarray(s_x)), _ptr(np.ascontiguousarray(s_w)),
+            _ptr(Xo), Xo.shape[1], _ptr(Wo), Wo.shape[1], int(k),
+            _ptr(rows), _ptr(cols), S, _ptr(acc), _ptr(Y))
+        if rc != 0:
+            raise OverflowError("integer accumulator exceeds int32")
+        return acc, Y
+
+
+@dataclass
+class LayerResult:
+    """Everything one oracle step produces."""
+    in_set: np.ndarray
+    idx: np.ndarray
+    count: int
+    flag: int
+    Xq: np.ndarray
+    s_x: np.ndarray
+    X_out: np.ndarray
+    acc: np.ndarray | None = None
+    Y: np.ndarray | None = None
+
+
+@dataclass
+class OracleLayer:
+    """A linear layer with its cached outlier set, stepped the way the MixQ
+    article describes decode: the set persists from call to call and is only
+    re-detected when the amax of the uncached channels exceeds the threshold."""
+    W: np.ndarray               # fp16 [N, K]
+    bits: int = 8
+    tau: float = 6.0
+    k_cap: int = 256
+    ldo: int = 0                # width of the outlier matrices (>= k_cap)
+    oracle: Oracle = field(default_factory=Oracle)
+
+    def __post_init__(self):
+        N, K = self.W.shape
+        if self.ldo < self.k_cap:
+            self.ldo = self.k_cap
+        self.in_set = np.zeros(K, np.uint8)
+        self.Wq, self.s_w = self.oracle.quantize_weight(self.W, self.bits)
+
+    def step(self, X: np.ndarray, products: bool = True) -> LayerResult:
+        o = self.oracle
+        new_set, count, flag = o.update_outlier_set(X, self.tau, self.in_set, self.k_cap)
+        self.in_set = new_set
+        Xq, s_x, X_out = o.quantize_act(X, self.in_set, self.ldo)
+        res = LayerResult(in_set=self.in_set.copy(), idx=o.outlier_list(self.in_set),
+                          count=count, flag=flag, Xq=Xq, s_x=s_x, X_out=X_out)
+        if products:
+            W_out = o.gather_weight_cols(self.W, self.in_set, self.ldo)
+            res.acc = o.int_gemm(Xq, self.Wq)
+            res.Y = o.output(res.acc, s_x, self.s_w, X_out, W_out, count)
+        return res
+
+
+def run_layer(X, W, bits=8, tau=6.0, k_cap=256, ldo=None, oracle=None) -> LayerResult:
+    """One call on a fresh (empty) cached set."""
+    layer = OracleLayer(W=W, bits=bits, tau=tau, k_cap=k_cap, ldo=ldo or k_cap,
+                        oracle=oracle or Oracle())
+    return layer.step(X)

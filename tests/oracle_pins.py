@@ -1,0 +1,444 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Each function takes an ``Oracle`` and raises ``AssertionError`` when the
+oracle disagrees with what the pages or the mathematics fix: hand-derived
+golden values (``tests/golden``), closed-form error bounds, exact identities,
+invariants, special cases that reduce to a textbook formula, and brute force
+on tiny inputs.  ``test_oracle.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` runs them on altered copies and requires that each
+alteration is caught by at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# Slack on top of half a quantization step: three binary32 roundings (the
+# reciprocal, the scale and the product x*r) each perturb x/s by at most
+# 2^-24 relative, and |x| <= amax = 127*s, so the extra error is below
+# 3 * 127 * 2^-24 * s ~= 2.3e-5 * s < 2^-14 * s.
+HALF_STEP_SLACK = 2.0 ** -14
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16(rows):
+    return np.asarray(rows, dtype=np.float64).astype(np.float16)
+
+
+def _mask(K, chans):
+    m = np.zeros(K, np.uint8)
+    m[list(chans)] = 1
+    return m
+
+
+def _rng(*key):
+    return np.random.default_rng(np.random.SeedSequence(list(key)))
+
+
+def _tiny_case(seed, M, K, n_out, scale=30.0):
+    r = _rng(seed, M, K, n_out)
+    X = r.standard_normal((M, K)).astype(np.float32)
+    ch = np.sort(r.choice(K, n_out, replace=False)) if n_out else np.zeros(0, int)
+    if n_out:
+        X[:, ch] *= np.float32(scale)
+    return X.astype(np.float16), ch
+
+
+TINY_SHAPES = [(1, 64, 0), (3, 64, 2), (7, 128, 5), (16, 256, 9), (33, 192, 1), (5, 64, 64)]
+
+
+# ----------------------------------------------------------------------------
+# golden, hand-derived
+# ----------------------------------------------------------------------------
+def pin_golden_act(o):
+    for c in _golden("act_quant_cases.json")["cases"]:
+        X = _f16(c["x"])
+        M, K = X.shape
+        new_set, cnt, flag = o.update_outlier_set(X, c["tau"], _mask(K, c["prev"]), k_cap=K)
+        got_set = list(np.nonzero(new_set)[0])
+        assert got_set == c["expect_set"], (c["name"], got_set)
+        assert (flag == 1) == c["expect_fired"], (c["name"], flag)
+        assert cnt == len(c["expect_set"])
+        assert list(o.outlier_list(new_set)) == c["expect_set"], c["name"]
+        ldo = max(1, len(c["expect_set"]))
+        Xq, s_x, X_out = o.quantize_act(X, new_set, ldo)
+        assert Xq.tolist() == c["expect_q"], (c["name"], Xq.tolist())
+        assert s_x.tolist() == c["expect_s"], (c["name"], s_x.tolist())
+        got_out = X_out.view(np.float16).astype(np.float64)[:, :len(c["expect_set"])]
+        assert got_out.tolist() == [[float(v) for v in r] for r in c["expect_xout"]], c["name"]
+        assert not X_out[:, len(c["expect_set"]):].any(), c["name"]
+
+
+def pin_golden_weight(o):
+    for c in _golden("weight_quant_cases.json")["cases"]:
+        Wq, s_w = o.quantize_weight(_f16(c["w"]), c["bits"])
+        assert Wq.tolist() == c["expect_q"], (c["name"], Wq.tolist())
+        assert s_w.tolist() == c["expect_s"], (c["name"], s_w.tolist())
+
+
+def golden_layer_inputs():
+    g = _golden("layer_worked_example.json")
+    Kt = g["k_total"]
+    X = np.zeros((len(g["X"]), Kt), np.float16)
+    W = np.zeros((len(g["W"]), Kt), np.float16)
+    X[:, :len(g["X"][0])] = _f16(g["X"])
+    W[:, :len(g["W"][0])] = _f16(g["W"])
+    return g, X, W
+
+
+def pin_golden_layer(o):
+    g, X, W = golden_layer_inputs()
+    K = X.shape[1]
+    k0 = len(g["X"][0])
+    new_set, cnt, flag = o.update_outlier_set(X, g["tau"], np.zeros(K, np.uint8), k_cap=K)
+    assert list(np.nonzero(new_set)[0]) == g["expect_set"] and flag == 1
+    Xq, s_x, X_out = o.quantize_act(X, new_set, 32)
+    Wq, s_w = o.quantize_weight(W, 8)
+    W_out = o.gather_weight_cols(W, new_set, 32)
+    assert Xq[:, :k0].tolist() == g["expect_q_x"] and not Xq[:, k0:].any()
+    assert Wq[:, :k0].tolist() == g["expect_q_w"] and not Wq[:, k0:].any()
+    assert s_x.tolist() == g["expect_s_x"] and s_w.tolist() == g["expect_s_w"]
+    assert X_out.view(np.float16)[:, :cnt].astype(float).tolist() == g["expect_x_out"]
+    assert W_out.view(np.float16)[:, :cnt].astype(float).tolist() == g["expect_w_out"]
+    acc = o.int_gemm(Xq, Wq)
+    assert acc.tolist() == g["expect_acc"], acc.tolist()
+    Y = o.output(acc, s_x, s_w, X_out, W_out, cnt)
+    assert Y.tolist() == g["expect_y"], Y.tolist()
+
+
+# ----------------------------------------------------------------------------
+# closed forms, bounds and brute force
+# ----------------------------------------------------------------------------
+def pin_half_decode(o):
+    """Every binary16 pattern decodes as NumPy's (independent) conversion."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    sample = np.concatenate([bits[:2048], bits[0x3000:0x3400], bits[0x7800:0x8800],
+                             bits[-2048:], bits[::97]])
+    for b in sample:
+        got = o.half_to_float(int(b))
+        want = ref[b]
+        if np.isnan(want):
+            assert np.isnan(got), hex(b)
+        else:
+            assert got == want, (hex(b), got, want)
+
+
+def pin_set_bruteforce(o):
+    """Gate + union against a direct column scan (all tokens, all channels)."""
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        X, _ = _tiny_case(seed, M, K, n_out)
+        Xa = np.abs(X.astype(np.float64))
+        r = _rng(99, seed)
+        prev = (r.random(K) < 0.05).astype(np.uint8)
+        for tau in (6.0, 3.0, 1e9):
+            uncached_over = (Xa[:, prev == 0] > tau).any()
+            want = prev.copy()
+            if uncached_over:
+                want |= (Xa > tau).any(axis=0).astype(np.uint8)
+            got, cnt, flag = o.update_outlier_set(X, tau, prev, k_cap=K)
+            assert (got == want).all(), (seed, tau)
+            assert flag == (1 if uncached_over else 0)
+            assert cnt == int(want.sum())
+            idx = o.outlier_list(got)
+            assert (idx == np.nonzero(want)[0]).all() and (np.diff(idx) > 0).all()
+
+
+def pin_quant_error_bound(o):
+    """|x - q*s| <= s*(1/2 + slack) off the set; q = 0 on it; the row's amax
+    maps to +-127; every uncached channel is at or under tau afterwards."""
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        X, _ = _tiny_case(seed, M, K, n_out)
+        tau = 6.0
+        s_set, _, _ = o.update_outlier_set(X, tau, np.zeros(K, np.uint8), k_cap=K)
+        Xq, s_x, _ = o.quantize_act(X, s_set, max(1, K))
+        x = X.astype(np.float64)
+        s = s_x.astype(np.float64)[:, None]
+        off = s_set == 0
+        err = np.abs(x - Xq.astype(np.float64) * s)[:, off]
+        assert (err <= (s * (0.5 + HALF_STEP_SLACK))).all() if off.any() else True
+        assert not Xq[:, ~off].any()
+        assert (np.abs(x[:, off]) <= tau).all() if off.any() else True
+        amax = np.abs(x[:, off]).max(axis=1) if off.any() else np.zeros(M)
+        for m in range(M):
+            if amax[m] > 0:
+                assert np.abs(Xq[m, off]).max() == 127, (seed, m)
+                assert s_x[m] == np.float32(amax[m]) / np.float32(127)
+            else:
+                assert s_x[m] == 1.0 and not Xq[m].any()
+
+
+def pin_nearest_code(o):
+    """Brute force over all 255 codes with exact rationals: the code is the
+    nearest level x / (a/127) (checked where no tie is within 1e-4)."""
+    for seed in range(4):
+        X, _ = _tiny_case(100 + seed, 4, 64, 0)
+        Xq, s_x, _ = o.quantize_act(X, np.zeros(64, np.uint8), 1)
+        for m in range(X.shape[0]):
+            row = [Fraction(float(v)) for v in X[m].astype(np.float64)]
+            a = max(abs(v) for v in row)
+            for k, v in enumerate(row):
+                t = v * 127 / a
+                best = min(range(-127, 128), key=lambda q: abs(t - q))
+                frac = abs(t - int(t)) if t >= 0 else abs(t - int(t))
+                if abs(frac - Fraction(1, 2)) > Fraction(1, 10000):
+                    assert Xq[m, k] == best, (seed, m, k, float(t), int(Xq[m, k]), best)
+
+
+def pin_weight_bound(o):
+    for bits, qmax in ((8, 127), (4, 7)):
+        r = _rng(7, bits)
+        W = (r.standard_normal((24, 128)) * 0.02).astype(np.float16)
+        W[3] = 0
+        Wq, s_w = o.quantize_weight(W, bits)
+        w = W.astype(np.float64)
+        s = s_w.astype(np.float64)[:, None]
+        assert (np.abs(w - Wq * s) <= s * (0.5 + HALF_STEP_SLACK)).all()
+        assert np.abs(Wq).max() <= qmax
+        for n in range(W.shape[0]):
+            if np.abs(w[n]).max() > 0:
+                assert np.abs(Wq[n]).max() == qmax
+            else:
+                assert s_w[n] == 1.0 and not Wq[n].any()
+
+
+def pin_int_gemm_bruteforce(o):
+    """Integer product against an int64 matrix product, incl. extreme codes."""
+    for seed, (M, N, K) in enumerate([(1, 1, 64), (5, 7, 64), (17, 9, 320), (4, 4, 8192)]):
+        r = _rng(11, seed)
+        A = r.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+        B = r.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+        if seed == 3:
+            A[:] = 127
+            B[0] = 127
+            B[1] = -127
+        acc = o.int_gemm(A, B)
+        want = A.astype(np.int64) @ B.astype(np.int64).T
+        assert (acc.astype(np.int64) == want).all(), seed
+
+
+def _layer(o, X, W, tau, bits=8, prev=None, ldo=None):
+    M, K = X.shape
+    prev = np.zeros(K, np.uint8) if prev is None else prev
+    s_set, cnt, flag = o.update_outlier_set(X, tau, prev, k_cap=K)
+    ldo = ldo or max(1, K)
+    Xq, s_x, X_out = o.quantize_act(X, s_set, ldo)
+    Wq, s_w = o.quantize_weight(W, bits)
+    W_out = o.gather_weight_cols(W, s_set, ldo)
+    acc = o.int_gemm(Xq, Wq)
+    Y = o.output(acc, s_x, s_w, X_out, W_out, cnt)
+    return dict(set=s_set, cnt=cnt, flag=flag, Xq=Xq, s_x=s_x, X_out=X_out, Wq=Wq,
+                s_w=s_w, W_out=W_out, acc=acc, Y=Y)
+
+
+def _wcase(seed, N, K, std=0.05):
+    return (_rng(21, seed, N, K).standard_normal((N, K)) * std).astype(np.float16)
+
+
+def pin_split_identity(o):
+    """Exact split in FP64 on the raw operands:
+    X W^T = (X with outlier channels zeroed) W^T + X_out W_out^T.
+    A misplaced, dropped or misordered outlier column breaks it."""
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        X, _ = _tiny_case(seed, M, K, n_out)
+        W = _wcase(seed, 11, K)
+        L = _layer(o, X, W, 6.0)
+        x = X.astype(np.float64)
+        w = W.astype(np.float64)
+        keep = (L["set"] == 0).astype(np.float64)
+        c = L["cnt"]
+        xo = L["X_out"].view(np.float16).astype(np.float64)[:, :c]
+        wo = L["W_out"].view(np.float16).astype(np.float64)[:, :c]
+        lhs = x @ w.T
+        rhs = (x * keep) @ w.T + xo @ wo.T
+        assert np.allclose(lhs, rhs, rtol=0, atol=1e-12 * max(1.0, np.abs(lhs).max())), seed
+
+
+def pin_output_vs_dequant(o):
+    """Y against a brute-force FP64 sum over dequantized operands:
+    sum_{k not in I} (q_x s_x)(q_w s_w) + sum_j X_out W_out."""
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        for bits in (8, 4):
+            X, _ = _tiny_case(seed, M, K, n_out)
+            W = _wcase(seed, 13, K)
+            L = _layer(o, X, W, 6.0, bits=bits)
+            xd = L["Xq"].astype(np.float64) * L["s_x"].astype(np.float64)[:, None]
+            wd = L["Wq"].astype(np.float64) * L["s_w"].astype(np.float64)[:, None]
+            c = L["cnt"]
+            xo = L["X_out"].view(np.float16).astype(np.float64)[:, :c]
+            wo = L["W_out"].view(np.float16).astype(np.float64)[:, :c]
+            want = np.zeros((M, W.shape[0]))
+            for m in range(M):
+                for n in range(W.shape[0]):
+                    want[m, n] = sum(xd[m, k] * wd[n, k] for k in range(K)) + \
+                        sum(xo[m, j] * wo[n, j] for j in range(c))
+            scale = max(1.0, np.abs(want).max())
+            assert np.abs(L["Y"] - want).max() <= 1e-12 * scale, (seed, bits)
+
+
+def pin_output_vs_truth_bound(o):
+    """|Y - X W^T| <= sum_{k not in I} (|x| e_w + |w| e_x + e_x e_w), with
+    e = s (1/2 + slack): the closed-form quantization error bound."""
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        for bits in (8, 4):
+            X, _ = _tiny_case(seed, M, K, n_out)
+            W = _wcase(seed, 9, K)
+            L = _layer(o, X, W, 6.0, bits=bits)
+            x = X.astype(np.float64)
+            w = W.astype(np.float64)
+            truth = x @ w.T
+            ex = L["s_x"].astype(np.float64) * (0.5 + HALF_STEP_SLACK)
+            ew = L["s_w"].astype(np.float64) * (0.5 + HALF_STEP_SLACK)
+            off = (L["set"] == 0).astype(np.float64)
+            bound = (np.abs(x) * off) @ np.ones((K, 1)) * ew[None, :] \
+                + ex[:, None] * ((np.abs(w) * off[None, :]).sum(axis=1))[None, :] \
+                + ex[:, None] * ew[None, :] * off.sum()
+            slack = 1e-9 * (np.abs(x) @ np.abs(w).T + 1.0)
+            assert (np.abs(L["Y"] - truth) <= bound + slack).all(), (seed, bits)
+
+
+def pin_no_outlier_textbook(o):
+    """Nothing above the threshold: the layer is plain W8A8 with per-token and
+    per-channel scales, Y = (q_x q_w^T) * (s_x s_w^T)."""
+    X, _ = _tiny_case(5, 9, 128, 0)
+    W = _wcase(5, 10, 128)
+    L = _layer(o, X, W, float("inf"))
+    assert L["cnt"] == 0 and L["flag"] == 0
+    want = (L["Xq"].astype(np.int64) @ L["Wq"].astype(np.int64).T).astype(np.float64)
+    want = want * L["s_x"].astype(np.float64)[:, None] * L["s_w"].astype(np.float64)[None, :]
+    assert np.abs(L["Y"] - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def pin_all_outlier(o):
+    """tau = 0: every nonzero channel is an outlier, all codes are 0 with unit
+    scales, and Y is the plain FP16-input product X W^T."""
+    X, _ = _tiny_case(6, 6, 64, 0)
+    X[:, 5] = 0
+    W = _wcase(6, 8, 64)
+    L = _layer(o, X, W, 0.0)
+    assert L["cnt"] == 63 and not L["Xq"].any() and (L["s_x"] == 1.0).all()
+    truth = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.abs(L["Y"] - truth).max() <= 1e-12 * np.abs(truth).max()
+
+
+def pin_sign_symmetry(o):
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        X, _ = _tiny_case(seed, M, K, n_out)
+        s1, c1, _ = o.update_outlier_set(X, 6.0, np.zeros(K, np.uint8), K)
+        s2, c2, _ = o.update_outlier_set(-X, 6.0, np.zeros(K, np.uint8), K)
+        assert (s1 == s2).all() and c1 == c2
+        q1, sx1, xo1 = o.quantize_act(X, s1, K)
+        q2, sx2, xo2 = o.quantize_act(-X, s2, K)
+        assert (q1 == -q2).all() and (sx1 == sx2).all()
+        assert (xo1.view(np.float16) == -xo2.view(np.float16)).all()
+
+
+def pin_pow2_scaling(o):
+    """X*2^p with tau*2^p: same set and codes, scales times 2^p (binary
+    scaling commutes with every rounding when nothing over/underflows)."""
+    for seed, (M, K, n_out) in enumerate(TINY_SHAPES):
+        X, _ = _tiny_case(seed, M, K, n_out, scale=10.0)
+        for p in (1, 3):
+            Xs = (X.astype(np.float32) * np.float32(2.0 ** p)).astype(np.float16)
+            assert (Xs.astype(np.float64) == X.astype(np.float64) * 2.0 ** p).all()
+            s1, _, _ = o.update_outlier_set(X, 6.0, np.zeros(K, np.uint8), K)
+            s2, _, _ = o.update_outlier_set(Xs, 6.0 * 2 ** p, np.zeros(K, np.uint8), K)
+            assert (s1 == s2).all()
+            q1, sx1, _ = o.quantize_act(X, s1, 1)
+            q2, sx2, _ = o.quantize_act(Xs, s2, 1)
+            assert (q1 == q2).all()
+            # rows whose amax is 0 keep the unit scale of the zero-scale rule
+            live = np.abs(X.astype(np.float64))[:, s1 == 0].max(axis=1, initial=0) > 0
+            assert (sx2[live].astype(np.float64) == sx1[live].astype(np.float64) * 2.0 ** p).all()
+            assert (sx1[~live] == 1).all() and (sx2[~live] == 1).all()
+
+
+def pin_permutation(o):
+    """Permuting channels of X and W together permutes the set and leaves the
+    integer product and Y unchanged."""
+    X, _ = _tiny_case(8, 12, 192, 6)
+    W = _wcase(8, 7, 192)
+    perm = _rng(8, 1).permutation(192)
+    A = _layer(o, X, W, 6.0)
+    B = _layer(o, np.ascontiguousarray(X[:, perm]), np.ascontiguousarray(W[:, perm]), 6.0)
+    assert (B["set"] == A["set"][perm]).all()
+    assert (A["acc"] == B["acc"]).all()
+    assert np.abs(A["Y"] - B["Y"]).max() <= 1e-12 * np.abs(A["Y"]).max()
+
+
+def pin_overflow(o):
+    """More outliers than k_cap: flag 2 and the set is left as it was; exactly
+    k_cap outliers still fit."""
+    X, ch = _tiny_case(9, 8, 128, 6, scale=40.0)
+    need = int((np.abs(X.astype(np.float64)) > 6.0).any(axis=0).sum())
+    s_ok, c_ok, f_ok = o.update_outlier_set(X, 6.0, np.zeros(128, np.uint8), k_cap=need)
+    assert f_ok == 1 and c_ok == need
+    s_no, c_no, f_no = o.update_outlier_set(X, 6.0, np.zeros(128, np.uint8), k_cap=need - 1)
+    assert f_no == 2 and c_no == 0 and not s_no.any()
+
+
+def pin_decode_sequence(o):
+    """A short decode run with a persistent set and planted transient
+    channels: the gate fires on exactly the steps that hold an uncached value
+    above tau, and after every step the set equals the union of everything
+    seen so far (the gated set equals the ungated one)."""
+    M, K, steps = 8, 256, 12
+    r = _rng(31)
+    pers = np.sort(r.choice(K, 5, replace=False))
+    rest = np.setdiff1d(np.arange(K), pers)
+    events = {2: r.choice(rest, 2, replace=False), 7: r.choice(rest, 1, replace=False),
+              8: r.choice(rest, 3, replace=False)}
+    cur = np.zeros(K, np.uint8)
+    seen = np.zeros(K, bool)
+    for st in range(steps):
+        X = r.standard_normal((M, K)).astype(np.float32)
+        X[:, pers] = r.uniform(20, 100, (M, pers.size)) * np.where(r.random((M, pers.size)) < .5, -1, 1)
+        if st in events:
+            e = events[st]
+            X[:, e] = r.uniform(20, 100, (M, e.size))
+        X = X.astype(np.float16)
+        over = (np.abs(X.astype(np.float64)) > 6.0).any(axis=0)
+        expect_fire = bool((over & (cur == 0)).any())
+        seen |= over
+        cur_new, cnt, flag = o.update_outlier_set(X, 6.0, cur, k_cap=K)
+        assert flag == (1 if expect_fire else 0), st
+        assert (cur_new.astype(bool) == seen).all(), st
+        cur = cur_new
+
+
+def pin_sampled_output(o):
+    """The per-pair entry point against an int64 matrix product and an FP64
+    sum over the outlier columns, at random (row, col) pairs."""
+    X, _ = _tiny_case(12, 19, 320, 7)
+    W = _wcase(12, 23, 320)
+    L = _layer(o, X, W, 6.0, ldo=32)
+    r = _rng(12, 5)
+    rows = r.integers(0, 19, 40)
+    cols = r.integers(0, 23, 40)
+    acc, Y = o.sampled_output(L["Xq"], L["Wq"], L["s_x"], L["s_w"], L["X_out"], L["W_out"],
+                              L["cnt"], rows, cols)
+    full = L["Xq"].astype(np.int64) @ L["Wq"].astype(np.int64).T
+    assert (acc == full[rows, cols]).all()
+    c = L["cnt"]
+    xo = L["X_out"].view(np.float16).astype(np.float64)[:, :c]
+    wo = L["W_out"].view(np.float16).astype(np.float64)[:, :c]
+    want = full[rows, cols] * L["s_x"].astype(np.float64)[rows] * L["s_w"].astype(np.float64)[cols] \
+        + (xo[rows] * wo[cols]).sum(axis=1)
+    assert np.abs(Y - want).max() <= 1e-12 * np.abs(want).max()
+
+
+ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode,
+            pin_set_bruteforce, pin_quant_error_bound, pin_nearest_code, pin_weight_bound,
+            pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
+            pin_output_vs_truth_bound, pin_no_outlier_textbook, pin_all_outlier,
+            pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
+            pin_decode_sequence, pin_sampled_output]

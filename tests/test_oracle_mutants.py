@@ -1,0 +1,90 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (a dropped term, a
+wrong comparison, a wrong index, a wrong constant, ...), builds the copy into
+a temporary directory and runs every pin on it: at least one pin must fail.
+The mistakes are planted in the oracle only, on the CPU.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle_pins
+from oracle import Oracle
+from oracle.mixq_oracle import CFLAGS, _SRC
+
+# (name, text to replace, replacement, which occurrence (0-based))
+MUTANTS = [
+    ("gate_ge", "if (g > tau) fired = 1;", "if (g >= tau) fired = 1;", 0),
+    ("detect_ge", "> tau) hit = 1;", ">= tau) hit = 1;", 0),
+    ("gate_ignores_cache", "if (in_set[k]) continue;", ";", 0),
+    ("fresh_set_not_union", "int hit = in_set[k] ? 1 : 0;", "int hit = 0;", 0),
+    ("overflow_ge", "if (after > k_cap)", "if (after >= k_cap)", 0),
+    ("round_half_away", "nearbyintf(x * recip)", "roundf(x * recip)", 0),
+    ("scale_off_by_one", "*scale = amax / (float)qmax;", "*scale = amax / (float)(qmax + 1);", 0),
+    ("recip_off_by_one", "*recip = (float)qmax / amax;", "*recip = (float)(qmax - 1) / amax;", 0),
+    ("zero_scale_rule", "*scale = 1.0f;", "*scale = 0.0f;", 0),
+    ("act_amax_includes_outliers", "if (in_set[k]) continue;", ";", 1),
+    ("outlier_code_not_zeroed", "Xq[m * K + k] = in_set[k] ? 0", "Xq[m * K + k] = 0 ? 0", 0),
+    ("list_descending", "for (k = 0; k < K; ++k)\n        if (in_set[k]) idx[n++] = (int32_t)k;",
+     "for (k = K - 1; k >= 0; --k)\n        if (in_set[k]) idx[n++] = (int32_t)k;", 0),
+    ("xout_wrong_column", "X_out[m * ldo + j++] = row[k];", "X_out[m * ldo + j++] = row[K - 1 - k];", 0),
+    ("wout_wrong_column", "W_out[n * ldo + j++] = W[n * K + k];",
+     "W_out[n * ldo + j++] = W[n * K + (K - 1 - k)];", 0),
+    ("gemm_reversed_k", "s += (int64_t)Xq[m * K + k] * (int64_t)Wq[n * K + k];",
+     "s += (int64_t)Xq[m * K + k] * (int64_t)Wq[n * K + (K - 1 - k)];", 0),
+    ("gemm_narrow_accumulator", "int64_t s = 0;", "int16_t s = 0;", 0),
+    ("output_drops_outliers", "y += (double)orc_half_to_float(X_out[m * ldxo + j]) *",
+     "y += 0.0 * (double)orc_half_to_float(X_out[m * ldxo + j]) *", 0),
+    ("output_drops_weight_scale",
+     "double y = (double)acc[m * N + n] * (double)s_x[m] * (double)s_w[n];",
+     "double y = (double)acc[m * N + n] * (double)s_x[m];", 0),
+    ("output_sign", "double y = (double)acc[m * N + n] * (double)s_x[m] * (double)s_w[n];",
+     "double y = -(double)acc[m * N + n] * (double)s_x[m] * (double)s_w[n];", 0),
+    ("sampled_reversed_k", "s += (int64_t)Xq[m * K + kk] * (int64_t)Wq[n * K + kk];",
+     "s += (int64_t)Xq[m * K + kk] * (int64_t)Wq[n * K + (K - 1 - kk)];", 0),
+    ("sampled_drops_outliers", "y += (double)orc_half_to_float(X_out[m * ldxo + j]) *",
+     "y += 0.0 * (double)orc_half_to_float(X_out[m * ldxo + j]) *", 1),
+    ("int4_range", "return (1 << (bits - 1)) - 1;", "return (1 << bits) - 1;", 0),
+    ("half_exponent_bias", "expo - 25", "expo - 24", 0),
+    ("half_subnormal", "ldexpf((float)mant, -24)", "ldexpf((float)mant, -25)", 0),
+]
+
+
+def _apply(src, old, new, occ):
+    pos = -1
+    for _ in range(occ + 1):
+        pos = src.find(old, pos + 1)
+        assert pos >= 0, f"mutation site not found: {old!r} #{occ}"
+    return src[:pos] + new + src[pos + len(old):]
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="mixq_mut_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(workdir, name, old, new, occ):
+    with open(_SRC) as f:
+        src = f.read()
+    mutated = _apply(src, old, new, occ)
+    assert mutated != src
+    c_path = os.path.join(workdir, f"{name}.c")
+    so_path = os.path.join(workdir, f"lib{name}.so")
+    with open(c_path, "w") as f:
+        f.write(mutated)
+    subprocess.run(["gcc", *CFLAGS, c_path, "-o", so_path, "-lm"], check=True)
+    o = Oracle(so_path)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, OverflowError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
