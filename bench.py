@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-precision linear layer on one MI355X.
+
+A step is one pass of the whole layer over one batch: mixq_quantize_act
+(amax, gate, quantize, outlier split), mixq_pack_weight in its
+outlier-column mode (a device-side no-op unless the set changed) and
+mixq_gemm (INT8 x INT8 product, FP16 outlier product, fused epilogue).
+Inputs are seeded synthetic tensors already resident in HBM; several copies
+of the inputs and packed weights are rotated so that the 256 MB Infinity
+Cache cannot serve them from one step to the next.
+
+Prints one JSON line.  ``value`` is the step throughput in effective TOPS
+(2*M*N*K per step, outliers counted once).  ``roofline`` reports the GEMM
+kernel, timed with HIP events around each launch on its stream.
+``cpu_baseline`` times the CPU oracle on a bounded row sample of the same
+workload (only with --gpus 1, on rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_I8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "mixed-precision GEMM effective TOPS + % of INT8 MFMA peak (LLaMA shapes)"
+CACHE_DEFEAT_BYTES = 768 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "mixed_precision_quantized_amax_amd", "csrc", "mixq_gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_sha() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def gemm_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken on the current GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha") != gemm_source_sha():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else int(w["hbm_bytes_per_launch"])
+
+
+def algorithmic_bytes(wl, k: int) -> int:
+    """Bytes a GEMM launch must move at least once: Xq, the packed weight,
+    the two scale vectors, the padded outlier matrices and the fp32 Y."""
+    kp = (k + 31) // 32 * 32
+    return (wl.M * wl.K + wl.N * wl.K * wl.bits // 8 + 4 * (wl.M + wl.N)
+            + 2 * kp * (wl.M + wl.N) + 4 * wl.M * wl.N)
+
+
+def run_gpu(wl, steps: int, warmup: int):
+    import torch
+    from mixed_precision_quantized_amax_amd import mixq, workloads
+
+    dev = torch.device("cuda", 0)
+    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits}")
+    W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
+    X0 = torch.from_numpy(workloads.make_activation(wl)).to(dev)
+    k_cap = 256
+    wq_bytes = wl.N * wl.K * wl.bits // 8
+    copies = int(min(8, max(2, math.ceil(CACHE_DEFEAT_BYTES / (wq_bytes + 3 * wl.M * wl.K)))))
+    state = mixq.OutlierState.create(wl.K, k_cap, dev)
+    packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev) for _ in range(copies)]
+    for p in packs:
+        mixq.pack_weight(W, state, p, mixq.PACK_FULL)
+    # activation copies: the same values in different buffers
+    Xs = [X0.clone() for _ in range(copies)]
+    ld = mixq.outlier_ld(k_cap)
+    Xq = [torch.empty(wl.M, wl.K, dtype=torch.int8, device=dev) for _ in range(copies)]
+    sx = [torch.empty(wl.M, dtype=torch.float32, device=dev) for _ in range(copies)]
+    Xo = [torch.zeros(wl.M * ld, dtype=torch.float16, device=dev) for _ in range(copies)]
+    Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps_c = [mixq.LayerStep(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y)
+               for c in range(copies)]
+
+    def step(i, ev=None):
+        s = steps_c[i % copies]
+        if ev is None:
+            s()
+            return
+        ev[0].record(stream)
+        s.act()
+        ev[1].record(stream)
+        s.gemm()
+        ev[2].record(stream)
+
+    # first call detects the planted outlier channels
+    step(0)
+    torch.cuda.synchronize()
+    count = int(state.count.cpu()[0])
+    log(f"[bench] outlier channels detected: {count}; weight copies: {copies}")
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # GEMM kernel duration: back-to-back launches bracketed by events on the
+    # launch stream (the host enqueues faster than the kernel runs)
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for i in range(steps):
+        steps_c[i % copies].gemm()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = g0.elapsed_time(g1) / steps
+    # activation side (quantize + gather gate), also back to back
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for i in range(steps):
+        steps_c[i % copies].act()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    act_ms = g0.elapsed_time(g1) / steps
+    flag = int(state.flag.cpu()[0])
+    return dict(ms_step=ms_step, gemm_ms=gemm_ms, act_ms=act_ms, count=count, flag=flag,
+                copies=copies)
+
+
+def run_cpu_baseline(wl, target_s: float = 12.0):
+    """The CPU oracle on a row sample of the workload: gate and quantization
+    of the sampled tokens, the integer product against all N weight rows, and
+    the dequantize/add output.  The weight is quantized beforehand (offline,
+    as on the GPU)."""
+    from mixed_precision_quantized_amax_amd import workloads
+    from oracle import Oracle
+
+    o = Oracle()
+    X = workloads.make_activation(wl)
+    W = workloads.make_weight(wl)
+    Wq, s_w = o.quantize_weight(W, wl.bits)
+    in_set, cnt, _ = o.update_outlier_set(X, wl.tau, np.zeros(wl.K, np.uint8), 256)
+    W_out = o.gather_weight_cols(W, in_set, 256)
+
+    def run(rows):
+        Xs = np.ascontiguousarray(X[:rows])
+        t = time.perf_counter()
+        s, c, _ = o.update_outlier_set(Xs, wl.tau, in_set, 256)
+        Xq, s_x, X_out = o.quantize_act(Xs, s, 256)
+        acc = o.int_gemm(Xq, Wq)
+        o.output(acc, s_x, s_w, X_out, W_out, c)
+        return time.perf_counter() - t
+
+    rows = 2
+    dt = run(rows)
+    while dt < target_s / 4 and rows < wl.M:
+        rows = min(wl.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 0.8)))
+        dt = run(rows)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    tops = 2.0 * rows * wl.N * wl.K / dt / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {wl.M} tokens x all {wl.N} outputs x K={wl.K} "
+                      f"(gate, quantize, int64-accumulated product, fp64 output) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_w8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer is not sharded across GPUs in this "
+              "build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from mixed_precision_quantized_amax_amd import workloads
+    wl = workloads.WORKLOADS[args.workload]
+    r = run_gpu(wl, args.steps, args.warmup)
+    ops = wl.ops
+    value = ops / (r["ms_step"] / 1e3) / 1e12
+    gemm_tops = ops / (r["gemm_ms"] / 1e3) / 1e12
+    alg_bytes = algorithmic_bytes(wl, r["count"])
+    traffic = gemm_traffic(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded N(0,1) activations with planted outlier channels, "
+                "N(0,std) weights)",
+        "config": {"workload": wl.description, "name": wl.name, "M": wl.M, "K": wl.K,
+                   "N": wl.N, "weight_bits": wl.bits, "outlier_channels": r["count"],
+                   "threshold": wl.tau, "parallelism": "single GPU"},
+        "pct_int8_peak": round(100.0 * value / PEAK_I8_TOPS, 2),
+        "gemm_tops": round(gemm_tops, 2),
+        "gemm_us": round(r["gemm_ms"] * 1e3, 2),
+        "act_quant_us": round(r["act_ms"] * 1e3, 2),
+        "act_quant_gbs": round((2 + 1) * wl.M * wl.K / (r["act_ms"] / 1e3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_I8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
+    }
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
+        except Exception as e:  # reported, never fatal for the GPU number
+            out["cpu_baseline"] = {"value": None, "error": repr(e)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * mixq.h -- C ABI of the MI355X (gfx950) mixed-precision linear layer
+ *
+ *     Y = X . W^T      X: fp16 [M, K] activations, W: fp16 [N, K] weights
+ *
+ * computed the MixQ way: activations quantized per token to INT8 from an
+ * amax pass; the few input channels holding outliers (|x| above a threshold)
+ * split out, in channel order, into a small FP16 matrix; the bulk multiplied
+ * as INT8 x INT8 (or INT8 x INT4 weights) with INT32 accumulation, the
+ * outlier columns as FP16 x FP16; the low-precision result dequantized,
+ * scaled and added to the outlier product in one fused epilogue.  The outlier
+ * channel set is cached across calls and re-detected only when the amax of
+ * the uncached channels exceeds the threshold.
+ *
+ * Sources (cited by page title and section; they print no API, so the calls
+ * below are this library's own):
+ *   MixQ article -- news article on MixQ, "一键部署LLM混合精度推理，端到端吞吐比
+ *     AWQ最大提升6倍！": section "研究背景：已有量化技术总结", Fig. 5 (split of
+ *     the product into a low-bit part and an FP16 outlier part, summed);
+ *     section "MixQ的解决方案": Fig. 9 (outliers recur in fixed channels across
+ *     decode steps), the amax-versus-threshold paragraph (the amax that
+ *     quantization computes anyway tells whether outliers exist), Fig. 10
+ *     (equivalent graph transform that skips detection), Fig. 11 (outliers
+ *     concatenated, order preserved, into a new matrix), Fig. 12 (dequantize,
+ *     scale and add fused in registers).
+ *   FP6 explainer -- "DeepSpeed FP6以 FP6 量化与 TC-FPx 全栈 GPU Kernel 为核心的
+ *     LLM 推理服务加速": section 2.3 (unsupported shapes rejected with an
+ *     explicit error), section 3 (explicit error on unsupported hardware;
+ *     per-output-channel scale = max|w| over the code range, zero scale -> 1).
+ *   QServe notes -- reading notes on QServe W4A8KV4: sections
+ *     "寄存器压力和并行性" and "小结" (INT4 weights decoded to INT8 inside the
+ *     GEMM main loop so that every product runs on INT8 matrix units).
+ *
+ * Conventions for every call
+ *   - Device pointers point to memory of the current HIP device; structs are
+ *     host memory passed by pointer and read during the call only.
+ *   - The library never allocates, frees or synchronizes.  Every buffer is
+ *     owned by the caller.  Work is enqueued on `stream` (a hipStream_t; NULL
+ *     = the default stream) and runs asynchronously.
+ *   - Arguments are validated on the host before any HIP call; a failed
+ *     check returns an error and enqueues nothing.
+ *   - Calls on different streams are safe when they touch disjoint buffers.
+ *     Two calls that share an activation state or a packed weight must be
+ *     ordered (same stream, or events).
+ *   - Return value: MIXQ_OK or one of the MIXQ_ERR_* codes below.  Nothing is
+ *     printed and no exception or abort crosses the ABI.
+ */
+#ifndef MIXQ_H
+#define MIXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+enum {
+    MIXQ_OK = 0,
+    MIXQ_ERR_INVALID_ARG = 1,        /* null pointer, size <= 0, bad enum, ...   */
+    MIXQ_ERR_UNSUPPORTED_SHAPE = 2,  /* K not a multiple of 64, or too large    */
+    MIXQ_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950            */
+    MIXQ_ERR_NO_DEVICE = 4,          /* no HIP device visible                    */
+    MIXQ_ERR_HIP = 5                 /* a HIP launch reported an error          */
+};
+
+/* ---- limits --------------------------------------------------------------- */
+#define MIXQ_K_MULTIPLE 64           /* K must be a multiple of this            */
+#define MIXQ_K_MAX 65536             /* largest supported K                     */
+#define MIXQ_OUTLIER_ALIGN 32        /* outlier matrices padded to this many k  */
+
+/* flag bits written by mixq_quantize_act into *state->flag */
+#define MIXQ_FLAG_FIRED 1            /* gate fired, set grew                    */
+#define MIXQ_FLAG_OVERFLOW 2         /* gate fired, but |set| would exceed k_cap;
+                                        set left unchanged                      */
+
+/* mixq_pack_weight modes */
+#define MIXQ_PACK_FULL 0             /* quantize all of W and gather outliers   */
+#define MIXQ_PACK_OUTLIER_COLS 1     /* only re-gather the outlier columns, and
+                                        only if the state's set has changed     */
+
+/*
+ * Cached outlier-channel set of one activation stream (MixQ article,
+ * "MixQ的解决方案", Fig. 9 and the amax paragraph).  All pointers are device
+ * memory, owned by the caller and zero-filled once before the first call
+ * (an empty set); after that only the library writes them.  The set only
+ * grows: channels found by a firing gate are added to it.
+ */
+typedef struct mixq_act_state {
+    int32_t *idx;      /* [k_cap]  outlier channel ids, ascending; first *count valid */
+    int32_t *count;    /* [1]      size of the set                                   */
+    int32_t *flag;     /* [1]      MIXQ_FLAG_* bits of the last quantize call        */
+    uint32_t *bitmap;  /* [mixq_bitmap_words(K)]  bit k%32 of word k/32 = channel k  */
+    uint32_t *work;    /* [mixq_state_work_words(K)]  library scratch: detection
+                          bits, rank prefix of the bitmap, counters               */
+    int32_t k_cap;     /* host value: capacity of the set, 0 <= k_cap <= K           */
+} mixq_act_state;
+
+/* Number of per-block version slots of a packed weight (see mixq_weight.k_out). */
+#define MIXQ_GATHER_SLOTS 256
+
+/*
+ * A packed weight (FP6 explainer, section 3: weights quantized once, per
+ * output channel, symmetric; MixQ article, Fig. 11: FP16 columns of the
+ * outlier channels kept beside them, in channel order).  Device buffers are
+ * owned by the caller; mixq_pack_weight fills them.
+ */
+typedef struct mixq_weight {
+    void *wq;          /* bits 8: int8 [N, K] row-major codes in [-127, 127];
+                          bits 4: uint8 [N, K/2]; each 32-bit word holds 8
+                          consecutive k: byte j = (q[k+j] & 15) | (q[k+j+4] & 15) << 4,
+                          codes in [-7, 7]                                        */
+    float *s_w;        /* [N] per-output-channel scale                            */
+    uint16_t *w_out;   /* fp16 [N, mixq_outlier_ld(k_cap)]: W at the outlier
+                          channels in set order, then zeros                       */
+    int32_t *k_out;    /* [MIXQ_GATHER_SLOTS] set size each slice of w_out was
+                          gathered for; zero-fill once                            */
+    int32_t bits;      /* 8 or 4                                                  */
+    int64_t N, K;
+    int32_t k_cap;     /* must equal the k_cap of the states it is used with      */
+} mixq_weight;
+
+/* ---- size helpers (pure host functions) ---------------------------------- */
+/* Row length of X_out and w_out: k_cap rounded up to MIXQ_OUTLIER_ALIGN. */
+int64_t mixq_outlier_ld(int32_t k_cap);
+/* Number of 32-bit words of a state's bitmap: ceil(K / 32). */
+int64_t mixq_bitmap_words(int64_t K);
+/* Number of 32-bit words of a state's work area: 2 * ceil(K / 32) + 4. */
+int64_t mixq_state_work_words(int64_t K);
+/* Bytes of mixq_weight.wq: N*K for 8 bits, N*K/2 for 4 bits; 0 if invalid. */
+size_t mixq_packed_weight_bytes(int64_t N, int64_t K, int32_t bits);
+
+/*
+ * mixq_quantize_act -- amax, gate, detection and per-token INT8 quantization
+ * with the outlier split (MixQ article, "MixQ的解决方案": the amax paragraph
+ * and Figs. 10-11; Fig. 5 for the split).
+ *
+ * For each token m:  a_m = max |X[m,k]| over channels k not in the set;
+ * s_x[m] = a_m / 127 and r = 127 / a_m (both single IEEE fp32 divisions; a_m = 0
+ * gives s_x = r = 1); Xq[m,k] = 0 for k in the set, else
+ * clamp(round_half_even(X[m,k] * r), -127, 127);  X_out[m, j] = X[m, idx[j]]
+ * for j < count, zeros up to the next multiple of MIXQ_OUTLIER_ALIGN.
+ * Before quantizing, the gate compares the amax of the uncached channels with
+ * `threshold` (strictly greater fires).  If it fires, every channel with some
+ * |X[m,k]| > threshold joins the set (if the set would exceed k_cap, it is
+ * left unchanged and MIXQ_FLAG_OVERFLOW is raised) and the call quantizes
+ * with the new set.  *state->flag is rewritten by every call.
+ *
+ *   X        fp16 [M, ldx] device, row-major, read-only; finite values
+ *   M        tokens, >= 1;   K: channels, multiple of 64, <= MIXQ_K_MAX
+ *   ldx      row stride of X in elements, >= K
+ *   threshold finite, >= 0
+ *   state    the cached set (see mixq_act_state); k_cap <= K
+ *   Xq       int8 [M, K] device, written
+ *   s_x      fp32 [M] device, written
+ *   X_out    fp16 [M, mixq_outlier_ld(k_cap)] device, written up to the padded
+ *            set size; may be NULL when k_cap == 0
+ * Errors: MIXQ_ERR_INVALID_ARG, MIXQ_ERR_UNSUPPORTED_SHAPE, MIXQ_ERR_NO_DEVICE,
+ *         MIXQ_ERR_UNSUPPORTED_DEVICE, MIXQ_ERR_HIP.
+ */
+int mixq_quantize_act(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
+                      const mixq_act_state *state, int8_t *Xq, float *s_x, uint16_t *X_out,
+                      void *stream);
+
+/*
+ * mixq_pack_weight -- per-output-channel symmetric quantization of W and the
+ * FP16 outlier columns (FP6 explainer, section 3; MixQ article, Fig. 11).
+ *
+ *   s_w[n] = alpha_n / Q and rho = Q / alpha_n, alpha_n = max_k |W[n,k]| over
+ *   all K, Q = 127 (bits 8) or 7 (bits 4), alpha_n = 0 gives 1;
+ *   code = clamp(round_half_even(W[n,k] * rho), -Q, Q), stored as documented
+ *   in mixq_weight;  w_out[n, j] = W[n, idx[j]] for j < count, then zeros.
+ *
+ *   W      fp16 [N, K] device, row-major (ld = K).  Keep it: the outlier
+ *          columns are gathered from it again when the set grows.
+ *   N, K   >= 1; K multiple of 64, <= MIXQ_K_MAX
+ *   bits   8 or 4
+ *   state  the activation state whose set selects the outlier columns
+ *   mode   MIXQ_PACK_FULL: everything.  MIXQ_PACK_OUTLIER_COLS: re-gather
+ *          w_out only, decided on the device (no host sync): it runs when
+ *          *state->count differs from *w->k_out, and is a no-op otherwise.
+ *          Call it after each mixq_quantize_act and before mixq_gemm.
+ *   w      the packed weight; w->N, w->K, w->bits, w->k_cap must match
+ * Errors: as mixq_quantize_act.
+ */
+int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
+                     const mixq_act_state *state, int32_t mode, const mixq_weight *w,
+                     void *stream);
+
+/*
+ * mixq_gemm -- the two products and the fused epilogue (MixQ article, Fig. 5
+ * and Fig. 12):
+ *
+ *   acc[m,n] = sum_k Xq[m,k] * Wq[n,k]                 (exact, int32)
+ *   Y[m,n]   = float(acc) * s_x[m] * s_w[n] + sum_{j < count} X_out[m,j] * w_out[n,j]
+ *
+ * with INT8 x INT8 (INT4 weights decoded to INT8 in the kernel) matrix-core
+ * products accumulated in int32, the outlier product on FP16 matrix cores
+ * accumulated in fp32, and the dequantize/scale/add done in registers.  The
+ * set size is read on the device from state->count (no host sync).
+ *
+ *   Xq, s_x, X_out  as written by mixq_quantize_act for the same state
+ *   state           the activation state (count and k_cap are used)
+ *   w               packed weight, gathered for the current set
+ *   M               tokens, >= 1
+ *   Y               fp32 [M, ldy] device, written; ldy >= N
+ *   acc_debug       NULL, or int32 [M, N] device: also receives acc
+ * Errors: as mixq_quantize_act.
+ */
+int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
+              const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
+              int64_t ldy, int32_t *acc_debug, void *stream);
+
+/* Text of a status code (static storage). */
+const char *mixq_status_string(int status);
+
+/* MIXQ_OK when the current HIP device is gfx950, else MIXQ_ERR_NO_DEVICE or
+ * MIXQ_ERR_UNSUPPORTED_DEVICE (FP6 explainer, section 3: explicit error on
+ * unsupported hardware). */
+int mixq_check_device(void);
+
+/* ABI version: 100 * major + minor. */
+int mixq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MIXQ_H */

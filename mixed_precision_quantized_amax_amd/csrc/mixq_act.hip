@@ -1,0 +1,334 @@
+// Activation side of the mixed-precision linear layer: fused amax, gate,
+// outlier detection, per-token INT8 quantization and outlier extraction.
+//
+// MixQ article, section "MixQ的解决方案":
+//   - outliers recur in fixed channels across decode steps (Fig. 9), so the
+//     channel set is cached in device memory and re-used;
+//   - the amax needed for the quantization scale also says whether any
+//     outlier exists (amax greater than the threshold), so detection only
+//     matters when that amax, taken over the uncached channels, crosses the
+//     threshold (Fig. 10, the equivalent transform);
+//   - outliers go, in channel order, into a separate FP16 matrix (Fig. 11).
+//   Prior systems lost time to atomics (Fig. 8): here the steady-state path
+//   issues none.
+//
+// Two kernels per call, both on the caller's stream, one wave per token:
+//   gate_quant  one pass over X: masked amax, quantization with the cached
+//               set, X_out gather (a channel's column is its rank in the set,
+//               kept as a prefix-popcount table in the state).  Uncached
+//               values above the threshold -- the gate -- are marked in LDS
+//               and, only then, OR-ed into a pending bitmap with one marker.
+//   requant     reads the marker.  No marker: writes flag = 0 and exits.
+//               Marker: every block forms the union set and its rank table in
+//               LDS, re-quantizes its tokens with it, and the last block to
+//               finish commits the set (bitmap, ranks, ascending ids, count,
+//               flag) and clears the scratch.
+#include "mixq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace mixq {
+namespace {
+
+struct ActArgs {
+    const uint16_t* X;
+    int64_t M;
+    int32_t K;
+    int64_t ldx;
+    float tau;
+    int32_t* idx;
+    int32_t* count;
+    int32_t* flag;
+    uint32_t* bitmap;
+    uint32_t* pending;  // work[0, words)
+    int32_t* rank;      // work[words, 2 words): exclusive popcount prefix of bitmap
+    uint32_t* marker;   // work[2 words]
+    uint32_t* arrive;   // work[2 words + 1]
+    int32_t k_cap;
+    int32_t words;
+    int32_t nchunks;  // K / 8
+    int8_t* Xq;
+    float* s_x;
+    uint16_t* X_out;
+    int32_t ld_out;
+};
+
+__device__ __forceinline__ uint16_t half_at(const uint4& v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (uint16_t)(w >> ((e & 1) * 16));
+}
+
+// One token processed by one wave.  Chunk = 8 consecutive channels (16 B);
+// lane l owns chunks l, l+64, ... of each segment of 64*CPT chunks, so every
+// load instruction of the wave reads 1 KB of the row contiguously.
+//   set_words / rank: the set the token is quantized with (global or LDS)
+//   newbits: LDS detection bitmap, or null when detection is off
+// Returns (in every lane) whether this token had an uncached value above tau.
+template <int CPT>
+__device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_words,
+                         const int32_t* rank, int set_size, uint32_t* newbits) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint16_t* xr = a.X + row * a.ldx;
+    const int seg_chunks = kWave * CPT;
+    const int nseg = (a.nchunks + seg_chunks - 1) / seg_chunks;
+
+    uint4 xv[CPT];
+    uint32_t wv[CPT];
+    float am = 0.0f;
+    bool det = false;
+    for (int s = 0; s < nseg; ++s) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = s * seg_chunks + i * kWave + lane;
+            if (c < a.nchunks) {
+                xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
+                wv[i] = set_words[c >> 2];
+            } else {
+                xv[i] = make_uint4(0, 0, 0, 0);
+                wv[i] = 0xFFFFFFFFu;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = s * seg_chunks + i * kWave + lane;
+            const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
+            uint32_t over = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = fabsf(half_bits_to_float(half_at(xv[i], e)));
+                if (!((cb >> e) & 1u)) {
+                    am = fmaxf(am, v);
+                    if (v > a.tau) over |= 1u << e;
+                }
+            }
+            if (newbits && over) {
+                atomicOr(&newbits[c >> 2], over << ((c & 3) * 8));
+                det = true;
+            }
+        }
+    }
+    const float g = wave_max(am);
+
+    // Scale and reciprocal: single IEEE divisions; zero amax -> 1.
+    float sc, r;
+    if (g == 0.0f) {
+        sc = 1.0f;
+        r = 1.0f;
+    } else {
+        sc = g / 127.0f;
+        r = 127.0f / g;
+    }
+    if (lane == 0) a.s_x[row] = sc;
+
+    int8_t* qr = a.Xq + row * (int64_t)a.K;
+    uint16_t* orow = a.ld_out ? a.X_out + row * (int64_t)a.ld_out : nullptr;
+    for (int s = 0; s < nseg; ++s) {
+        if (nseg > 1) {  // the row did not fit in registers: read the segment again
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = s * seg_chunks + i * kWave + lane;
+                if (c < a.nchunks) {
+                    xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
+                    wv[i] = set_words[c >> 2];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = s * seg_chunks + i * kWave + lane;
+            if (c >= a.nchunks) continue;
+            const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t hb = half_at(xv[i], e);
+                int q = 0;
+                if (!((cb >> e) & 1u)) {
+                    float y = __builtin_rintf(half_bits_to_float(hb) * r);
+                    y = fminf(fmaxf(y, -127.0f), 127.0f);
+                    q = (int)y;
+                } else {
+                    // outlier channel: its column in X_out is its rank in the set
+                    const int bit = (c & 3) * 8 + e;
+                    const int j = rank[c >> 2] + __popc(wv[i] & ((1u << bit) - 1u));
+                    orow[j] = hb;
+                }
+                packed[e >> 2] |= ((uint32_t)q & 0xFFu) << ((e & 3) * 8);
+            }
+            *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) = make_uint2(packed[0], packed[1]);
+        }
+    }
+    if (orow) {
+        const int kpad = (set_size + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+        for (int j = set_size + lane; j < kpad; j += kWave) orow[j] = 0;
+    }
+    return __any(det);
+}
+
+template <int CPT>
+__global__ __launch_bounds__(kWave) void gate_quant_kernel(ActArgs a) {
+    extern __shared__ uint32_t newbits[];  // [words]
+    for (int w = threadIdx.x; w < a.words; w += kWave) newbits[w] = 0u;
+    __syncthreads();
+    const int set_size = *a.count;
+    bool det = false;
+    for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x)
+        det |= wave_row<CPT>(a, row, a.bitmap, a.rank, set_size, newbits);
+    __syncthreads();
+    if (det) {  // wave-uniform: only blocks whose tokens crossed the gate
+        for (int w = threadIdx.x; w < a.words; w += kWave)
+            if (newbits[w]) atomicOr(&a.pending[w], newbits[w]);
+        if (threadIdx.x == 0) atomicOr(a.marker, 1u);
+    }
+}
+
+// Exclusive prefix of popcount(src[w]) into prefix[w] (LDS); returns the total.
+// Block of any size; tot must hold one int per wave.
+__device__ int scan_popcounts(const uint32_t* src, int words, int* prefix, int* tot) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int nw = blockDim.x / kWave;
+    const int per = (words + blockDim.x - 1) / blockDim.x;
+    const int b = tid * per, e = min(words, b + per);
+    int local = 0;
+    for (int w = b; w < e; ++w) local += __popc(src[w]);
+    const int incl = wave_inclusive_scan(local);
+    if (lane == kWave - 1) tot[wave] = incl;
+    __syncthreads();
+    int off = 0, total = 0;
+    for (int w = 0; w < nw; ++w) {
+        off += (w < wave) ? tot[w] : 0;
+        total += tot[w];
+    }
+    int run = off + incl - local;
+    for (int w = b; w < e; ++w) {
+        prefix[w] = run;
+        run += __popc(src[w]);
+    }
+    __syncthreads();
+    return total;
+}
+
+constexpr int kReqThreads = 256;
+
+template <int CPT>
+__global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
+    if (*a.marker == 0u) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
+        return;
+    }
+    extern __shared__ uint32_t dyn[];
+    uint32_t* neww = dyn;                                // [words]
+    int32_t* prefix = reinterpret_cast<int32_t*>(dyn + a.words);  // [words]
+    __shared__ int tot[kReqThreads / kWave];
+    __shared__ int last;
+
+    for (int w = threadIdx.x; w < a.words; w += kReqThreads) neww[w] = a.bitmap[w] | a.pending[w];
+    __syncthreads();
+    const int total = scan_popcounts(neww, a.words, prefix, tot);
+    const bool overflow = total > a.k_cap;
+    if (!overflow) {
+        const int wave = threadIdx.x / kWave;
+        const int64_t stride = (int64_t)gridDim.x * (kReqThreads / kWave);
+        for (int64_t row = (int64_t)blockIdx.x * (kReqThreads / kWave) + wave; row < a.M;
+             row += stride)
+            wave_row<CPT>(a, row, neww, prefix, total, nullptr);
+    }
+    // arrival (fired calls only): the last block commits
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        last = atomicAdd(a.arrive, 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    for (int w = threadIdx.x; w < a.words; w += kReqThreads) {
+        if (!overflow) {
+            uint32_t bits = neww[w];
+            int j = prefix[w];
+            a.bitmap[w] = bits;
+            a.rank[w] = j;
+            while (bits) {
+                a.idx[j++] = w * 32 + __builtin_ctz(bits);
+                bits &= bits - 1u;
+            }
+        }
+        a.pending[w] = 0u;
+    }
+    if (threadIdx.x == 0) {
+        if (!overflow) *a.count = total;
+        *a.flag = overflow ? MIXQ_FLAG_OVERFLOW : MIXQ_FLAG_FIRED;
+        *a.marker = 0u;
+        *a.arrive = 0u;
+    }
+}
+
+template <int CPT>
+int launch_act(const ActArgs& a, hipStream_t st) {
+    const int grid = (int)(a.M < 4096 ? a.M : 4096);
+    hipLaunchKernelGGL(gate_quant_kernel<CPT>, dim3(grid), dim3(kWave), (size_t)a.words * 4, st,
+                       a);
+    int rc = launch_status();
+    if (rc != MIXQ_OK) return rc;
+    const int64_t rows_per_block = kReqThreads / kWave;
+    int64_t g2 = (a.M + rows_per_block - 1) / rows_per_block;
+    if (g2 > 128) g2 = 128;
+    hipLaunchKernelGGL(requant_kernel<CPT>, dim3((int)g2), dim3(kReqThreads),
+                       (size_t)a.words * 8, st, a);
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace mixq
+
+extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                 float threshold, const mixq_act_state* state, int8_t* Xq,
+                                 float* s_x, uint16_t* X_out, void* stream) {
+    using namespace mixq;
+    if (!X || !state || !Xq || !s_x) return MIXQ_ERR_INVALID_ARG;
+    if (!state->idx && state->k_cap > 0) return MIXQ_ERR_INVALID_ARG;
+    if (!state->count || !state->flag || !state->bitmap || !state->work)
+        return MIXQ_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || ldx < K) return MIXQ_ERR_INVALID_ARG;
+    if (!(threshold >= 0.0f) || !isfinite(threshold)) return MIXQ_ERR_INVALID_ARG;
+    if (state->k_cap < 0 || state->k_cap > K) return MIXQ_ERR_INVALID_ARG;
+    if (state->k_cap > 0 && !X_out) return MIXQ_ERR_INVALID_ARG;
+    if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (ldx % 8 != 0 || ((uintptr_t)X & 15u) != 0 || ((uintptr_t)Xq & 15u) != 0)
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (M > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    int rc = check_device_cached();
+    if (rc != MIXQ_OK) return rc;
+
+    ActArgs a;
+    const int32_t words = (int32_t)bitmap_words(K);
+    a.X = X;
+    a.M = M;
+    a.K = (int32_t)K;
+    a.ldx = ldx;
+    a.tau = threshold;
+    a.idx = state->idx;
+    a.count = state->count;
+    a.flag = state->flag;
+    a.bitmap = state->bitmap;
+    a.pending = state->work;
+    a.rank = reinterpret_cast<int32_t*>(state->work + words);
+    a.marker = state->work + 2 * words;
+    a.arrive = state->work + 2 * words + 1;
+    a.k_cap = state->k_cap;
+    a.words = words;
+    a.nchunks = (int32_t)(K / 8);
+    a.Xq = Xq;
+    a.s_x = s_x;
+    a.X_out = state->k_cap > 0 ? X_out : nullptr;
+    a.ld_out = (int32_t)outlier_ld(state->k_cap);
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // chunks per lane and segment: the whole row in registers up to K = 8192
+    const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
+    if (per_lane <= 1) return launch_act<1>(a, st);
+    if (per_lane <= 2) return launch_act<2>(a, st);
+    if (per_lane <= 4) return launch_act<4>(a, st);
+    if (per_lane <= 8) return launch_act<8>(a, st);
+    return launch_act<16>(a, st);
+}

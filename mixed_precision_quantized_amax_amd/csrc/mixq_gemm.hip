@@ -1,0 +1,480 @@
+// The mixed-precision GEMM: INT8 x INT8 (or INT8 x INT4) main product on
+// gfx950 i8 matrix cores, FP16 outlier product on f16 matrix cores, fused
+// dequantize / scale / add epilogue, one kernel.
+//
+// MixQ article: section "研究背景：已有量化技术总结", Fig. 5 -- the product is
+// split into a low-bit part and an FP16 outlier part whose results are
+// added; section "MixQ的解决方案", Fig. 12 -- the low-precision result is
+// dequantized in registers and added to the high-precision one.
+// QServe notes, "寄存器压力和并行性" -- keeping two sets of partial sums (one
+// int32, one fp32) costs registers and occupancy; here the int32
+// accumulators are converted in place once, after the K loop, and the fp32
+// values then serve as the C operand of the f16 outlier MFMAs, so only one
+// accumulator set is ever live.  INT4 weights are decoded to INT8 on their
+// way into LDS ("小结": decode inside the main loop, all products on INT8
+// units).
+//
+// Tiling (CDNA4, wave64):
+//   block tile BM x BN, K step 64 bytes; waves arranged WM x WN, each owning
+//   a (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA fragments
+//   (v_mfma_i32_32x32x32_i8: 16 B of A and 16 B of B per lane, 16 int32
+//   results per lane).
+//   Operand tiles live in LDS as rows of 64 bytes = four 16-byte chunks;
+//   chunk c of row r is stored at slot c ^ swz(r) so that both the
+//   row-contiguous writes and the MFMA fragment reads (32 rows, one chunk
+//   each) hit distinct banks.
+//   Two LDS stages: global loads for tile k+1 are in flight in registers
+//   while tile k is multiplied.
+//   Tile order: consecutive block ids go to different XCDs (round-robin), so
+//   block ids are remapped to give each XCD a compact rectangle of tiles that
+//   share A rows and B rows in its L2.
+#include <stdlib.h>
+
+#include "mixq_internal.h"
+
+namespace mixq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kBK = 64;  // bytes of K per tile: 64 int8 codes or 32 fp16 values
+
+struct GemmArgs {
+    const int8_t* Xq;
+    const float* s_x;
+    const uint16_t* X_out;
+    const int32_t* count;
+    const void* wq;
+    const float* s_w;
+    const uint16_t* w_out;
+    int32_t ld_out;
+    int32_t M, N, K;
+    float* Y;
+    int64_t ldy;
+    int32_t* acc_debug;
+    int32_t tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ swz(r)) << 4); }
+
+// Sign-extend eight 4-bit codes held as the low nibbles of four bytes.
+__device__ __forceinline__ uint32_t sext_nibbles(uint32_t v) {
+    const uint32_t s = v & 0x08080808u;
+    return v | ((s << 5) - (s << 1));  // s * 0x1E: 0x08 -> 0xF0 per byte, no carries
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0,
+// which covers the ragged last tile rows without clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (<= n, n < 64).
+#define MIXQ_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8)))
+
+template <int BM, int BN, int WM, int WN, int BITS>
+struct Cfg {
+    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int kNW = WM * WN;
+    static constexpr int kWTM = BM / WM;
+    static constexpr int kWTN = BN / WN;
+    static constexpr int kFM = kWTM / 32;
+    static constexpr int kFN = kWTN / 32;
+    // one load instruction of a wave fills 16 rows x 64 B (int8 / fp16 rows)
+    static constexpr int kAI = BM / 16 / kNW;
+    static constexpr int kBI = BN / 16 / kNW;
+    // packed INT4 rows: 32 rows x 32 B per wave instruction
+    static constexpr int kBI4 = BN / 32 / kNW;
+    static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "tile/wave mismatch");
+    static_assert(BM % (16 * kNW) == 0 && BN % (32 * kNW) == 0, "loader mismatch");
+};
+
+// STAGES == 2: global -> VGPR -> LDS, double-buffered LDS.
+// STAGES >= 3: global -> LDS directly (buffer_load ... lds), STAGES-deep ring.
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES, bool DEBUG>
+__global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
+    using C = Cfg<BM, BN, WM, WN, BITS>;
+    static_assert(STAGES == 2 || BITS == 8, "INT4 weights use the register-staged loader");
+    __shared__ __attribute__((aligned(1024))) uint8_t As[STAGES][BM * kBK];
+    __shared__ __attribute__((aligned(1024))) uint8_t Bs[STAGES][BN * kBK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // ---- block id -> tile, XCD-aware ------------------------------------------
+    int bid = blockIdx.x;
+    const int T = gridDim.x;
+    if ((T & 7) == 0) bid = (bid & 7) * (T >> 3) + (bid >> 3);
+    const int gm = a.tiles_m < 8 ? a.tiles_m : 8;
+    const int group = bid / (gm * a.tiles_n);
+    const int first_m = group * gm;
+    const int gsize = min(gm, a.tiles_m - first_m);
+    const int within = bid - group * gm * a.tiles_n;
+    const int tm = first_m + within % gsize;
+    const int tn = within / gsize;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int K = a.K;
+    const int KT = K / kBK;
+    const int rows_a = min(BM, a.M - m0);
+    const int rows_b = min(BN, a.N - n0);
+    const int wrow_bytes = BITS == 8 ? K : K / 2;
+
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.Xq + (int64_t)m0 * K, (int64_t)rows_a * K);
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(static_cast<const uint8_t*>(a.wq) + (int64_t)n0 * wrow_bytes,
+                  (int64_t)rows_b * wrow_bytes);
+
+    // ---- per-lane load slots ------------------------------------------------------
+    // Wave instruction i fills rows R0..R0+15 (R0 = (i*NW + wave)*16); lane l
+    // writes LDS bytes R0*64 + 16*l, i.e. row R0 + l/4, slot l%4, which holds
+    // chunk (l%4) ^ swz(row) of that row.
+    int voffA[C::kAI], voffB[C::kBI];
+#pragma unroll
+    for (int i = 0; i < C::kAI; ++i) {
+        const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+        voffA[i] = row * K + (((lane & 3) ^ swz(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kBI; ++i) {
+        const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+        voffB[i] = row * K + (((lane & 3) ^ swz(row)) << 4);
+    }
+    // INT4: wave instruction i covers packed rows R0..R0+31, lane -> row R0 + l/2, half l%2
+    int voffB4[C::kBI4];
+#pragma unroll
+    for (int i = 0; i < C::kBI4; ++i) {
+        const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
+        voffB4[i] = row * (K / 2) + ((lane & 1) << 4);
+    }
+
+    // ---- per-lane fragment read offsets (bytes within a stage) ------------------------
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    int rdA[2], rdB[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        rdA[ks] = (wm * C::kWTM + fr) * kBK + (((2 * ks + fh) ^ swz(fr)) << 4);
+        rdB[ks] = (wn * C::kWTN + fr) * kBK + (((2 * ks + fh) ^ swz(fr)) << 4);
+    }
+
+    v16i acc[C::kFM][C::kFN];
+#pragma unroll
+    for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kFN; ++j) acc[i][j] = v16i{};
+
+    auto mma_tile = [&](const uint8_t* Ab, const uint8_t* Bb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            v4i af[C::kFM], bf[C::kFN];
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+                af[i] = *reinterpret_cast<const v4i*>(Ab + rdA[ks] + i * 32 * kBK);
+#pragma unroll
+            for (int j = 0; j < C::kFN; ++j)
+                bf[j] = *reinterpret_cast<const v4i*>(Bb + rdB[ks] + j * 32 * kBK);
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kFN; ++j)
+                    acc[i][j] =
+                        __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    if constexpr (STAGES == 2) {
+        // ---- register-staged, double-buffered ---------------------------------------
+        v4i ra[C::kAI];
+        v4i rb[BITS == 8 ? C::kBI : C::kBI4];
+        auto gload = [&](int kt) {
+#pragma unroll
+            for (int i = 0; i < C::kAI; ++i)
+                ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA[i], kt * kBK, 0);
+            if constexpr (BITS == 8) {
+#pragma unroll
+                for (int i = 0; i < C::kBI; ++i)
+                    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[i], kt * kBK, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::kBI4; ++i)
+                    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+            }
+        };
+        auto lstore = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < C::kAI; ++i)
+                *reinterpret_cast<v4i*>(&As[buf][((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                    ra[i];
+            if constexpr (BITS == 8) {
+#pragma unroll
+                for (int i = 0; i < C::kBI; ++i)
+                    *reinterpret_cast<v4i*>(
+                        &Bs[buf][((i * C::kNW + wave) * 16) * kBK + lane * 16]) = rb[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::kBI4; ++i) {
+                    const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
+                    const int c2 = lane & 1;
+                    const uint32_t w0 = rb[i][0], w1 = rb[i][1], w2 = rb[i][2], w3 = rb[i][3];
+                    v4i lo, hi;
+                    lo[0] = (int)sext_nibbles(w0 & 0x0F0F0F0Fu);
+                    lo[1] = (int)sext_nibbles((w0 >> 4) & 0x0F0F0F0Fu);
+                    lo[2] = (int)sext_nibbles(w1 & 0x0F0F0F0Fu);
+                    lo[3] = (int)sext_nibbles((w1 >> 4) & 0x0F0F0F0Fu);
+                    hi[0] = (int)sext_nibbles(w2 & 0x0F0F0F0Fu);
+                    hi[1] = (int)sext_nibbles((w2 >> 4) & 0x0F0F0F0Fu);
+                    hi[2] = (int)sext_nibbles(w3 & 0x0F0F0F0Fu);
+                    hi[3] = (int)sext_nibbles((w3 >> 4) & 0x0F0F0F0Fu);
+                    *reinterpret_cast<v4i*>(&Bs[buf][lds_off(row, 2 * c2)]) = lo;
+                    *reinterpret_cast<v4i*>(&Bs[buf][lds_off(row, 2 * c2 + 1)]) = hi;
+                }
+            }
+        };
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < KT) gload(kt + 1);
+            mma_tile(As[cur], Bs[cur]);
+            if (kt + 1 < KT) lstore(cur ^ 1);
+            __syncthreads();
+        }
+    } else {
+        // ---- direct global -> LDS, STAGES-deep ring -----------------------------------
+        constexpr int kLoads = C::kAI + C::kBI;  // per thread per tile
+        auto issue = [&](int kt, int buf) {
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts exist only in the device pass
+#pragma unroll
+            for (int i = 0; i < C::kAI; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rA, (lds_ptr_t)(&As[buf][((i * C::kNW + wave) * 16) * kBK]), 16, voffA[i],
+                    kt * kBK, 0, 0);
+#pragma unroll
+            for (int i = 0; i < C::kBI; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rB, (lds_ptr_t)(&Bs[buf][((i * C::kNW + wave) * 16) * kBK]), 16, voffB[i],
+                    kt * kBK, 0, 0);
+#endif
+        };
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < KT) issue(s, s);
+        for (int kt = 0; kt < KT; ++kt) {
+            // tiles kt+1 .. kt+STAGES-2 may stay in flight
+            const int ahead = min(KT - 1 - kt, STAGES - 2);
+            if (ahead >= 2) {
+                MIXQ_WAIT_VMCNT(2 * kLoads);
+            } else if (ahead == 1) {
+                MIXQ_WAIT_VMCNT(kLoads);
+            } else {
+                MIXQ_WAIT_VMCNT(0);
+            }
+            __syncthreads();
+            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+            mma_tile(As[kt % STAGES], Bs[kt % STAGES]);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: dequantize and scale in registers, in place ---------------------
+    // 32x32 fragment layout: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32
+    const int count = *a.count;
+    const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+
+    float sw[C::kFN];
+#pragma unroll
+    for (int j = 0; j < C::kFN; ++j) {
+        const int col = n0 + wn * C::kWTN + j * 32 + fr;
+        sw[j] = a.s_w[min(col, a.N - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < C::kFM; ++i) {
+        float sx[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = m0 + wm * C::kWTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+            sx[e] = a.s_x[min(row, a.M - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < C::kFN; ++j) {
+            if constexpr (DEBUG) {
+                const int col = n0 + wn * C::kWTN + j * 32 + fr;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = m0 + wm * C::kWTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+                    if (row < a.M && col < a.N)
+                        a.acc_debug[(int64_t)row * a.N + col] = acc[i][j][e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = __float_as_int(((float)acc[i][j][e] * sx[e]) * sw[j]);
+        }
+    }
+
+    // ---- outlier product: fp16 x fp16 -> fp32, accumulated onto the dequantized tile --
+    if (kpad > 0) {
+        const int ldb = a.ld_out * 2;  // bytes per outlier row
+        const __amdgpu_buffer_rsrc_t rXo =
+            make_rsrc(reinterpret_cast<const uint8_t*>(a.X_out) + (int64_t)m0 * ldb,
+                      (int64_t)rows_a * ldb);
+        const __amdgpu_buffer_rsrc_t rWo =
+            make_rsrc(reinterpret_cast<const uint8_t*>(a.w_out) + (int64_t)n0 * ldb,
+                      (int64_t)rows_b * ldb);
+        for (int kt2 = 0; kt2 < kpad / 32; ++kt2) {
+#pragma unroll
+            for (int i = 0; i < C::kAI; ++i) {
+                const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+                const int off = row * ldb + (((lane & 3) ^ swz(row)) << 4);
+                *reinterpret_cast<v4i*>(&As[0][((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                    __builtin_amdgcn_raw_buffer_load_b128(rXo, off, kt2 * kBK, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < C::kBI; ++i) {
+                const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+                const int off = row * ldb + (((lane & 3) ^ swz(row)) << 4);
+                *reinterpret_cast<v4i*>(&Bs[0][((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                    __builtin_amdgcn_raw_buffer_load_b128(rWo, off, kt2 * kBK, 0);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                v8h af[C::kFM], bf[C::kFN];
+#pragma unroll
+                for (int i = 0; i < C::kFM; ++i)
+                    af[i] = *reinterpret_cast<const v8h*>(&As[0][rdA[ks] + i * 32 * kBK]);
+#pragma unroll
+                for (int j = 0; j < C::kFN; ++j)
+                    bf[j] = *reinterpret_cast<const v8h*>(&Bs[0][rdB[ks] + j * 32 * kBK]);
+#pragma unroll
+                for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::kFN; ++j) {
+                        v16f yv = __builtin_bit_cast(v16f, acc[i][j]);
+                        yv = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], yv, 0, 0, 0);
+                        acc[i][j] = __builtin_bit_cast(v16i, yv);
+                    }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- store Y (fp32) ---------------------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kFN; ++j) {
+            const int col = n0 + wn * C::kWTN + j * 32 + fr;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * C::kWTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+                if (row < a.M && col < a.N)
+                    a.Y[(int64_t)row * a.ldy + col] = __int_as_float(acc[i][j][e]);
+            }
+        }
+}
+
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES>
+int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.tiles_n = (a.N + BN - 1) / BN;
+    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * kWave);
+    if (debug)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, false>), grid, block, 0, st, a);
+    return launch_status();
+}
+
+// Tile configurations; MIXQ_GEMM_TILE=<id> forces one (0 = automatic).
+enum {
+    kCfgAuto = 0,
+    kCfg256x256 = 1,   // 4 waves of 128x128, register-staged
+    kCfg128x128 = 2,   // 4 waves of 64x64, register-staged
+    kCfg256x256D = 3,  // 4 waves of 128x128, direct-to-LDS, 3 stages
+    kCfg256x128 = 4,   // 4 waves of 128x64, register-staged
+};
+
+int forced_cfg() {
+    const char* e = getenv("MIXQ_GEMM_TILE");
+    return e ? atoi(e) : 0;
+}
+
+int pick_cfg(int64_t M, int64_t N, int bits) {
+    const int f = forced_cfg();
+    if (f >= 1 && f <= 4 && !(bits == 4 && f == kCfg256x256D)) return f;
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    return big >= 192 ? kCfg256x256 : kCfg128x128;
+}
+
+int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
+    switch (pick_cfg(a.M, a.N, 8)) {
+        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 8, 2>(a, debug, st);
+        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 8, 2>(a, debug, st);
+        case kCfg256x256D: return launch_cfg<256, 256, 2, 2, 8, 3>(a, debug, st);
+        default: return launch_cfg<128, 128, 2, 2, 8, 2>(a, debug, st);
+    }
+}
+
+int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
+    switch (pick_cfg(a.M, a.N, 4)) {
+        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2>(a, debug, st);
+        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2>(a, debug, st);
+        default: return launch_cfg<128, 128, 2, 2, 4, 2>(a, debug, st);
+    }
+}
+
+}  // namespace
+}  // namespace mixq
+
+extern "C" int mixq_gemm(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
+                         const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,
+                         int64_t ldy, int32_t* acc_debug, void* stream) {
+    using namespace mixq;
+    if (!Xq || !s_x || !state || !w || !Y) return MIXQ_ERR_INVALID_ARG;
+    if (!state->count || !w->wq || !w->s_w) return MIXQ_ERR_INVALID_ARG;
+    if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < w->N) return MIXQ_ERR_INVALID_ARG;
+    if (w->bits != 8 && w->bits != 4) return MIXQ_ERR_INVALID_ARG;
+    if (state->k_cap < 0 || state->k_cap > w->K || w->k_cap != state->k_cap)
+        return MIXQ_ERR_INVALID_ARG;
+    if (state->k_cap > 0 && (!X_out || !w->w_out)) return MIXQ_ERR_INVALID_ARG;
+    if (!valid_k(w->K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (M > (1 << 30) || w->N > (1 << 30)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (((uintptr_t)Xq & 15u) || ((uintptr_t)w->wq & 15u) || ((uintptr_t)X_out & 15u) ||
+        ((uintptr_t)w->w_out & 15u))
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    int rc = check_device_cached();
+    if (rc != MIXQ_OK) return rc;
+
+    GemmArgs a;
+    a.Xq = Xq;
+    a.s_x = s_x;
+    a.X_out = X_out;
+    a.count = state->count;
+    a.wq = w->wq;
+    a.s_w = w->s_w;
+    a.w_out = w->w_out;
+    a.ld_out = (int32_t)outlier_ld(state->k_cap);
+    a.M = (int32_t)M;
+    a.N = (int32_t)w->N;
+    a.K = (int32_t)w->K;
+    a.Y = Y;
+    a.ldy = ldy;
+    a.acc_debug = acc_debug;
+    a.tiles_m = a.tiles_n = 0;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return w->bits == 8 ? launch_w8(a, acc_debug != nullptr, st)
+                        : launch_w4(a, acc_debug != nullptr, st);
+}

@@ -1,0 +1,75 @@
+// Internal helpers of the mixq library (host validation, device check,
+// small device utilities).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mixq.h"
+
+namespace mixq {
+
+constexpr int kWave = 64;
+
+// ---- host side -------------------------------------------------------------
+int check_device_cached();  // MIXQ_OK / MIXQ_ERR_NO_DEVICE / MIXQ_ERR_UNSUPPORTED_DEVICE
+
+inline bool valid_k(int64_t K) { return K > 0 && K % MIXQ_K_MULTIPLE == 0 && K <= MIXQ_K_MAX; }
+
+inline int64_t outlier_ld(int32_t k_cap) {
+    return ((int64_t)k_cap + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+}
+
+inline int64_t bitmap_words(int64_t K) { return (K + 31) / 32; }
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MIXQ_OK : MIXQ_ERR_HIP;
+}
+
+// ---- device side -------------------------------------------------------------
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+    _Float16 v;
+    __builtin_memcpy(&v, &h, 2);
+    return (float)v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Device-scope (L2) load that bypasses the non-coherent per-CU cache.
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace mixq

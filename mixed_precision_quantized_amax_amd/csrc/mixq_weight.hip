@@ -1,0 +1,180 @@
+// Weight side of the mixed-precision linear layer: per-output-channel
+// symmetric INT8 / INT4 quantization and the FP16 outlier columns.
+//
+// FP6 explainer, section 3: each output channel's scale is its max |w| over
+// the code range, a zero scale becomes 1, values round to nearest; weights
+// are quantized once, when the layer is loaded.
+// MixQ article, section "MixQ的解决方案", Fig. 11: the outlier channels are
+// concatenated in order into a separate FP16 matrix -- here the weight's
+// columns at those channels, w_out[n, j] = W[n, idx[j]].
+// QServe notes, "寄存器压力和并行性" / "小结": INT4 weights are decoded to INT8
+// inside the GEMM; the nibble layout below lets one 32-bit word expand into
+// eight INT8 codes with a few bitwise operations.
+#include "mixq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace mixq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <int CPT, int BITS>
+__global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_t* __restrict__ W,
+                                                                    int64_t N, int32_t K,
+                                                                    void* __restrict__ wq,
+                                                                    float* __restrict__ s_w) {
+    __shared__ float red[kWaves];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int nchunks = K / 8;
+    constexpr float kQ = BITS == 8 ? 127.0f : 7.0f;
+    for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+        const uint16_t* wr = W + n * (int64_t)K;
+        uint4 v[CPT];
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            v[i] = c < nchunks ? *reinterpret_cast<const uint4*>(wr + (int64_t)c * 8)
+                               : make_uint4(0, 0, 0, 0);
+            const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                am = fmaxf(am, fabsf(half_bits_to_float((uint16_t)(u[e >> 1] >> ((e & 1) * 16)))));
+        }
+        am = wave_max(am);
+        if (lane == 0) red[wave] = am;
+        __syncthreads();
+        float g = red[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) g = fmaxf(g, red[w]);
+        __syncthreads();
+
+        float s, rho;
+        if (g == 0.0f) {
+            s = 1.0f;
+            rho = 1.0f;
+        } else {
+            s = g / kQ;
+            rho = kQ / g;
+        }
+        if (tid == 0) s_w[n] = s;
+
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (c >= nchunks) continue;
+            const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            int q[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float y = __builtin_rintf(
+                    half_bits_to_float((uint16_t)(u[e >> 1] >> ((e & 1) * 16))) * rho);
+                y = fminf(fmaxf(y, -kQ), kQ);
+                q[e] = (int)y;
+            }
+            if (BITS == 8) {
+                uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p0 |= ((uint32_t)q[e] & 0xFFu) << (8 * e);
+                    p1 |= ((uint32_t)q[e + 4] & 0xFFu) << (8 * e);
+                }
+                int8_t* dst = static_cast<int8_t*>(wq) + n * (int64_t)K + (int64_t)c * 8;
+                *reinterpret_cast<uint2*>(dst) = make_uint2(p0, p1);
+            } else {
+                // one word per 8 consecutive k: byte j = q[j] | q[j+4] << 4
+                uint32_t word = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    word |= (((uint32_t)q[j] & 0xFu) | (((uint32_t)q[j + 4] & 0xFu) << 4)) << (8 * j);
+                uint8_t* dst = static_cast<uint8_t*>(wq) + n * (int64_t)(K / 2) + (int64_t)c * 4;
+                *reinterpret_cast<uint32_t*>(dst) = word;
+            }
+        }
+    }
+}
+
+// w_out[n, j] = W[n, idx[j]] for j < count, zeros up to the padded width.
+// Block b owns rows b, b + G, b + 2G, ... (G = gridDim.x, fixed for a given N)
+// and slot k_out[b], the set size its rows were last gathered for: it runs
+// when forced or when that differs from the state's count.  No block reads
+// another block's slot, so the check needs no atomics.
+__global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* __restrict__ W,
+                                                               int64_t N, int32_t K,
+                                                               const int32_t* __restrict__ idx,
+                                                               const int32_t* __restrict__ count_p,
+                                                               uint16_t* __restrict__ w_out,
+                                                               int32_t ld_out, int32_t* k_out,
+                                                               int force) {
+    const int count = *count_p;
+    if (!force && k_out[blockIdx.x] == count) return;
+    const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+    const int64_t G = gridDim.x;
+    const int64_t my_rows = (N - blockIdx.x + G - 1) / G;
+    const int64_t total = my_rows * kpad;
+    for (int64_t t = threadIdx.x; t < total; t += kThreads) {
+        const int64_t n = blockIdx.x + (t / kpad) * G;
+        const int j = (int)(t % kpad);
+        w_out[n * ld_out + j] = j < count ? W[n * (int64_t)K + idx[j]] : (uint16_t)0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) k_out[blockIdx.x] = count;
+}
+
+template <int CPT>
+int launch_quant(const uint16_t* W, int64_t N, int32_t K, int bits, const mixq_weight* w,
+                 hipStream_t st) {
+    const int grid = (int)(N < 4096 ? N : 4096);
+    if (bits == 8)
+        hipLaunchKernelGGL((quantize_weight_kernel<CPT, 8>), dim3(grid), dim3(kThreads), 0, st, W,
+                           N, K, w->wq, w->s_w);
+    else
+        hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4>), dim3(grid), dim3(kThreads), 0, st, W,
+                           N, K, w->wq, w->s_w);
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace mixq
+
+extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t bits,
+                                const mixq_act_state* state, int32_t mode, const mixq_weight* w,
+                                void* stream) {
+    using namespace mixq;
+    if (!W || !state || !w) return MIXQ_ERR_INVALID_ARG;
+    if (N <= 0 || K <= 0) return MIXQ_ERR_INVALID_ARG;
+    if (bits != 8 && bits != 4) return MIXQ_ERR_INVALID_ARG;
+    if (mode != MIXQ_PACK_FULL && mode != MIXQ_PACK_OUTLIER_COLS) return MIXQ_ERR_INVALID_ARG;
+    if (w->N != N || w->K != K || w->bits != bits || w->k_cap != state->k_cap)
+        return MIXQ_ERR_INVALID_ARG;
+    if (!w->wq || !w->s_w || !w->k_out) return MIXQ_ERR_INVALID_ARG;
+    if (state->k_cap < 0 || state->k_cap > K) return MIXQ_ERR_INVALID_ARG;
+    if (state->k_cap > 0 && (!w->w_out || !state->idx)) return MIXQ_ERR_INVALID_ARG;
+    if (!state->count) return MIXQ_ERR_INVALID_ARG;
+    if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (((uintptr_t)W & 15u) != 0 || ((uintptr_t)w->wq & 15u) != 0)
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (N > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    int rc = check_device_cached();
+    if (rc != MIXQ_OK) return rc;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (mode == MIXQ_PACK_FULL) {
+        const int64_t cpt = (K / 8 + kThreads - 1) / kThreads;
+        if (cpt <= 1) rc = launch_quant<1>(W, N, (int32_t)K, bits, w, st);
+        else if (cpt <= 2) rc = launch_quant<2>(W, N, (int32_t)K, bits, w, st);
+        else if (cpt <= 4) rc = launch_quant<4>(W, N, (int32_t)K, bits, w, st);
+        else if (cpt <= 8) rc = launch_quant<8>(W, N, (int32_t)K, bits, w, st);
+        else if (cpt <= 16) rc = launch_quant<16>(W, N, (int32_t)K, bits, w, st);
+        else rc = launch_quant<32>(W, N, (int32_t)K, bits, w, st);
+        if (rc != MIXQ_OK) return rc;
+    }
+    const int ld_out = (int)outlier_ld(state->k_cap);
+    const int grid = (int)(N < MIXQ_GATHER_SLOTS ? N : MIXQ_GATHER_SLOTS);
+    hipLaunchKernelGGL(gather_cols_kernel, dim3(grid), dim3(kThreads), 0, st, W, N, (int32_t)K,
+                       state->idx, state->count, w->w_out, ld_out, w->k_out,
+                       mode == MIXQ_PACK_FULL ? 1 : 0);
+    return launch_status();
+}

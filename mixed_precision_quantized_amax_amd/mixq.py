@@ -1,0 +1,290 @@
+"""Python binding of ``libmixq.so`` (the C ABI declared in ``include/mixq.h``).
+
+Argument marshalling only: torch tensors supply device memory and the
+current stream; every step of the layer runs in the library's HIP kernels.
+There is no fallback -- if the library is missing or the device is not a
+gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmixq.so")
+
+MIXQ_OK = 0
+STATUS = {0: "MIXQ_OK", 1: "MIXQ_ERR_INVALID_ARG", 2: "MIXQ_ERR_UNSUPPORTED_SHAPE",
+          3: "MIXQ_ERR_UNSUPPORTED_DEVICE", 4: "MIXQ_ERR_NO_DEVICE", 5: "MIXQ_ERR_HIP"}
+FLAG_FIRED = 1
+FLAG_OVERFLOW = 2
+PACK_FULL = 0
+PACK_OUTLIER_COLS = 1
+OUTLIER_ALIGN = 32
+K_MULTIPLE = 64
+GATHER_SLOTS = 256
+
+
+class MixqError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({msg})")
+        self.code = code
+
+
+class ActState(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("flag", ctypes.c_void_p), ("bitmap", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("k_cap", ctypes.c_int32)]
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
+                ("k_out", ctypes.c_void_p), ("bits", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("k_cap", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m mixed_precision_quantized_amax_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.mixq_outlier_ld.argtypes = [I32]
+        L.mixq_outlier_ld.restype = I64
+        L.mixq_bitmap_words.argtypes = [I64]
+        L.mixq_bitmap_words.restype = I64
+        L.mixq_state_work_words.argtypes = [I64]
+        L.mixq_state_work_words.restype = I64
+        L.mixq_packed_weight_bytes.argtypes = [I64, I64, I32]
+        L.mixq_packed_weight_bytes.restype = ctypes.c_size_t
+        L.mixq_quantize_act.argtypes = [P, I64, I64, I64, ctypes.c_float,
+                                        ctypes.POINTER(ActState), P, P, P, P]
+        L.mixq_quantize_act.restype = ctypes.c_int
+        L.mixq_pack_weight.argtypes = [P, I64, I64, I32, ctypes.POINTER(ActState), I32,
+                                       ctypes.POINTER(Weight), P]
+        L.mixq_pack_weight.restype = ctypes.c_int
+        L.mixq_gemm.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
+                                P, I64, P, P]
+        L.mixq_gemm.restype = ctypes.c_int
+        L.mixq_status_string.argtypes = [ctypes.c_int]
+        L.mixq_status_string.restype = ctypes.c_char_p
+        L.mixq_check_device.argtypes = []
+        L.mixq_check_device.restype = ctypes.c_int
+        L.mixq_version.argtypes = []
+        L.mixq_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != MIXQ_OK:
+        raise MixqError(fn, rc, lib().mixq_status_string(rc).decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def outlier_ld(k_cap: int) -> int:
+    return int(lib().mixq_outlier_ld(k_cap))
+
+
+def bitmap_words(K: int) -> int:
+    return int(lib().mixq_bitmap_words(K))
+
+
+@dataclass
+class OutlierState:
+    """Device memory of one cached outlier-channel set (zero = empty)."""
+    K: int
+    k_cap: int
+    idx: torch.Tensor
+    count: torch.Tensor
+    flag: torch.Tensor
+    bitmap: torch.Tensor
+    work: torch.Tensor
+
+    @classmethod
+    def create(cls, K: int, k_cap: int, device="cuda") -> "OutlierState":
+        w = bitmap_words(K)
+        ww = int(lib().mixq_state_work_words(K))
+        z = lambda n, dt: torch.zeros(max(n, 1), dtype=dt, device=device)  # noqa: E731
+        return cls(K=K, k_cap=k_cap, idx=z(k_cap, torch.int32), count=z(1, torch.int32),
+                   flag=z(1, torch.int32), bitmap=z(w, torch.int32), work=z(ww, torch.int32))
+
+    def c(self) -> ActState:
+        return ActState(self.idx.data_ptr(), self.count.data_ptr(), self.flag.data_ptr(),
+                        self.bitmap.data_ptr(), self.work.data_ptr(), self.k_cap)
+
+    def reset(self):
+        for t in (self.idx, self.count, self.flag, self.bitmap, self.work):
+            t.zero_()
+
+
+@dataclass
+class PackedWeight:
+    N: int
+    K: int
+    bits: int
+    k_cap: int
+    wq: torch.Tensor
+    s_w: torch.Tensor
+    w_out: torch.Tensor
+    k_out: torch.Tensor
+
+    @classmethod
+    def create(cls, N: int, K: int, bits: int, k_cap: int, device="cuda") -> "PackedWeight":
+        nbytes = int(lib().mixq_packed_weight_bytes(N, K, bits))
+        if nbytes == 0:
+            raise ValueError("invalid weight shape or bits")
+        ld = outlier_ld(k_cap)
+        return cls(N=N, K=K, bits=bits, k_cap=k_cap,
+                   wq=torch.empty(nbytes, dtype=torch.uint8, device=device),
+                   s_w=torch.empty(N, dtype=torch.float32, device=device),
+                   w_out=torch.zeros(max(N * ld, 1), dtype=torch.float16, device=device),
+                   k_out=torch.zeros(GATHER_SLOTS, dtype=torch.int32, device=device))
+
+    def c(self) -> Weight:
+        return Weight(self.wq.data_ptr(), self.s_w.data_ptr(), self.w_out.data_ptr(),
+                      self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap)
+
+    def codes_view(self) -> torch.Tensor:
+        """int8 [N, K] (bits 8) or packed uint8 [N, K/2] (bits 4) view of wq."""
+        if self.bits == 8:
+            return self.wq.view(torch.int8).view(self.N, self.K)
+        return self.wq.view(self.N, self.K // 2)
+
+    def w_out_view(self) -> torch.Tensor:
+        return self.w_out[: self.N * outlier_ld(self.k_cap)].view(self.N, outlier_ld(self.k_cap))
+
+
+def quantize_act(X: torch.Tensor, tau: float, state: OutlierState, Xq: torch.Tensor,
+                 s_x: torch.Tensor, X_out: torch.Tensor | None) -> None:
+    """mixq_quantize_act on the current stream.  X: fp16 [M, ldx] (row-major,
+    the first K columns used)."""
+    assert X.dtype == torch.float16 and X.dim() == 2 and X.stride(1) == 1
+    M = X.shape[0]
+    st = state.c()
+    rc = lib().mixq_quantize_act(_ptr(X), M, state.K, X.stride(0), float(tau), ctypes.byref(st),
+                                 _ptr(Xq), _ptr(s_x), _ptr(X_out), _stream(X.device))
+    _check("mixq_quantize_act", rc)
+
+
+def pack_weight(W: torch.Tensor, state: OutlierState, pw: PackedWeight,
+                mode: int = PACK_FULL) -> None:
+    assert W.dtype == torch.float16 and W.is_contiguous()
+    N, K = W.shape
+    st = state.c()
+    w = pw.c()
+    rc = lib().mixq_pack_weight(_ptr(W), N, K, pw.bits, ctypes.byref(st), mode, ctypes.byref(w),
+                                _stream(W.device))
+    _check("mixq_pack_weight", rc)
+
+
+def gemm(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None, state: OutlierState,
+         pw: PackedWeight, Y: torch.Tensor, acc_debug: torch.Tensor | None = None) -> None:
+    M = Xq.shape[0]
+    st = state.c()
+    w = pw.c()
+    rc = lib().mixq_gemm(_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(st), ctypes.byref(w), M,
+                         _ptr(Y), Y.stride(0), _ptr(acc_debug), _stream(Y.device))
+    _check("mixq_gemm", rc)
+
+
+class LayerStep:
+    """One layer step (quantize, outlier-column gather, GEMM) with every
+    ctypes argument built once, so that a hot loop pays only the three
+    foreign calls and their kernel launches."""
+
+    def __init__(self, X: torch.Tensor, tau: float, state: OutlierState, W: torch.Tensor,
+                 pw: PackedWeight, Xq: torch.Tensor, s_x: torch.Tensor,
+                 X_out: torch.Tensor | None, Y: torch.Tensor,
+                 acc_debug: torch.Tensor | None = None, stream=None):
+        L = lib()
+        dev = X.device
+        s = ctypes.c_void_p(stream if stream is not None
+                            else torch.cuda.current_stream(dev).cuda_stream)
+        self._keep = (X, W, Xq, s_x, X_out, Y, acc_debug, state, pw)
+        self._st = state.c()
+        self._w = pw.c()
+        M = X.shape[0]
+        self._calls = [
+            ("mixq_quantize_act", L.mixq_quantize_act,
+             (_ptr(X), M, state.K, X.stride(0), ctypes.c_float(tau), ctypes.byref(self._st),
+              _ptr(Xq), _ptr(s_x), _ptr(X_out), s)),
+            ("mixq_pack_weight", L.mixq_pack_weight,
+             (_ptr(W), pw.N, pw.K, pw.bits, ctypes.byref(self._st), PACK_OUTLIER_COLS,
+              ctypes.byref(self._w), s)),
+            ("mixq_gemm", L.mixq_gemm,
+             (_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(self._st), ctypes.byref(self._w),
+              M, _ptr(Y), Y.stride(0), _ptr(acc_debug), s)),
+        ]
+
+    def act(self):
+        """The activation side and the gather: everything before the GEMM."""
+        for name, fn, args in self._calls[:2]:
+            rc = fn(*args)
+            if rc:
+                _check(name, rc)
+
+    def gemm(self):
+        name, fn, args = self._calls[2]
+        rc = fn(*args)
+        if rc:
+            _check(name, rc)
+
+    def __call__(self):
+        for name, fn, args in self._calls:
+            rc = fn(*args)
+            if rc:
+                _check(name, rc)
+
+
+class MixQLinear:
+    """Y = X W^T through the three library calls, with the outlier set cached
+    across calls (the layer the MixQ article describes)."""
+
+    def __init__(self, W: torch.Tensor, bits: int = 8, tau: float = 6.0, k_cap: int = 256):
+        N, K = W.shape
+        self.W = W.contiguous()
+        self.N, self.K, self.bits, self.tau = N, K, bits, float(tau)
+        self.k_cap = min(k_cap, K)
+        self.state = OutlierState.create(K, self.k_cap, W.device)
+        self.pw = PackedWeight.create(N, K, bits, self.k_cap, W.device)
+        pack_weight(self.W, self.state, self.pw, PACK_FULL)
+        self._bufs = {}
+
+    def buffers(self, M: int):
+        if M not in self._bufs:
+            dev = self.W.device
+            ld = outlier_ld(self.k_cap)
+            self._bufs[M] = (torch.empty(M, self.K, dtype=torch.int8, device=dev),
+                             torch.empty(M, dtype=torch.float32, device=dev),
+                             torch.zeros(max(M * ld, 1), dtype=torch.float16, device=dev))
+        return self._bufs[M]
+
+    def forward(self, X: torch.Tensor, Y: torch.Tensor | None = None,
+                acc_debug: torch.Tensor | None = None) -> torch.Tensor:
+        M = X.shape[0]
+        Xq, s_x, X_out = self.buffers(M)
+        if Y is None:
+            Y = torch.empty(M, self.N, dtype=torch.float32, device=X.device)
+        quantize_act(X, self.tau, self.state, Xq, s_x, X_out)
+        pack_weight(self.W, self.state, self.pw, PACK_OUTLIER_COLS)
+        gemm(Xq, s_x, X_out, self.state, self.pw, Y, acc_debug)
+        return Y
+
+    __call__ = forward

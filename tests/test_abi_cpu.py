@@ -1,0 +1,117 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, its
+size helpers are right, and argument validation answers before any HIP call.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixed_precision_quantized_amax_amd import mixq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mixq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mixq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("mixq_quantize_act", "mixq_pack_weight", "mixq_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = mixq.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_size_helpers():
+    L = mixq.lib()
+    assert [L.mixq_outlier_ld(k) for k in (0, 1, 31, 32, 33, 82, 96)] == [0, 32, 32, 32, 64, 96, 96]
+    assert L.mixq_bitmap_words(8192) == 256 and L.mixq_bitmap_words(64) == 2
+    assert L.mixq_state_work_words(8192) == 2 * 256 + 4
+    assert L.mixq_packed_weight_bytes(8192, 8192, 8) == 8192 * 8192
+    assert L.mixq_packed_weight_bytes(8192, 8192, 4) == 8192 * 4096
+    assert L.mixq_packed_weight_bytes(8, 64, 5) == 0
+    assert L.mixq_version() >= 100
+    for c in range(6):
+        assert L.mixq_status_string(c)
+
+
+def _state(k_cap=8, null=None):
+    vals = dict(idx=0x1000, count=0x2000, flag=0x3000, bitmap=0x4000, work=0x5000)
+    if null:
+        vals[null] = 0
+    return mixq.ActState(vals["idx"], vals["count"], vals["flag"], vals["bitmap"],
+                         vals["work"], k_cap)
+
+
+def _quant(X=0x10000, M=4, K=64, ldx=64, tau=6.0, st=None, Xq=0x20000, sx=0x30000, xo=0x40000):
+    st = st or _state()
+    return mixq.lib().mixq_quantize_act(ctypes.c_void_p(X), M, K, ldx, tau, ctypes.byref(st),
+                                        ctypes.c_void_p(Xq), ctypes.c_void_p(sx),
+                                        ctypes.c_void_p(xo), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=0), 1), (dict(Xq=0), 1), (dict(sx=0), 1), (dict(M=0), 1), (dict(K=0), 1),
+    (dict(ldx=32), 1), (dict(tau=float("nan")), 1), (dict(tau=float("inf")), 1),
+    (dict(tau=-1.0), 1), (dict(st=_state(k_cap=65)), 1), (dict(st=_state(k_cap=-1)), 1),
+    (dict(st=_state(null="work")), 1), (dict(xo=0), 1),
+    (dict(K=96, ldx=96), 2), (dict(K=65536 + 64, ldx=65536 + 64), 2), (dict(X=0x10008), 2),
+    (dict(ldx=68), 2),
+])
+def test_quantize_act_validation(kw, code):
+    assert _quant(**kw) == code
+
+
+def test_valid_arguments_need_a_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _quant() == 4                       # MIXQ_ERR_NO_DEVICE, nothing launched
+    assert mixq.lib().mixq_check_device() == 4
+
+
+def _weight(N=16, K=64, bits=8, k_cap=8, **null):
+    vals = dict(wq=0x100000, s_w=0x200000, w_out=0x300000, k_out=0x400000)
+    vals.update(null)
+    return mixq.Weight(vals["wq"], vals["s_w"], vals["w_out"], vals["k_out"], bits, N, K, k_cap)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(bits=5), 1), (dict(mode=7), 1), (dict(N=0), 1), (dict(w=_weight(N=8)), 1),
+    (dict(w=_weight(bits=4)), 1), (dict(w=_weight(k_cap=4)), 1), (dict(w=_weight(wq=0)), 1),
+    (dict(w=_weight(k_out=0)), 1), (dict(K=96, w=_weight(K=96)), 2),
+])
+def test_pack_weight_validation(args, code):
+    N = args.get("N", 16)
+    K = args.get("K", 64)
+    bits = args.get("bits", 8)
+    mode = args.get("mode", 0)
+    w = args.get("w", _weight(N=N or 16, K=K, bits=bits if bits in (4, 8) else 8))
+    st = _state()
+    rc = mixq.lib().mixq_pack_weight(ctypes.c_void_p(0x900000), N, K, bits, ctypes.byref(st), mode,
+                                     ctypes.byref(w), None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(M=0), 1), (dict(Y=0), 1), (dict(ldy=8), 1), (dict(Xq=0), 1),
+    (dict(w=_weight(k_cap=3)), 1), (dict(w=_weight(bits=6)), 1), (dict(xo=0), 1),
+    (dict(w=_weight(K=100)), 2), (dict(Xq=0x20004), 2),
+])
+def test_gemm_validation(args, code):
+    w = args.get("w", _weight())
+    st = _state()
+    rc = mixq.lib().mixq_gemm(ctypes.c_void_p(args.get("Xq", 0x20000)), ctypes.c_void_p(0x30000),
+                              ctypes.c_void_p(args.get("xo", 0x40000)), ctypes.byref(st),
+                              ctypes.byref(w), args.get("M", 4), ctypes.c_void_p(args.get("Y", 0x50000)),
+                              args.get("ldy", 16), None, None)
+    assert rc == code
