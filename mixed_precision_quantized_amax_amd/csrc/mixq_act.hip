@@ -74,6 +74,7 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
 
     uint4 xv[CPT];
     uint32_t wv[CPT];
+    int32_t rk[CPT];  // rank of the first channel of the chunk's bitmap word
     float am = 0.0f;
     bool det = false;
     for (int s = 0; s < nseg; ++s) {
@@ -83,9 +84,11 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
             if (c < a.nchunks) {
                 xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
                 wv[i] = set_words[c >> 2];
+                rk[i] = rank[c >> 2];
             } else {
                 xv[i] = make_uint4(0, 0, 0, 0);
                 wv[i] = 0xFFFFFFFFu;
+                rk[i] = 0;
             }
         }
 #pragma unroll
@@ -130,6 +133,7 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
                 if (c < a.nchunks) {
                     xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
                     wv[i] = set_words[c >> 2];
+                    rk[i] = rank[c >> 2];
                 }
             }
         }
@@ -150,7 +154,7 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
                 } else {
                     // outlier channel: its column in X_out is its rank in the set
                     const int bit = (c & 3) * 8 + e;
-                    const int j = rank[c >> 2] + __popc(wv[i] & ((1u << bit) - 1u));
+                    const int j = rk[i] + __popc(wv[i] & ((1u << bit) - 1u));
                     orow[j] = hb;
                 }
                 packed[e >> 2] |= ((uint32_t)q & 0xFFu) << ((e & 3) * 8);

@@ -80,6 +80,27 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #define MIXQ_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8)))
 
+// Scheduling pattern for one pipelined tile: the first half of the MFMAs each
+// followed by LDS reads, the second half each followed by LDS writes or global
+// loads (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x200 LDS
+// write, 0x020 global load).
+template <int MF, int RD, int WR, int LD>
+__device__ __forceinline__ void sched_interleave() {
+    constexpr int H = MF / 2;
+    constexpr int rpm = (RD + H - 1) / H;
+    constexpr int opm = (WR + LD + (MF - H) - 1) / (MF - H);
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, rpm, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MF - H; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x220, opm, 0);
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int BITS>
 struct Cfg {
     static constexpr int kThreads = WM * WN * kWave;
@@ -99,12 +120,35 @@ struct Cfg {
 
 // STAGES == 2: global -> VGPR -> LDS, double-buffered LDS.
 // STAGES >= 3: global -> LDS directly (buffer_load ... lds), STAGES-deep ring.
-template <int BM, int BN, int WM, int WN, int BITS, int STAGES, bool DEBUG>
-__global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
+// Large tiles hold 256 int32 accumulators per lane, so one wave per SIMD is
+// all that fits; saying so lets the scheduler spend registers on overlapping
+// LDS reads with MFMAs instead of saving them for an occupancy it cannot get.
+template <int BM, int BN, int WM, int WN>
+constexpr int waves_per_eu() {
+    return (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2;
+}
+
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF, bool DEBUG>
+__global__ __launch_bounds__(WM* WN* kWave)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, WM, WN>(), waves_per_eu<BM, BN, WM, WN>())))
+void gemm_kernel(GemmArgs a) {
     using C = Cfg<BM, BN, WM, WN, BITS>;
     static_assert(STAGES == 2 || BITS == 8, "INT4 weights use the register-staged loader");
-    __shared__ __attribute__((aligned(1024))) uint8_t As[STAGES][BM * kBK];
-    __shared__ __attribute__((aligned(1024))) uint8_t Bs[STAGES][BN * kBK];
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+    // One array per stage (A tile, then B tile): the compiler then tracks each
+    // stage's pending global->LDS transfers separately and waits only for the
+    // right ones.
+    constexpr int kStageBytes = (BM + BN) * kBK;
+    __shared__ __attribute__((aligned(1024))) uint8_t sS0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sS1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sS2[STAGES > 2 ? kStageBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sS3[STAGES > 3 ? kStageBytes : 16];
+    uint8_t* const sA0 = sS0;
+    uint8_t* const sA1 = sS1;
+    uint8_t* const sB0 = sS0 + BM * kBK;
+    uint8_t* const sB1 = sS1 + BM * kBK;
+    uint8_t* const As[4] = {sS0, sS1, sS2, sS3};
+    uint8_t* const Bs[4] = {sS0 + BM * kBK, sS1 + BM * kBK, sS2 + BM * kBK, sS3 + BM * kBK};
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -174,59 +218,72 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < C::kFN; ++j) acc[i][j] = v16i{};
 
+    // One K tile: both 32-byte K halves' fragments are read from LDS up
+    // front, so the second half's reads overlap the first half's MFMAs.
     auto mma_tile = [&](const uint8_t* Ab, const uint8_t* Bb) {
+        v4i af[2][C::kFM], bf[2][C::kFN];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            v4i af[C::kFM], bf[C::kFN];
-#pragma unroll
-            for (int i = 0; i < C::kFM; ++i)
-                af[i] = *reinterpret_cast<const v4i*>(Ab + rdA[ks] + i * 32 * kBK);
 #pragma unroll
             for (int j = 0; j < C::kFN; ++j)
-                bf[j] = *reinterpret_cast<const v4i*>(Bb + rdB[ks] + j * 32 * kBK);
+                bf[ks][j] = *reinterpret_cast<const v4i*>(Bb + rdB[ks] + j * 32 * kBK);
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+                af[ks][i] = *reinterpret_cast<const v4i*>(Ab + rdA[ks] + i * 32 * kBK);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::kFN; ++j)
-                    acc[i][j] =
-                        __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][i], bf[ks][j],
+                                                                      acc[i][j], 0, 0, 0);
+        // schedule: the first half's reads, the second half's reads, then the
+        // MFMAs (the second half's reads land while the first half multiplies)
+        __builtin_amdgcn_sched_group_barrier(0x100, C::kFM + C::kFN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, C::kFM + C::kFN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::kFM * C::kFN, 0);
     };
 
     if constexpr (STAGES == 2) {
-        // ---- register-staged, double-buffered ---------------------------------------
-        v4i ra[C::kAI];
-        v4i rb[BITS == 8 ? C::kBI : C::kBI4];
-        auto gload = [&](int kt) {
+        // ---- register-staged, double-buffered LDS ------------------------------------
+        // Global loads run PF tiles ahead of the multiply, in PF register sets.
+        struct Regs {
+            v4i a[C::kAI];
+            v4i b[BITS == 8 ? C::kBI : C::kBI4];
+        };
+        auto gload = [&](int kt, Regs& R) {
 #pragma unroll
             for (int i = 0; i < C::kAI; ++i)
-                ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA[i], kt * kBK, 0);
+                R.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffA[i], kt * kBK, 0);
             if constexpr (BITS == 8) {
 #pragma unroll
                 for (int i = 0; i < C::kBI; ++i)
-                    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[i], kt * kBK, 0);
+                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[i], kt * kBK, 0);
             } else {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i)
-                    rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
             }
         };
-        auto lstore = [&](int buf) {
+        auto lstore = [&](const Regs& R, int buf) {
+            uint8_t* Ab = buf ? sA1 : sA0;
+            uint8_t* Bb = buf ? sB1 : sB0;
 #pragma unroll
             for (int i = 0; i < C::kAI; ++i)
-                *reinterpret_cast<v4i*>(&As[buf][((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
-                    ra[i];
+                *reinterpret_cast<v4i*>(&Ab[((i * C::kNW + wave) * 16) * kBK + lane * 16]) = R.a[i];
             if constexpr (BITS == 8) {
 #pragma unroll
                 for (int i = 0; i < C::kBI; ++i)
-                    *reinterpret_cast<v4i*>(
-                        &Bs[buf][((i * C::kNW + wave) * 16) * kBK + lane * 16]) = rb[i];
+                    *reinterpret_cast<v4i*>(&Bb[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                        R.b[i];
             } else {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i) {
                     const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
                     const int c2 = lane & 1;
-                    const uint32_t w0 = rb[i][0], w1 = rb[i][1], w2 = rb[i][2], w3 = rb[i][3];
+                    const uint32_t w0 = R.b[i][0], w1 = R.b[i][1], w2 = R.b[i][2], w3 = R.b[i][3];
                     v4i lo, hi;
                     lo[0] = (int)sext_nibbles(w0 & 0x0F0F0F0Fu);
                     lo[1] = (int)sext_nibbles((w0 >> 4) & 0x0F0F0F0Fu);
@@ -236,77 +293,281 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
                     hi[1] = (int)sext_nibbles((w2 >> 4) & 0x0F0F0F0Fu);
                     hi[2] = (int)sext_nibbles(w3 & 0x0F0F0F0Fu);
                     hi[3] = (int)sext_nibbles((w3 >> 4) & 0x0F0F0F0Fu);
-                    *reinterpret_cast<v4i*>(&Bs[buf][lds_off(row, 2 * c2)]) = lo;
-                    *reinterpret_cast<v4i*>(&Bs[buf][lds_off(row, 2 * c2 + 1)]) = hi;
+                    *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2)]) = lo;
+                    *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2 + 1)]) = hi;
                 }
             }
         };
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < KT) gload(kt + 1);
-            mma_tile(As[cur], Bs[cur]);
-            if (kt + 1 < KT) lstore(cur ^ 1);
+        // B-only staging (used when A fragments come straight from memory)
+        auto bload = [&](int kt, Regs& R) {
+            if constexpr (BITS == 8) {
+#pragma unroll
+                for (int i = 0; i < C::kBI; ++i)
+                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[i], kt * kBK, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::kBI4; ++i)
+                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+            }
+        };
+        if constexpr (PF == 4) {
+            // Cross-tile software pipeline.  Iteration k multiplies tile k from
+            // fragments already in registers while it (a) reads tile k+1's
+            // fragments from LDS, (b) writes tile k+2 (staged in registers two
+            // iterations earlier) into the LDS buffer tile k used, and (c)
+            // loads tile k+4 from global memory into the freed staging
+            // registers.  One barrier per iteration; the MFMA pipe never waits
+            // for an LDS read issued in the same iteration.
+            typedef v4i AFr[2][C::kFM];
+            typedef v4i BFr[2][C::kFN];
+            auto lread = [&](const uint8_t* Ab, const uint8_t* Bb, AFr& fa, BFr& fb) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int i = 0; i < C::kFM; ++i)
+                        fa[ks][i] = *reinterpret_cast<const v4i*>(Ab + rdA[ks] + i * 32 * kBK);
+#pragma unroll
+                    for (int j = 0; j < C::kFN; ++j)
+                        fb[ks][j] = *reinterpret_cast<const v4i*>(Bb + rdB[ks] + j * 32 * kBK);
+                }
+            };
+            auto mfmas = [&](const AFr& fa, const BFr& fb) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                        for (int j = 0; j < C::kFN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+            };
+            AFr fa0, fa1;
+            BFr fb0, fb1;
+            Regs S0, S1;
+            gload(0, S0);
+            gload(1, S1);
+            lstore(S0, 0);
+            lstore(S1, 1);
+            if (KT > 2) gload(2, S0);
+            if (KT > 3) gload(3, S1);
             __syncthreads();
+            lread(sA0, sB0, fa0, fb0);
+            __syncthreads();
+            int k = 0;
+            // steady state: every read, write and load of the pair exists, so
+            // the body is one basic block and the interleave pattern applies
+            for (; k + 6 <= KT; k += 2) {
+                lread(sA1, sB1, fa1, fb1);
+                mfmas(fa0, fb0);
+                lstore(S0, 0);
+                gload(k + 4, S0);
+                sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN),
+                                 C::kAI + (BITS == 8 ? C::kBI : 2 * C::kBI4),
+                                 C::kAI + (BITS == 8 ? C::kBI : C::kBI4)>();
+                __syncthreads();
+                lread(sA0, sB0, fa0, fb0);
+                mfmas(fa1, fb1);
+                lstore(S1, 1);
+                gload(k + 5, S1);
+                sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN),
+                                 C::kAI + (BITS == 8 ? C::kBI : 2 * C::kBI4),
+                                 C::kAI + (BITS == 8 ? C::kBI : C::kBI4)>();
+                __syncthreads();
+            }
+            // last pairs (KT even)
+            for (; k < KT; k += 2) {
+                lread(sA1, sB1, fa1, fb1);
+                mfmas(fa0, fb0);
+                if (k + 2 < KT) lstore(S0, 0);
+                if (k + 4 < KT) gload(k + 4, S0);
+                __syncthreads();
+                if (k + 2 < KT) lread(sA0, sB0, fa0, fb0);
+                mfmas(fa1, fb1);
+                if (k + 3 < KT) lstore(S1, 1);
+                if (k + 5 < KT) gload(k + 5, S1);
+                __syncthreads();
+            }
+        } else if constexpr (PF == 3) {
+            // A fragments are loaded from global memory directly into the
+            // MFMA operand layout (one tile ahead, two register sets); only B
+            // goes through LDS (two tiles ahead).  This halves the LDS
+            // traffic, which otherwise competes with the MFMAs for issue
+            // slots and LDS bandwidth.  Lane l of fragment i, half ks reads
+            // row wm*WTM + 32*i + l%32, bytes 32*ks + 16*(l/32) of the tile.
+            int voffAd[C::kFM];
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i) voffAd[i] = (wm * C::kWTM + i * 32 + fr) * K + fh * 16;
+            typedef v4i AFrags[2][C::kFM];
+            auto aload = [&](int kt, AFrags& X) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int i = 0; i < C::kFM; ++i)
+                        X[ks][i] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffAd[i] + ks * 32,
+                                                                         kt * kBK, 0);
+            };
+            auto mma_ra = [&](const AFrags& X, const uint8_t* Bb) {
+                v4i bf[2][C::kFN];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int j = 0; j < C::kFN; ++j)
+                        bf[ks][j] = *reinterpret_cast<const v4i*>(Bb + rdB[ks] + j * 32 * kBK);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                        for (int j = 0; j < C::kFN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(X[ks][i], bf[ks][j],
+                                                                              acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, C::kFN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, C::kFN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::kFM * C::kFN, 0);
+            };
+            auto bstore = [&](const Regs& R, int buf) {
+                uint8_t* Bb = buf ? sB1 : sB0;
+                if constexpr (BITS == 8) {
+#pragma unroll
+                    for (int i = 0; i < C::kBI; ++i)
+                        *reinterpret_cast<v4i*>(&Bb[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                            R.b[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < C::kBI4; ++i) {
+                        const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
+                        const int c2 = lane & 1;
+                        const uint32_t w0 = R.b[i][0], w1 = R.b[i][1], w2 = R.b[i][2],
+                                       w3 = R.b[i][3];
+                        v4i lo, hi;
+                        lo[0] = (int)sext_nibbles(w0 & 0x0F0F0F0Fu);
+                        lo[1] = (int)sext_nibbles((w0 >> 4) & 0x0F0F0F0Fu);
+                        lo[2] = (int)sext_nibbles(w1 & 0x0F0F0F0Fu);
+                        lo[3] = (int)sext_nibbles((w1 >> 4) & 0x0F0F0F0Fu);
+                        hi[0] = (int)sext_nibbles(w2 & 0x0F0F0F0Fu);
+                        hi[1] = (int)sext_nibbles((w2 >> 4) & 0x0F0F0F0Fu);
+                        hi[2] = (int)sext_nibbles(w3 & 0x0F0F0F0Fu);
+                        hi[3] = (int)sext_nibbles((w3 >> 4) & 0x0F0F0F0Fu);
+                        *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2)]) = lo;
+                        *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2 + 1)]) = hi;
+                    }
+                }
+            };
+            AFrags X0, X1;
+            Regs R0, R1;
+            aload(0, X0);
+            bload(0, R0);
+            bload(1, R1);
+            bstore(R0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 2) {  // KT even (host checks K % 128 == 0)
+                aload(kt + 1, X1);
+                if (kt + 2 < KT) bload(kt + 2, R0);
+                mma_ra(X0, sB0);
+                bstore(R1, 1);
+                __syncthreads();
+                if (kt + 2 < KT) aload(kt + 2, X0);
+                if (kt + 3 < KT) bload(kt + 3, R1);
+                mma_ra(X1, sB1);
+                if (kt + 2 < KT) bstore(R0, 0);
+                __syncthreads();
+            }
+        } else if constexpr (PF == 1) {
+            Regs R;
+            gload(0, R);
+            lstore(R, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; ++kt) {
+                const int cur = kt & 1;
+                if (kt + 1 < KT) gload(kt + 1, R);
+                mma_tile(cur ? sA1 : sA0, cur ? sB1 : sB0);
+                if (kt + 1 < KT) lstore(R, cur ^ 1);
+                __syncthreads();
+            }
+        } else {
+            // Tile kt+2 is loaded into the register set tile kt came from;
+            // tile kt+1, loaded an iteration earlier, goes to the other LDS
+            // buffer.  KT is even here (the host checks K % 128 == 0), so the
+            // loop body has no early exit and the accumulators stay put.
+            Regs R0, R1;
+            gload(0, R0);
+            gload(1, R1);
+            lstore(R0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < KT; kt += 2) {
+                if (kt + 2 < KT) gload(kt + 2, R0);
+                mma_tile(sA0, sB0);
+                lstore(R1, 1);
+                __syncthreads();
+                if (kt + 3 < KT) gload(kt + 3, R1);
+                mma_tile(sA1, sB1);
+                if (kt + 2 < KT) lstore(R0, 0);
+                __syncthreads();
+            }
         }
     } else {
         // ---- direct global -> LDS, STAGES-deep ring -----------------------------------
-        constexpr int kLoads = C::kAI + C::kBI;  // per thread per tile
-        auto issue = [&](int kt, int buf) {
+        // Iteration kt: wait until this wave's transfers for tile kt have
+        // landed (those of tiles kt+1 .. kt+STAGES-2 may stay in flight),
+        // barrier (every wave's tile kt has landed, and every wave is done
+        // with tile kt-1), refill the stage tile kt-1 used with tile
+        // kt+STAGES-1, multiply tile kt.  The barrier carries no memory fence,
+        // so the in-flight transfers are not drained.
+        constexpr int kLoads = C::kAI + C::kBI;  // transfers per thread per tile
+        auto issue = [&](int kt, uint8_t* Ab, uint8_t* Bb) {
 #if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts exist only in the device pass
 #pragma unroll
             for (int i = 0; i < C::kAI; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rA, (lds_ptr_t)(&As[buf][((i * C::kNW + wave) * 16) * kBK]), 16, voffA[i],
-                    kt * kBK, 0, 0);
+                    rA, (lds_ptr_t)(Ab + ((i * C::kNW + wave) * 16) * kBK), 16, voffA[i], kt * kBK,
+                    0, 0);
 #pragma unroll
             for (int i = 0; i < C::kBI; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rB, (lds_ptr_t)(&Bs[buf][((i * C::kNW + wave) * 16) * kBK]), 16, voffB[i],
-                    kt * kBK, 0, 0);
+                    rB, (lds_ptr_t)(Bb + ((i * C::kNW + wave) * 16) * kBK), 16, voffB[i], kt * kBK,
+                    0, 0);
 #endif
         };
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < KT) issue(s, s);
-        for (int kt = 0; kt < KT; ++kt) {
-            // tiles kt+1 .. kt+STAGES-2 may stay in flight
-            const int ahead = min(KT - 1 - kt, STAGES - 2);
-            if (ahead >= 2) {
-                MIXQ_WAIT_VMCNT(2 * kLoads);
-            } else if (ahead == 1) {
-                MIXQ_WAIT_VMCNT(kLoads);
-            } else {
-                MIXQ_WAIT_VMCNT(0);
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < KT) issue(st, As[st], Bs[st]);
+        for (int kt0 = 0; kt0 < KT; kt0 += STAGES) {
+#pragma unroll
+            for (int st = 0; st < STAGES; ++st) {
+                const int kt = kt0 + st;
+                if (kt < KT) {
+                    if (kt + STAGES - 2 < KT) {
+                        if constexpr (STAGES == 4)
+                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoads) : "memory");
+                        else
+                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+                    } else {
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    }
+                    __builtin_amdgcn_s_barrier();
+                    const int nxt = (st + STAGES - 1) % STAGES;
+                    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, As[nxt], Bs[nxt]);
+                    mma_tile(As[st], Bs[st]);
+                }
             }
-            __syncthreads();
-            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-            mma_tile(As[kt % STAGES], Bs[kt % STAGES]);
         }
         __syncthreads();
     }
 
     // ---- epilogue: dequantize and scale in registers, in place ---------------------
-    // 32x32 fragment layout: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32
+    // 32x32 fragment layout: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
+    // The tile's scales are staged in LDS so that a lane reads its four
+    // consecutive rows' scales with one 16-byte LDS read.
+    __shared__ __attribute__((aligned(16))) float sx_t[BM];
+    __shared__ __attribute__((aligned(16))) float sw_t[BN];
+    for (int t = tid; t < BM; t += C::kThreads) sx_t[t] = a.s_x[min(m0 + t, a.M - 1)];
+    for (int t = tid; t < BN; t += C::kThreads) sw_t[t] = a.s_w[min(n0 + t, a.N - 1)];
+    __syncthreads();
     const int count = *a.count;
     const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
 
-    float sw[C::kFN];
-#pragma unroll
-    for (int j = 0; j < C::kFN; ++j) {
-        const int col = n0 + wn * C::kWTN + j * 32 + fr;
-        sw[j] = a.s_w[min(col, a.N - 1)];
-    }
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i) {
-        float sx[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = m0 + wm * C::kWTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-            sx[e] = a.s_x[min(row, a.M - 1)];
-        }
 #pragma unroll
         for (int j = 0; j < C::kFN; ++j) {
             if constexpr (DEBUG) {
@@ -318,9 +579,17 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
                         a.acc_debug[(int64_t)row * a.N + col] = acc[i][j][e];
                 }
             }
+            const float swj = sw_t[wn * C::kWTN + j * 32 + fr];
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[i][j][e] = __float_as_int(((float)acc[i][j][e] * sx[e]) * sw[j]);
+            for (int q = 0; q < 4; ++q) {
+                const float4 sx4 = *reinterpret_cast<const float4*>(
+                    &sx_t[wm * C::kWTM + i * 32 + 8 * q + 4 * fh]);
+                const float sxe[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][4 * q + r] =
+                        __float_as_int(((float)acc[i][j][4 * q + r] * sxe[r]) * swj);
+            }
         }
     }
 
@@ -338,14 +607,14 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
             for (int i = 0; i < C::kAI; ++i) {
                 const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
                 const int off = row * ldb + (((lane & 3) ^ swz(row)) << 4);
-                *reinterpret_cast<v4i*>(&As[0][((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                *reinterpret_cast<v4i*>(&sA0[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
                     __builtin_amdgcn_raw_buffer_load_b128(rXo, off, kt2 * kBK, 0);
             }
 #pragma unroll
             for (int i = 0; i < C::kBI; ++i) {
                 const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
                 const int off = row * ldb + (((lane & 3) ^ swz(row)) << 4);
-                *reinterpret_cast<v4i*>(&Bs[0][((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
+                *reinterpret_cast<v4i*>(&sB0[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
                     __builtin_amdgcn_raw_buffer_load_b128(rWo, off, kt2 * kBK, 0);
             }
             __syncthreads();
@@ -354,10 +623,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
                 v8h af[C::kFM], bf[C::kFN];
 #pragma unroll
                 for (int i = 0; i < C::kFM; ++i)
-                    af[i] = *reinterpret_cast<const v8h*>(&As[0][rdA[ks] + i * 32 * kBK]);
+                    af[i] = *reinterpret_cast<const v8h*>(&sA0[rdA[ks] + i * 32 * kBK]);
 #pragma unroll
                 for (int j = 0; j < C::kFN; ++j)
-                    bf[j] = *reinterpret_cast<const v8h*>(&Bs[0][rdB[ks] + j * 32 * kBK]);
+                    bf[j] = *reinterpret_cast<const v8h*>(&sB0[rdB[ks] + j * 32 * kBK]);
 #pragma unroll
                 for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
@@ -372,29 +641,40 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(GemmArgs a) {
     }
 
     // ---- store Y (fp32) ---------------------------------------------------------------
+    // Buffer stores relative to the tile's first row: 32-bit offsets, and rows
+    // past M fall outside the buffer as well as failing the explicit check.
+    const __amdgpu_buffer_rsrc_t rY =
+        make_rsrc(a.Y + (int64_t)m0 * a.ldy, (int64_t)rows_a * a.ldy * 4);
+    const int ldy4 = (int)a.ldy * 4;
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kFN; ++j) {
             const int col = n0 + wn * C::kWTN + j * 32 + fr;
+            const int r0 = wm * C::kWTM + i * 32 + 4 * fh;  // tile-relative row of e = 0
+            if (col < a.N) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * C::kWTM + i * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-                if (row < a.M && col < a.N)
-                    a.Y[(int64_t)row * a.ldy + col] = __int_as_float(acc[i][j][e]);
+                for (int e = 0; e < 16; ++e) {
+                    const int rl = r0 + 8 * (e >> 2) + (e & 3);
+                    if (rl < rows_a)
+                        __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][e], rY, rl * ldy4 + col * 4,
+                                                              0, 0);
+                }
             }
         }
 }
 
-template <int BM, int BN, int WM, int WN, int BITS, int STAGES>
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1>
 int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * kWave);
     if (debug)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true>), grid, block, 0,
+                           st, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false>), grid, block, 0,
+                           st, a);
     return launch_status();
 }
 
@@ -405,6 +685,13 @@ enum {
     kCfg128x128 = 2,   // 4 waves of 64x64, register-staged
     kCfg256x256D = 3,  // 4 waves of 128x128, direct-to-LDS, 3 stages
     kCfg256x128 = 4,   // 4 waves of 128x64, register-staged
+    kCfg256x256D4 = 5, // 4 waves of 128x128, direct-to-LDS, 4 stages
+    kCfg256x256P2 = 6, // 4 waves of 128x128, register-staged, loads two tiles ahead
+    kCfg256x128P2 = 7, // 4 waves of 128x64, register-staged, loads two tiles ahead
+    kCfg256x256AD = 8, // 4 waves of 128x128, A fragments from global, B via LDS
+    kCfg256x128AD = 9, // 4 waves of 128x64, A fragments from global, B via LDS
+    kCfg256x256SP = 10,  // 4 waves of 128x128, cross-tile software pipeline
+    kCfg256x128SP = 11,  // 4 waves of 128x64, cross-tile software pipeline
 };
 
 int forced_cfg() {
@@ -412,26 +699,43 @@ int forced_cfg() {
     return e ? atoi(e) : 0;
 }
 
-int pick_cfg(int64_t M, int64_t N, int bits) {
+int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     const int f = forced_cfg();
-    if (f >= 1 && f <= 4 && !(bits == 4 && f == kCfg256x256D)) return f;
+    if ((f == kCfg256x256P2 || f == kCfg256x128P2 || f == kCfg256x256AD || f == kCfg256x128AD ||
+         f == kCfg256x256SP || f == kCfg256x128SP) &&
+        K % 128 != 0)
+        return kCfg128x128;
+    if (f >= 1 && f <= 11 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
     const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
     return big >= 192 ? kCfg256x256 : kCfg128x128;
 }
 
 int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
-    switch (pick_cfg(a.M, a.N, 8)) {
+    switch (pick_cfg(a.M, a.N, a.K, 8)) {
         case kCfg256x256: return launch_cfg<256, 256, 2, 2, 8, 2>(a, debug, st);
         case kCfg256x128: return launch_cfg<256, 128, 2, 2, 8, 2>(a, debug, st);
         case kCfg256x256D: return launch_cfg<256, 256, 2, 2, 8, 3>(a, debug, st);
+        case kCfg256x256D4: return launch_cfg<256, 256, 2, 2, 8, 4>(a, debug, st);
+        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 8, 2, 2>(a, debug, st);
+        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 8, 2, 2>(a, debug, st);
+        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 8, 2, 3>(a, debug, st);
+        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 8, 2, 3>(a, debug, st);
+        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 8, 2, 4>(a, debug, st);
+        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 8, 2, 4>(a, debug, st);
         default: return launch_cfg<128, 128, 2, 2, 8, 2>(a, debug, st);
     }
 }
 
 int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
-    switch (pick_cfg(a.M, a.N, 4)) {
+    switch (pick_cfg(a.M, a.N, a.K, 4)) {
         case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2>(a, debug, st);
         case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2>(a, debug, st);
+        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2>(a, debug, st);
+        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2>(a, debug, st);
+        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3>(a, debug, st);
+        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3>(a, debug, st);
+        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4>(a, debug, st);
+        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4>(a, debug, st);
         default: return launch_cfg<128, 128, 2, 2, 4, 2>(a, debug, st);
     }
 }

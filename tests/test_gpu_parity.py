@@ -18,7 +18,9 @@ from oracle import Oracle, OracleLayer
 
 pytestmark = pytest.mark.gpu
 
-TILES = {"auto": "0", "256x256": "1", "128x128": "2", "256x256_lds3": "3", "256x128": "4"}
+TILES = {"auto": "0", "256x256": "1", "128x128": "2", "256x256_lds3": "3", "256x128": "4",
+         "256x256_lds4": "5", "256x256_pf2": "6", "256x128_pf2": "7", "256x256_adirect": "8",
+         "256x128_adirect": "9", "256x256_swp": "10", "256x128_swp": "11"}
 
 
 @pytest.fixture(scope="module")
@@ -87,7 +89,7 @@ SMALL = [  # M, K, N, planted outlier channels, bits
 @pytest.mark.parametrize("tile", list(TILES), indirect=True)
 @pytest.mark.parametrize("M,K,N,n_out,bits", SMALL)
 def test_small_random(orc, tile, M, K, N, n_out, bits):
-    if tile == "256x256_lds3" and bits == 4:
+    if tile.startswith("256x256_lds") and bits == 4:
         pytest.skip("INT4 weights always take the register-staged loader")
     X, W, _ = workloads.random_case(7, M, K, N, n_out)
     full_compare(orc, X, W, bits, 6.0, min(K, 128), tag=f"small[{tile}]")
