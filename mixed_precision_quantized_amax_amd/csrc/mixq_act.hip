@@ -36,6 +36,7 @@ struct ActArgs {
     int32_t K;
     int64_t ldx;
     float tau;
+    uint32_t tau_bits;  // bits of the largest fp16 value <= tau
     int32_t* idx;
     int32_t* count;
     int32_t* flag;
@@ -53,20 +54,64 @@ struct ActArgs {
     int32_t ld_out;
 };
 
+// LDS table: for the 8 cached-channel bits of a chunk (8 halves = 4 dwords),
+// the dword masks that keep the uncached halves (0xFFFF) and clear the cached
+// ones.  Built once per block.
+constexpr int kLutEntries = 256;
+
+__device__ __forceinline__ void build_keep_lut(uint4* lut) {
+    for (int c = threadIdx.x; c < kLutEntries; c += blockDim.x) {
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            d[j] = (((c >> (2 * j)) & 1) ? 0u : 0x0000FFFFu) |
+                   (((c >> (2 * j + 1)) & 1) ? 0u : 0xFFFF0000u);
+        lut[c] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// Two 16-bit unsigned maxima in one packed integer operation.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a),
+                                                                  __builtin_bit_cast(us2, b)));
+}
+
 __device__ __forceinline__ uint16_t half_at(const uint4& v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
     return (uint16_t)(w >> ((e & 1) * 16));
+}
+
+// Code of one value: round half to even of x*r, clamped to [-127, 127].
+// The product is one fp32 rounding (fma with a zero addend); adding
+// 1.5 * 2^23 to a value in [-127, 127] rounds it to the nearest integer
+// (ties to even) and leaves that integer in the low bits of the sum.
+__device__ __forceinline__ uint32_t code_bits(uint16_t h, float r) {
+    float t = __builtin_fmaf(half_bits_to_float(h), r, 0.0f);
+    t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
+    return __float_as_uint(t + 12582912.0f);
+}
+
+// Low bytes of four code words -> one dword (byte k from word k).
+__device__ __forceinline__ uint32_t pack4(uint32_t u0, uint32_t u1, uint32_t u2, uint32_t u3) {
+    const uint32_t p01 = __builtin_amdgcn_perm(u1, u0, 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(u3, u2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
 // One token processed by one wave.  Chunk = 8 consecutive channels (16 B);
 // lane l owns chunks l, l+64, ... of each segment of 64*CPT chunks, so every
 // load instruction of the wave reads 1 KB of the row contiguously.
 //   set_words / rank: the set the token is quantized with (global or LDS)
+//   lut: keep-mask table (LDS)
 //   newbits: LDS detection bitmap, or null when detection is off
+// The amax is taken on the fp16 bit patterns: for non-negative halves the
+// integer order is the value order, so the packed unsigned max is exact.
 // Returns (in every lane) whether this token had an uncached value above tau.
 template <int CPT>
 __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_words,
-                         const int32_t* rank, int set_size, uint32_t* newbits) {
+                         const int32_t* rank, int set_size, const uint4* lut, uint32_t* newbits) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint16_t* xr = a.X + row * a.ldx;
     const int seg_chunks = kWave * CPT;
@@ -75,9 +120,8 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
     uint4 xv[CPT];
     uint32_t wv[CPT];
     int32_t rk[CPT];  // rank of the first channel of the chunk's bitmap word
-    float am = 0.0f;
-    bool det = false;
-    for (int s = 0; s < nseg; ++s) {
+    uint32_t amx = 0;  // packed max of |x| bits (two halves)
+    auto load_seg = [&](int s) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = s * seg_chunks + i * kWave + lane;
@@ -87,34 +131,56 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
                 rk[i] = rank[c >> 2];
             } else {
                 xv[i] = make_uint4(0, 0, 0, 0);
-                wv[i] = 0xFFFFFFFFu;
+                wv[i] = 0u;
                 rk[i] = 0;
             }
         }
+    };
+    auto keep_of = [&](int i, int c) -> uint4 {
+        return lut[(wv[i] >> ((c & 3) * 8)) & 0xFFu];
+    };
+    for (int s = 0; s < nseg; ++s) {
+        load_seg(s);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = s * seg_chunks + i * kWave + lane;
-            const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
-            uint32_t over = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = fabsf(half_bits_to_float(half_at(xv[i], e)));
-                if (!((cb >> e) & 1u)) {
-                    am = fmaxf(am, v);
-                    if (v > a.tau) over |= 1u << e;
-                }
-            }
-            if (newbits && over) {
-                atomicOr(&newbits[c >> 2], over << ((c & 3) * 8));
-                det = true;
-            }
+            const uint4 kp = keep_of(i, c);
+            amx = pk_max_u16(amx, xv[i].x & kp.x & 0x7FFF7FFFu);
+            amx = pk_max_u16(amx, xv[i].y & kp.y & 0x7FFF7FFFu);
+            amx = pk_max_u16(amx, xv[i].z & kp.z & 0x7FFF7FFFu);
+            amx = pk_max_u16(amx, xv[i].w & kp.w & 0x7FFF7FFFu);
         }
     }
-    const float g = wave_max(am);
+    uint32_t gb = max(amx & 0xFFFFu, amx >> 16);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) gb = max(gb, (uint32_t)__shfl_xor((int)gb, o, kWave));
+
+    bool det = false;
+    if (newbits && gb > a.tau_bits) {
+        // The gate fired for this token (rare): mark every uncached channel
+        // above the threshold.  Reads the row again segment by segment.
+        for (int s = 0; s < nseg; ++s) {
+            if (nseg > 1) load_seg(s);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = s * seg_chunks + i * kWave + lane;
+                if (c >= a.nchunks) continue;
+                const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
+                uint32_t over = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (!((cb >> e) & 1u) && (uint32_t)(half_at(xv[i], e) & 0x7FFFu) > a.tau_bits)
+                        over |= 1u << e;
+                if (over) atomicOr(&newbits[c >> 2], over << ((c & 3) * 8));
+            }
+        }
+        det = true;
+    }
 
     // Scale and reciprocal: single IEEE divisions; zero amax -> 1.
+    const float g = half_bits_to_float((uint16_t)gb);
     float sc, r;
-    if (g == 0.0f) {
+    if (gb == 0u) {
         sc = 1.0f;
         r = 1.0f;
     } else {
@@ -126,40 +192,29 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
     int8_t* qr = a.Xq + row * (int64_t)a.K;
     uint16_t* orow = a.ld_out ? a.X_out + row * (int64_t)a.ld_out : nullptr;
     for (int s = 0; s < nseg; ++s) {
-        if (nseg > 1) {  // the row did not fit in registers: read the segment again
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = s * seg_chunks + i * kWave + lane;
-                if (c < a.nchunks) {
-                    xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
-                    wv[i] = set_words[c >> 2];
-                    rk[i] = rank[c >> 2];
-                }
-            }
-        }
+        if (nseg > 1) load_seg(s);  // the row did not fit in registers: read it again
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = s * seg_chunks + i * kWave + lane;
             if (c >= a.nchunks) continue;
             const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
-            uint32_t packed[2] = {0u, 0u};
+            const uint4 kp = keep_of(i, c);
+            // cached channels become +0 and so get code 0
+            const uint32_t m[4] = {xv[i].x & kp.x, xv[i].y & kp.y, xv[i].z & kp.z, xv[i].w & kp.w};
+            uint32_t u[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t hb = half_at(xv[i], e);
-                int q = 0;
-                if (!((cb >> e) & 1u)) {
-                    float y = __builtin_rintf(half_bits_to_float(hb) * r);
-                    y = fminf(fmaxf(y, -127.0f), 127.0f);
-                    q = (int)y;
-                } else {
-                    // outlier channel: its column in X_out is its rank in the set
-                    const int bit = (c & 3) * 8 + e;
-                    const int j = rk[i] + __popc(wv[i] & ((1u << bit) - 1u));
-                    orow[j] = hb;
-                }
-                packed[e >> 2] |= ((uint32_t)q & 0xFFu) << ((e & 3) * 8);
+            for (int e = 0; e < 8; ++e) u[e] = code_bits((uint16_t)(m[e >> 1] >> ((e & 1) * 16)), r);
+            *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) =
+                make_uint2(pack4(u[0], u[1], u[2], u[3]), pack4(u[4], u[5], u[6], u[7]));
+            if (cb) {
+                // outlier channels: column in X_out = rank in the set
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((cb >> e) & 1u) {
+                        const int bit = (c & 3) * 8 + e;
+                        orow[rk[i] + __popc(wv[i] & ((1u << bit) - 1u))] = half_at(xv[i], e);
+                    }
             }
-            *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) = make_uint2(packed[0], packed[1]);
         }
     }
     if (orow) {
@@ -169,18 +224,28 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
     return __any(det);
 }
 
+constexpr int kGateThreads = 256;
+
 template <int CPT>
-__global__ __launch_bounds__(kWave) void gate_quant_kernel(ActArgs a) {
+__global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     extern __shared__ uint32_t newbits[];  // [words]
-    for (int w = threadIdx.x; w < a.words; w += kWave) newbits[w] = 0u;
+    __shared__ uint4 lut[kLutEntries];
+    __shared__ int any_det;
+    build_keep_lut(lut);
+    for (int w = threadIdx.x; w < a.words; w += kGateThreads) newbits[w] = 0u;
+    if (threadIdx.x == 0) any_det = 0;
     __syncthreads();
     const int set_size = *a.count;
+    const int wave = threadIdx.x / kWave;
+    constexpr int kWavesPerBlock = kGateThreads / kWave;
     bool det = false;
-    for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x)
-        det |= wave_row<CPT>(a, row, a.bitmap, a.rank, set_size, newbits);
+    for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < a.M;
+         row += (int64_t)gridDim.x * kWavesPerBlock)
+        det |= wave_row<CPT>(a, row, a.bitmap, a.rank, set_size, lut, newbits);
+    if (det && (threadIdx.x & (kWave - 1)) == 0) any_det = 1;
     __syncthreads();
-    if (det) {  // wave-uniform: only blocks whose tokens crossed the gate
-        for (int w = threadIdx.x; w < a.words; w += kWave)
+    if (any_det) {  // block-uniform: only blocks whose tokens crossed the gate
+        for (int w = threadIdx.x; w < a.words; w += kGateThreads)
             if (newbits[w]) atomicOr(&a.pending[w], newbits[w]);
         if (threadIdx.x == 0) atomicOr(a.marker, 1u);
     }
@@ -225,6 +290,8 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
     int32_t* prefix = reinterpret_cast<int32_t*>(dyn + a.words);  // [words]
     __shared__ int tot[kReqThreads / kWave];
     __shared__ int last;
+    __shared__ uint4 lut[kLutEntries];
+    build_keep_lut(lut);
 
     for (int w = threadIdx.x; w < a.words; w += kReqThreads) neww[w] = a.bitmap[w] | a.pending[w];
     __syncthreads();
@@ -235,7 +302,7 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
         const int64_t stride = (int64_t)gridDim.x * (kReqThreads / kWave);
         for (int64_t row = (int64_t)blockIdx.x * (kReqThreads / kWave) + wave; row < a.M;
              row += stride)
-            wave_row<CPT>(a, row, neww, prefix, total, nullptr);
+            wave_row<CPT>(a, row, neww, prefix, total, lut, nullptr);
     }
     // arrival (fired calls only): the last block commits
     __syncthreads();
@@ -269,9 +336,11 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
 
 template <int CPT>
 int launch_act(const ActArgs& a, hipStream_t st) {
-    const int grid = (int)(a.M < 4096 ? a.M : 4096);
-    hipLaunchKernelGGL(gate_quant_kernel<CPT>, dim3(grid), dim3(kWave), (size_t)a.words * 4, st,
-                       a);
+    constexpr int kRowsPerBlock = kGateThreads / kWave;
+    int64_t g1 = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int grid = (int)(g1 < 2048 ? g1 : 2048);
+    hipLaunchKernelGGL(gate_quant_kernel<CPT>, dim3(grid), dim3(kGateThreads),
+                       (size_t)a.words * 4, st, a);
     int rc = launch_status();
     if (rc != MIXQ_OK) return rc;
     const int64_t rows_per_block = kReqThreads / kWave;
@@ -311,6 +380,7 @@ extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_
     a.K = (int32_t)K;
     a.ldx = ldx;
     a.tau = threshold;
+    a.tau_bits = half_floor_bits(threshold);
     a.idx = state->idx;
     a.count = state->count;
     a.flag = state->flag;

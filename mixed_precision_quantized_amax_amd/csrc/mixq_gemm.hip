@@ -348,8 +348,14 @@ void gemm_kernel(GemmArgs a) {
             gload(1, S1);
             lstore(S0, 0);
             lstore(S1, 1);
+            // Same issue order as the loop (S0's tile before S1's), kept by
+            // scheduling barriers, so that the waits the compiler derives at
+            // the loop head let S1's loads stay in flight.
+            __builtin_amdgcn_sched_barrier(0);
             if (KT > 2) gload(2, S0);
+            __builtin_amdgcn_sched_barrier(0);
             if (KT > 3) gload(3, S1);
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             lread(sA0, sB0, fa0, fb0);
             __syncthreads();

@@ -17,11 +17,35 @@ int check_device_cached();  // MIXQ_OK / MIXQ_ERR_NO_DEVICE / MIXQ_ERR_UNSUPPORT
 
 inline bool valid_k(int64_t K) { return K > 0 && K % MIXQ_K_MULTIPLE == 0 && K <= MIXQ_K_MAX; }
 
+// Value of a non-negative fp16 bit pattern (host side, exact).
+inline float half_bits_value(uint32_t h) {
+    const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+    if (e == 0u) return ldexpf((float)m, -24);
+    return ldexpf((float)(m + 1024u), (int)e - 25);
+}
+
 inline int64_t outlier_ld(int32_t k_cap) {
     return ((int64_t)k_cap + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
 }
 
 inline int64_t bitmap_words(int64_t K) { return (K + 31) / 32; }
+
+// Bit pattern of the largest finite fp16 value <= t (t >= 0, finite).  For an
+// fp16 value x >= 0:  x > t  <=>  bits(x) > half_floor_bits(t).
+inline uint32_t half_floor_bits(float t) {
+    if (!(t > 0.0f)) return 0u;
+    if (t >= 65504.0f) return 0x7BFFu;
+    // binary search over the bit patterns, which are ordered like the values
+    uint32_t lo = 0u, hi = 0x7BFFu;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1u) / 2u;
+        if (half_bits_value(mid) <= t)
+            lo = mid;
+        else
+            hi = mid - 1u;
+    }
+    return lo;
+}
 
 inline int launch_status() {
     hipError_t e = hipGetLastError();

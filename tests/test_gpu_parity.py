@@ -249,3 +249,18 @@ def test_decode_sequence_full_size(orc):
     assert fired[0]
     for e in events:
         assert fired[e]
+
+
+@pytest.mark.parametrize("tau", [6.0, 6.001, 5.9999, 63.5, 1e-6, 70000.0, 0.0])
+def test_thresholds_between_fp16_values(orc, tau):
+    """The gate and detection compare fp16 data with an fp32 threshold; values
+    that are not fp16 numbers (and the extremes) must decide like the oracle."""
+    rng = np.random.default_rng(17)
+    X = rng.standard_normal((48, 256)).astype(np.float32)
+    X[:, 7] = 6.0            # exactly fp16 6.0
+    X[:, 9] = 6.00390625     # next fp16 after 6.0
+    X[3, 11] = 5.99609375    # previous fp16 before 6.0
+    X[:, 20] = 64.0
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((72, 256)) * 0.05).astype(np.float16)
+    full_compare(orc, X, W, 8, tau, 256, tag=f"tau={tau}")
