@@ -80,24 +80,26 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #define MIXQ_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8)))
 
-// Scheduling pattern for one pipelined tile: the first half of the MFMAs each
-// followed by LDS reads, the second half each followed by LDS writes or global
-// loads (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x200 LDS
-// write, 0x020 global load).
+// Scheduling pattern for one pipelined tile: the first MFMAs each followed by
+// an LDS write or a global load (so the loads issue early and have the whole
+// tile to land), the next ones each followed by LDS reads of the next tile's
+// fragments, then the rest (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS
+// read, 0x200 LDS write, 0x020 global load).
 template <int MF, int RD, int WR, int LD>
 __device__ __forceinline__ void sched_interleave() {
-    constexpr int H = MF / 2;
-    constexpr int rpm = (RD + H - 1) / H;
-    constexpr int opm = (WR + LD + (MF - H) - 1) / (MF - H);
+    constexpr int H = (WR + LD) < MF / 2 ? (WR + LD) : MF / 2;
+    constexpr int opm = (WR + LD + H - 1) / H;
+    constexpr int R = MF - H;
+    constexpr int rpm = (RD + R - 1) / R;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, rpm, 0);
+        __builtin_amdgcn_sched_group_barrier(0x220, opm, 0);
     }
 #pragma unroll
-    for (int i = 0; i < MF - H; ++i) {
+    for (int i = 0; i < R; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x220, opm, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, rpm, 0);
     }
 }
 
@@ -712,8 +714,11 @@ int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
         K % 128 != 0)
         return kCfg128x128;
     if (f >= 1 && f <= 11 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
+    // Large 256x256 tiles (software-pipelined when K allows) once they give
+    // about one tile per CU; 128x128 tiles for thinner products.
     const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-    return big >= 192 ? kCfg256x256 : kCfg128x128;
+    if (big >= 192) return K % 128 == 0 ? kCfg256x256SP : kCfg256x256;
+    return kCfg128x128;
 }
 
 int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
