@@ -150,6 +150,57 @@ def run_gpu(wl, steps: int, warmup: int):
                 copies=copies)
 
 
+def run_decode_sequence(wl, repeats: int = 3):
+    """The outlier-locality decode sequence: every step runs the whole layer on
+    a new batch, the cached set carrying over; the set is re-detected only on
+    steps whose uncached amax crosses the threshold.  Inputs for all steps are
+    generated up front and resident on the GPU.  Returns per-step time."""
+    import torch
+    from mixed_precision_quantized_amax_amd import mixq, workloads
+
+    dev = torch.device("cuda", 0)
+    log(f"[bench] decode sequence: {wl.steps} steps of M={wl.M} K={wl.K} N={wl.N}")
+    W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
+    plan = workloads.decode_plan(wl)
+    Xs = [torch.from_numpy(workloads.decode_step(wl, t, plan)).to(dev) for t in range(wl.steps)]
+    k_cap = 256
+    ld = mixq.outlier_ld(k_cap)
+    Xq = torch.empty(wl.M, wl.K, dtype=torch.int8, device=dev)
+    sx = torch.empty(wl.M, dtype=torch.float32, device=dev)
+    Xo = torch.zeros(wl.M * ld, dtype=torch.float16, device=dev)
+    Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
+    times, fired = [], 0
+    for rep in range(repeats):
+        state = mixq.OutlierState.create(wl.K, k_cap, dev)   # fresh, empty set
+        pw = mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev)
+        mixq.pack_weight(W, state, pw, mixq.PACK_FULL)
+        steps = [mixq.LayerStep(X, wl.tau, state, W, pw, Xq, sx, Xo, Y) for X in Xs]
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for st in steps:
+            st()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / wl.steps)
+        count = int(state.count.cpu()[0])
+    ms = float(np.median(times))
+    return dict(ms_step=ms, count=count)
+
+
+def copy_calibration(nbytes: int = 256 << 20):
+    """A device-to-device copy of known size, so that the HBM byte counters
+    of a profiling run can be scaled (read nbytes, write nbytes)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {nbytes} bytes, 3 times")
+
+
 def run_cpu_baseline(wl, target_s: float = 12.0):
     """The CPU oracle on a row sample of the workload: gate and quantization
     of the sampled tokens, the integer product against all N weight rows, and
@@ -194,6 +245,10 @@ def main():
     ap.add_argument("--workload", default="prefill_w8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (for scaling byte counters)")
+    ap.add_argument("--all", action="store_true",
+                    help="also measure the other workload shapes and the decode sequence")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -204,6 +259,18 @@ def main():
 
     from mixed_precision_quantized_amax_amd import workloads
     wl = workloads.WORKLOADS[args.workload]
+    if args.copy_calibration:
+        copy_calibration()
+    if wl.steps > 1:
+        d = run_decode_sequence(wl)
+        tops = wl.ops / (d["ms_step"] / 1e3) / 1e12
+        print(json.dumps({"metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1,
+                          "steps": wl.steps, "warmup": 0, "ms_per_step": round(d["ms_step"], 5),
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                          "dtype": "i8", "data": "synthetic decode sequence",
+                          "config": {"workload": wl.description, "name": wl.name,
+                                     "outlier_channels_final": d["count"]}}), flush=True)
+        return
     r = run_gpu(wl, args.steps, args.warmup)
     ops = wl.ops
     value = ops / (r["ms_step"] / 1e3) / 1e12
@@ -237,6 +304,22 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
     }
+    if args.all:
+        others = {}
+        for name in ("llama7b_up", "llama70b_up", "prefill_w4"):
+            w2 = workloads.WORKLOADS[name]
+            r2 = run_gpu(w2, max(10, args.steps // 2), args.warmup)
+            others[name] = {"step_tops": round(w2.ops / (r2["ms_step"] / 1e3) / 1e12, 1),
+                            "gemm_tops": round(w2.ops / (r2["gemm_ms"] / 1e3) / 1e12, 1),
+                            "gemm_us": round(r2["gemm_ms"] * 1e3, 1),
+                            "act_quant_us": round(r2["act_ms"] * 1e3, 1),
+                            "ms_per_step": round(r2["ms_step"], 4)}
+        dwl = workloads.WORKLOADS["decode_seq"]
+        d = run_decode_sequence(dwl)
+        others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),
+                                "ms_per_step": round(d["ms_step"], 4),
+                                "outlier_channels_final": d["count"]}
+        out["workloads"] = others
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
