@@ -350,13 +350,15 @@ void gemm_kernel(GemmArgs a) {
             gload(1, S1);
             lstore(S0, 0);
             lstore(S1, 1);
-            // Same issue order as the loop (S0's tile before S1's), kept by
-            // scheduling barriers, so that the waits the compiler derives at
-            // the loop head let S1's loads stay in flight.
+            // Same issue order as the loop (S0's tile before S1's), and no
+            // condition: every path into the loop then has S1's loads newest,
+            // so the waits derived at the loop head leave them in flight.  For
+            // KT < 4 the extra loads read past the row's K range, which stays
+            // inside the buffer (or reads zeros past its end) and is unused.
             __builtin_amdgcn_sched_barrier(0);
-            if (KT > 2) gload(2, S0);
+            gload(2, S0);
             __builtin_amdgcn_sched_barrier(0);
-            if (KT > 3) gload(3, S1);
+            gload(3, S1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             lread(sA0, sB0, fa0, fb0);
