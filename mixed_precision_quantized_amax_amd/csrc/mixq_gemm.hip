@@ -23,8 +23,12 @@
 //   chunk c of row r is stored at slot c ^ swz(r) so that both the
 //   row-contiguous writes and the MFMA fragment reads (32 rows, one chunk
 //   each) hit distinct banks.
-//   Two LDS stages: global loads for tile k+1 are in flight in registers
-//   while tile k is multiplied.
+//   Large products with INT8 weights use 128-byte K pairs: each global load
+//   instruction covers eight rows x 128 bytes (whole L2 lines), two pair
+//   buffers in LDS, two fragment register sets, and a fixed issue order that
+//   spreads a phase's LDS reads, LDS writes and global loads over its MFMAs.
+//   The other variants (64-byte K steps, register-staged or LDS-direct) serve
+//   INT4 weights, K not a multiple of 128 and thin products.
 //   Tile order: consecutive block ids go to different XCDs (round-robin), so
 //   block ids are remapped to give each XCD a compact rectangle of tiles that
 //   share A rows and B rows in its L2.
@@ -248,7 +252,182 @@ void gemm_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::kFM * C::kFN, 0);
     };
 
-    if constexpr (STAGES == 2) {
+    if constexpr (PF == 5 || PF == 6) {
+        // ---- 128-byte K pairs, register-staged ------------------------------------------
+        // Global loads fetch 128 bytes of K per row (eight lanes per row),
+        // i.e. whole L2 lines: with 64-byte row pieces every request moves
+        // half a line and the L2 delivers markedly fewer bytes per clock.
+        // LDS holds two pair buffers, each A[BM][128] + B[BN][128]; chunk c of
+        // row r sits at slot c ^ (r & 7), which keeps both the linear
+        // per-lane writes and the 32-row fragment reads on distinct banks.
+        // Tiles (64 bytes of K) alternate between two fragment register sets:
+        //   phase A of pair p: MFMAs of tile 2p; read tile 2p+1 (pair p, upper
+        //     half); write pair p+1's B rows; load pair p+2's B rows; barrier.
+        //   phase B of pair p: MFMAs of tile 2p+1; read tile 2p+2 (pair p+1,
+        //     lower half); write pair p+2's A rows; load pair p+3's A rows.
+        // Every load has two phases to land, each phase carries the same mix
+        // of MFMAs, LDS reads, LDS writes and global loads, and the one
+        // barrier per pair orders all buffer reuse: a pair buffer is rewritten
+        // only after the barrier that follows the last read of its previous
+        // pair.
+        static_assert(BITS == 8 && STAGES == 4, "pair loader: int8 operands, four 32 KiB arrays");
+        constexpr int kPR = 2 * kBK;           // LDS row bytes
+        constexpr int kPI = BM / 8 / C::kNW;   // load instructions per operand per wave
+        static_assert(BM == BN && BM * kPR == kStageBytes, "pair buffer = one stage array");
+        auto PA = [&](int c) { return c ? sS2 : sS0; };
+        auto PB = [&](int c) { return c ? sS3 : sS1; };
+        const int KP = K / kPR;
+        // load lane -> row (i*NW + wave)*8 + lane/8 (so row & 7 == lane/8), LDS slot lane%8,
+        // holding chunk (lane%8) ^ (lane/8); the LDS write of a wave instruction is linear
+        const int lr = lane >> 3, ls = lane & 7;
+        int voff[kPI];
+#pragma unroll
+        for (int i = 0; i < kPI; ++i) voff[i] = ((i * C::kNW + wave) * 8 + lr) * K + ((ls ^ lr) << 4);
+        const int wr = wave * 8 * kPR + lane * 16;  // + i * NW * 8 * kPR
+        // fragment reads: tile half h, K half ks -> chunk 4h + 2ks + fh of row r, r & 7 == fr & 7
+        int rdA2[2][2], rdB2[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int sl = ((4 * h + 2 * ks + fh) ^ (fr & 7)) << 4;
+                rdA2[h][ks] = (wm * C::kWTM + fr) * kPR + sl;
+                rdB2[h][ks] = (wn * C::kWTN + fr) * kPR + sl;
+            }
+        typedef v4i Stg[kPI];
+        typedef v4i AFr[2][C::kFM];
+        typedef v4i BFr[2][C::kFN];
+        // Pair offsets go into the per-lane offset, which the buffer range
+        // check covers: loads of rows past the tile's last row read zeros.
+        auto gload = [&](const __amdgpu_buffer_rsrc_t& r, int p, Stg& S) {
+#pragma unroll
+            for (int i = 0; i < kPI; ++i)
+                S[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i] + p * kPR, 0, 0);
+        };
+        auto lstore = [&](const Stg& S, uint8_t* buf) {
+#pragma unroll
+            for (int i = 0; i < kPI; ++i)
+                *reinterpret_cast<v4i*>(&buf[wr + i * C::kNW * 8 * kPR]) = S[i];
+        };
+        auto lread = [&](const uint8_t* Ab, const uint8_t* Bb, int h, AFr& fa, BFr& fb) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int i = 0; i < C::kFM; ++i)
+                    fa[ks][i] = *reinterpret_cast<const v4i*>(Ab + rdA2[h][ks] + i * 32 * kPR);
+#pragma unroll
+                for (int j = 0; j < C::kFN; ++j)
+                    fb[ks][j] = *reinterpret_cast<const v4i*>(Bb + rdB2[h][ks] + j * 32 * kPR);
+            }
+        };
+        auto mfmas = [&](const AFr& fa, const BFr& fb) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::kFN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ks][i], fb[ks][j],
+                                                                          acc[i][j], 0, 0, 0);
+        };
+        AFr fa0, fa1;
+        BFr fb0, fb1;
+        Stg SA, SB;
+        // prologue: pair 0 to LDS, tile 0 to registers, pair 1's A rows to
+        // LDS, loads of pair 1's B rows and pair 2's A rows in flight.  No
+        // conditions, so that the loop is entered with the same loads in
+        // flight, in the same order, on every path and its waits count
+        // exactly; for K < 384 the extra loads fetch bytes past the row's end,
+        // from the next row (or zeros past the buffer), which are never read.
+        gload(rA, 0, SA);
+        gload(rB, 0, SB);
+        lstore(SA, PA(0));
+        lstore(SB, PB(0));
+        gload(rA, 1, SA);
+        gload(rB, 1, SB);
+        __syncthreads();
+        lread(PA(0), PB(0), 0, fa0, fb0);
+        lstore(SA, PA(1));
+        gload(rA, 2, SA);
+        int p = 0;
+        // steady state: every load, write and read of the pair exists
+        if constexpr (PF == 6) {
+            // Issue order pinned slot by slot (the scheduler may not move
+            // anything across a slot): each of a phase's 32 MFMAs is followed
+            // by at most one LDS read or one LDS write + global load, reads
+            // first (their results are needed right after the phase), the
+            // write/load pairs next, the last eight MFMAs alone -- so the
+            // phase's LDS operations have completed when the barrier's wait
+            // comes and the matrix pipe never idles behind them.
+            constexpr int kMF = 2 * C::kFM * C::kFN;   // 32 MFMAs per phase
+            constexpr int kRD = 2 * (C::kFM + C::kFN); // 16 fragment reads
+            static_assert(kMF == 32 && kRD == 16 && kPI == 8, "slot plan for 128x128 waves");
+            auto mf = [&](const AFr& fa, const BFr& fb, int t) {
+                const int ks = t >> 4, i = (t >> 2) & 3, j = t & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ks][i], fb[ks][j], acc[i][j],
+                                                                  0, 0, 0);
+            };
+            auto rd = [&](const uint8_t* Ab, const uint8_t* Bb, int h, AFr& fa, BFr& fb, int r) {
+                const int ks = r >> 3, q = r & 7;
+                if (q < 4)
+                    fa[ks][q] = *reinterpret_cast<const v4i*>(Ab + rdA2[h][ks] + q * 32 * kPR);
+                else
+                    fb[ks][q - 4] =
+                        *reinterpret_cast<const v4i*>(Bb + rdB2[h][ks] + (q - 4) * 32 * kPR);
+            };
+            auto wl = [&](Stg& S, uint8_t* buf, const __amdgpu_buffer_rsrc_t& r, int pl, int w) {
+                *reinterpret_cast<v4i*>(&buf[wr + w * C::kNW * 8 * kPR]) = S[w];
+                S[w] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[w] + pl * kPR, 0, 0);
+            };
+            for (; p + 3 < KP; ++p) {
+                const int c = p & 1, n = c ^ 1;
+#pragma unroll
+                for (int t = 0; t < kMF; ++t) {
+                    mf(fa0, fb0, t);
+                    if (t < kRD) rd(PA(c), PB(c), 1, fa1, fb1, t);
+                    else if (t < kRD + kPI) wl(SB, PB(n), rB, p + 2, t - kRD);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int t = 0; t < kMF; ++t) {
+                    mf(fa1, fb1, t);
+                    if (t < kRD) rd(PA(n), PB(n), 0, fa0, fb0, t);
+                    else if (t < kRD + kPI) wl(SA, PA(c), rA, p + 3, t - kRD);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            for (; p + 3 < KP; ++p) {
+                const int c = p & 1, n = c ^ 1;
+                lread(PA(c), PB(c), 1, fa1, fb1);
+                mfmas(fa0, fb0);
+                lstore(SB, PB(n));
+                gload(rB, p + 2, SB);
+                sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN), kPI, kPI>();
+                __syncthreads();
+                lread(PA(n), PB(n), 0, fa0, fb0);
+                mfmas(fa1, fb1);
+                lstore(SA, PA(c));
+                gload(rA, p + 3, SA);
+                sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN), kPI, kPI>();
+            }
+        }
+        // last pairs
+        for (; p < KP; ++p) {
+            const int c = p & 1, n = c ^ 1;
+            lread(PA(c), PB(c), 1, fa1, fb1);
+            mfmas(fa0, fb0);
+            if (p + 1 < KP) lstore(SB, PB(n));
+            if (p + 2 < KP) gload(rB, p + 2, SB);
+            __syncthreads();
+            if (p + 1 < KP) lread(PA(n), PB(n), 0, fa0, fb0);
+            mfmas(fa1, fb1);
+            if (p + 2 < KP) lstore(SA, PA(c));
+            if (p + 3 < KP) gload(rA, p + 3, SA);
+        }
+        __syncthreads();
+    } else if constexpr (STAGES == 2) {
         // ---- register-staged, double-buffered LDS ------------------------------------
         // Global loads run PF tiles ahead of the multiply, in PF register sets.
         struct Regs {
@@ -702,6 +881,8 @@ enum {
     kCfg256x128AD = 9, // 4 waves of 128x64, A fragments from global, B via LDS
     kCfg256x256SP = 10,  // 4 waves of 128x128, cross-tile software pipeline
     kCfg256x128SP = 11,  // 4 waves of 128x64, cross-tile software pipeline
+    kCfg256x256KP = 12,  // 4 waves of 128x128, 128-byte K pairs (whole-line loads)
+    kCfg256x256KS = 13,  // as 12, issue order pinned slot by slot
 };
 
 int forced_cfg() {
@@ -712,14 +893,19 @@ int forced_cfg() {
 int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     const int f = forced_cfg();
     if ((f == kCfg256x256P2 || f == kCfg256x128P2 || f == kCfg256x256AD || f == kCfg256x128AD ||
-         f == kCfg256x256SP || f == kCfg256x128SP) &&
+         f == kCfg256x256SP || f == kCfg256x128SP || f == kCfg256x256KP ||
+         f == kCfg256x256KS) &&
         K % 128 != 0)
         return kCfg128x128;
-    if (f >= 1 && f <= 11 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
+    if ((f == kCfg256x256KP || f == kCfg256x256KS) && bits == 4) return kCfg256x256SP;
+    if (f >= 1 && f <= 13 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
     // Large 256x256 tiles (software-pipelined when K allows) once they give
     // about one tile per CU; 128x128 tiles for thinner products.
     const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-    if (big >= 192) return K % 128 == 0 ? kCfg256x256SP : kCfg256x256;
+    if (big >= 192) {
+        if (K % 128 != 0) return kCfg256x256;
+        return bits == 8 ? kCfg256x256KS : kCfg256x256SP;
+    }
     return kCfg128x128;
 }
 
@@ -735,6 +921,8 @@ int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
         case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 8, 2, 3>(a, debug, st);
         case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 8, 2, 4>(a, debug, st);
         case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 8, 2, 4>(a, debug, st);
+        case kCfg256x256KP: return launch_cfg<256, 256, 2, 2, 8, 4, 5>(a, debug, st);
+        case kCfg256x256KS: return launch_cfg<256, 256, 2, 2, 8, 4, 6>(a, debug, st);
         default: return launch_cfg<128, 128, 2, 2, 8, 2>(a, debug, st);
     }
 }
