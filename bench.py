@@ -240,8 +240,10 @@ def run_cpu_baseline(wl, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # the engine clock ramps up over tens of milliseconds of sustained work;
+    # 200 steps (about 35 ms) reach the steady state the timed steps measure
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill_w8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
