@@ -83,13 +83,15 @@ __device__ __forceinline__ uint16_t half_at(const uint4& v, int e) {
     return (uint16_t)(w >> ((e & 1) * 16));
 }
 
-// Code of one value: round half to even of x*r, clamped to [-127, 127].
-// The product is one fp32 rounding (fma with a zero addend); adding
-// 1.5 * 2^23 to a value in [-127, 127] rounds it to the nearest integer
-// (ties to even) and leaves that integer in the low bits of the sum.
+// Code of one value: round half to even of x*r.  The product is one fp32
+// rounding (fma with a zero addend, the fp16 operand widened exactly);
+// adding 1.5 * 2^23 rounds it to the nearest integer (ties to even) and
+// leaves that integer in the low bits of the sum.  No clamp is needed: every
+// quantized value satisfies |x| <= g with r = fl(127 / g), so
+// |fl(x * r)| <= 127 (1 + 2^-24)^2 < 127.5 and the code is within [-127, 127]
+// (finite inputs; g = 0 gives r = 1 and all-zero values).
 __device__ __forceinline__ uint32_t code_bits(uint16_t h, float r) {
-    float t = __builtin_fmaf(half_bits_to_float(h), r, 0.0f);
-    t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
+    const float t = __builtin_fmaf(half_bits_to_float(h), r, 0.0f);
     return __float_as_uint(t + 12582912.0f);
 }
 
@@ -109,7 +111,11 @@ __device__ __forceinline__ uint32_t pack4(uint32_t u0, uint32_t u1, uint32_t u2,
 // The amax is taken on the fp16 bit patterns: for non-negative halves the
 // integer order is the value order, so the packed unsigned max is exact.
 // Returns (in every lane) whether this token had an uncached value above tau.
-template <int CPT>
+//   GATHER_IDX: X_out is filled from the ascending channel list a.idx (the
+//   committed set) with one coalesced pass per row; otherwise from the
+//   bitmap and rank table (the set being formed, whose list does not exist
+//   yet).
+template <int CPT, bool GATHER_IDX>
 __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_words,
                          const int32_t* rank, int set_size, const uint4* lut, uint32_t* newbits) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -128,7 +134,7 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
             if (c < a.nchunks) {
                 xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
                 wv[i] = set_words[c >> 2];
-                rk[i] = rank[c >> 2];
+                rk[i] = GATHER_IDX ? 0 : rank[c >> 2];
             } else {
                 xv[i] = make_uint4(0, 0, 0, 0);
                 wv[i] = 0u;
@@ -206,7 +212,7 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
             for (int e = 0; e < 8; ++e) u[e] = code_bits((uint16_t)(m[e >> 1] >> ((e & 1) * 16)), r);
             *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) =
                 make_uint2(pack4(u[0], u[1], u[2], u[3]), pack4(u[4], u[5], u[6], u[7]));
-            if (cb) {
+            if (!GATHER_IDX && cb) {
                 // outlier channels: column in X_out = rank in the set
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -218,6 +224,11 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
         }
     }
     if (orow) {
+        if constexpr (GATHER_IDX) {
+            // the row is still in the caches: one gather load and one
+            // contiguous store per 64 set members
+            for (int j = lane; j < set_size; j += kWave) orow[j] = xr[a.idx[j]];
+        }
         const int kpad = (set_size + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
         for (int j = set_size + lane; j < kpad; j += kWave) orow[j] = 0;
     }
@@ -226,23 +237,153 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
 
 constexpr int kGateThreads = 256;
 
-template <int CPT>
+// The steady-state pass: W waves per token, each owning a contiguous part of
+// the row (CPT chunks per lane and segment), so that a token's chain of
+// load -> amax -> quantize -> store is W times shorter than with one wave per
+// token and the memory traffic of the waves overlaps.  The token's amax is
+// combined through LDS (one barrier per token group).  The cached set's
+// bitmap is staged in LDS; the outlier gather reads the committed channel
+// list and issues its loads together with the row's, so their latency hides
+// behind the amax.
+template <int CPT, int W>
 __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
-    extern __shared__ uint32_t newbits[];  // [words]
+    constexpr int kRB = kGateThreads / kWave / W;  // tokens per block and round
+    extern __shared__ uint32_t dyn[];              // newbits[words], sbits[words]
+    uint32_t* const newbits = dyn;
+    uint32_t* const sbits = dyn + a.words;
     __shared__ uint4 lut[kLutEntries];
+    __shared__ uint32_t red[2][kRB][W];
     __shared__ int any_det;
     build_keep_lut(lut);
-    for (int w = threadIdx.x; w < a.words; w += kGateThreads) newbits[w] = 0u;
+    for (int w = threadIdx.x; w < a.words; w += kGateThreads) {
+        newbits[w] = 0u;
+        sbits[w] = a.bitmap[w];
+    }
     if (threadIdx.x == 0) any_det = 0;
-    __syncthreads();
     const int set_size = *a.count;
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    constexpr int kWavesPerBlock = kGateThreads / kWave;
+    const int slot = wave / W, part = wave % W;
+    const int seg_chunks = W * kWave * CPT;
+    const int nseg = (a.nchunks + seg_chunks - 1) / seg_chunks;
+    const int kpad = (set_size + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
     bool det = false;
-    for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < a.M;
-         row += (int64_t)gridDim.x * kWavesPerBlock)
-        det |= wave_row<CPT>(a, row, a.bitmap, a.rank, set_size, lut, newbits);
-    if (det && (threadIdx.x & (kWave - 1)) == 0) any_det = 1;
+    int parity = 0;
+    // block-uniform loop (the barrier inside needs every wave)
+    for (int64_t row0 = (int64_t)blockIdx.x * kRB; row0 < a.M;
+         row0 += (int64_t)gridDim.x * kRB, parity ^= 1) {
+        const int64_t row = row0 + slot;
+        const bool valid = row < a.M;
+        const uint16_t* xr = a.X + (valid ? row : 0) * a.ldx;
+        uint16_t* orow = (a.ld_out && valid) ? a.X_out + row * (int64_t)a.ld_out : nullptr;
+
+        uint4 xv[CPT];
+        uint32_t wv[CPT];
+        auto chunk = [&](int s, int i) { return s * seg_chunks + (part * CPT + i) * kWave + lane; };
+        auto load_seg = [&](int s) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = chunk(s, i);
+                if (valid && c < a.nchunks) {
+                    xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
+                    wv[i] = sbits[c >> 2];
+                } else {
+                    xv[i] = make_uint4(0, 0, 0, 0);
+                    wv[i] = 0u;
+                }
+            }
+        };
+        auto keep_of = [&](int i, int c) -> uint4 { return lut[(wv[i] >> ((c & 3) * 8)) & 0xFFu]; };
+
+        load_seg(0);
+        // first gather round, loads issued with the row's
+        const int gj = part * kWave + lane;
+        const bool gon = orow != nullptr && gj < set_size;
+        uint16_t gval = 0;
+        if (gon) gval = xr[a.idx[gj]];
+
+        uint32_t amx = 0;
+        for (int s = 0; s < nseg; ++s) {
+            if (s > 0) load_seg(s);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const uint4 kp = keep_of(i, chunk(s, i));
+                amx = pk_max_u16(amx, xv[i].x & kp.x & 0x7FFF7FFFu);
+                amx = pk_max_u16(amx, xv[i].y & kp.y & 0x7FFF7FFFu);
+                amx = pk_max_u16(amx, xv[i].z & kp.z & 0x7FFF7FFFu);
+                amx = pk_max_u16(amx, xv[i].w & kp.w & 0x7FFF7FFFu);
+            }
+        }
+        uint32_t gb = max(amx & 0xFFFFu, amx >> 16);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1)
+            gb = max(gb, (uint32_t)__shfl_xor((int)gb, o, kWave));
+        if (lane == 0) red[parity][slot][part] = gb;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < W; ++w) gb = max(gb, red[parity][slot][w]);
+
+        if (gb > a.tau_bits) {
+            // The gate fired for this token (rare): mark every uncached
+            // channel of this wave's part above the threshold.
+            for (int s = 0; s < nseg; ++s) {
+                if (nseg > 1) load_seg(s);
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    const int c = chunk(s, i);
+                    if (!valid || c >= a.nchunks) continue;
+                    const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
+                    uint32_t over = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (!((cb >> e) & 1u) && (uint32_t)(half_at(xv[i], e) & 0x7FFFu) > a.tau_bits)
+                            over |= 1u << e;
+                    if (over) atomicOr(&newbits[c >> 2], over << ((c & 3) * 8));
+                }
+            }
+            det = true;
+        }
+
+        // scale and reciprocal: single IEEE divisions; zero amax -> 1
+        const float g = half_bits_to_float((uint16_t)gb);
+        float sc, r;
+        if (gb == 0u) {
+            sc = 1.0f;
+            r = 1.0f;
+        } else {
+            sc = g / 127.0f;
+            r = 127.0f / g;
+        }
+        if (valid && part == 0 && lane == 0) a.s_x[row] = sc;
+
+        int8_t* qr = a.Xq + (valid ? row : 0) * (int64_t)a.K;
+        for (int s = 0; s < nseg; ++s) {
+            if (nseg > 1) load_seg(s);  // the part did not fit in registers: read it again
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = chunk(s, i);
+                if (!valid || c >= a.nchunks) continue;
+                const uint4 kp = keep_of(i, c);
+                // cached channels become +0 and so get code 0
+                const uint32_t m[4] = {xv[i].x & kp.x, xv[i].y & kp.y, xv[i].z & kp.z,
+                                       xv[i].w & kp.w};
+                uint32_t u[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    u[e] = code_bits((uint16_t)(m[e >> 1] >> ((e & 1) * 16)), r);
+                *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) =
+                    make_uint2(pack4(u[0], u[1], u[2], u[3]), pack4(u[4], u[5], u[6], u[7]));
+            }
+        }
+        if (orow) {
+            if (gon) orow[gj] = gval;
+            for (int j = gj + W * kWave; j < set_size; j += W * kWave) orow[j] = xr[a.idx[j]];
+            for (int j = set_size + gj; j < kpad; j += W * kWave) orow[j] = 0;
+        }
+    }
+    if (det && lane == 0) any_det = 1;
     __syncthreads();
     if (any_det) {  // block-uniform: only blocks whose tokens crossed the gate
         for (int w = threadIdx.x; w < a.words; w += kGateThreads)
@@ -302,7 +443,7 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
         const int64_t stride = (int64_t)gridDim.x * (kReqThreads / kWave);
         for (int64_t row = (int64_t)blockIdx.x * (kReqThreads / kWave) + wave; row < a.M;
              row += stride)
-            wave_row<CPT>(a, row, neww, prefix, total, lut, nullptr);
+            wave_row<CPT, false>(a, row, neww, prefix, total, lut, nullptr);
     }
     // arrival (fired calls only): the last block commits
     __syncthreads();
@@ -334,21 +475,34 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
     }
 }
 
-template <int CPT>
+constexpr int kGateWaves = 4;  // waves per token in the steady-state pass
+
+template <int CPT_G, int CPT_R>
 int launch_act(const ActArgs& a, hipStream_t st) {
-    constexpr int kRowsPerBlock = kGateThreads / kWave;
+    constexpr int kRowsPerBlock = kGateThreads / kWave / kGateWaves;
     int64_t g1 = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int grid = (int)(g1 < 2048 ? g1 : 2048);
-    hipLaunchKernelGGL(gate_quant_kernel<CPT>, dim3(grid), dim3(kGateThreads),
-                       (size_t)a.words * 4, st, a);
+    const int grid = (int)(g1 < 16384 ? g1 : 16384);
+    hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves>), dim3(grid), dim3(kGateThreads),
+                       (size_t)a.words * 8, st, a);
     int rc = launch_status();
     if (rc != MIXQ_OK) return rc;
     const int64_t rows_per_block = kReqThreads / kWave;
     int64_t g2 = (a.M + rows_per_block - 1) / rows_per_block;
     if (g2 > 128) g2 = 128;
-    hipLaunchKernelGGL(requant_kernel<CPT>, dim3((int)g2), dim3(kReqThreads),
+    hipLaunchKernelGGL(requant_kernel<CPT_R>, dim3((int)g2), dim3(kReqThreads),
                        (size_t)a.words * 8, st, a);
     return launch_status();
+}
+
+template <int CPT_G>
+int launch_act_r(const ActArgs& a, int64_t K, hipStream_t st) {
+    // requant: one wave per token, the whole row in registers up to K = 8192
+    const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
+    if (per_lane <= 1) return launch_act<CPT_G, 1>(a, st);
+    if (per_lane <= 2) return launch_act<CPT_G, 2>(a, st);
+    if (per_lane <= 4) return launch_act<CPT_G, 4>(a, st);
+    if (per_lane <= 8) return launch_act<CPT_G, 8>(a, st);
+    return launch_act<CPT_G, 16>(a, st);
 }
 
 }  // namespace
@@ -398,11 +552,12 @@ extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_
     a.ld_out = (int32_t)outlier_ld(state->k_cap);
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    // chunks per lane and segment: the whole row in registers up to K = 8192
-    const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) return launch_act<1>(a, st);
-    if (per_lane <= 2) return launch_act<2>(a, st);
-    if (per_lane <= 4) return launch_act<4>(a, st);
-    if (per_lane <= 8) return launch_act<8>(a, st);
-    return launch_act<16>(a, st);
+    // steady-state pass: chunks per lane and segment, the whole row in
+    // registers of its kGateWaves waves up to K = 32768
+    const int64_t per_lane = (K / 8 + kWave * kGateWaves - 1) / (kWave * kGateWaves);
+    if (per_lane <= 1) return launch_act_r<1>(a, K, st);
+    if (per_lane <= 2) return launch_act_r<2>(a, K, st);
+    if (per_lane <= 4) return launch_act_r<4>(a, K, st);
+    if (per_lane <= 8) return launch_act_r<8>(a, K, st);
+    return launch_act_r<16>(a, K, st);
 }

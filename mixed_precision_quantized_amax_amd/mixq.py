@@ -253,6 +253,28 @@ class LayerStep:
                 _check(name, rc)
 
 
+class LayerGraph:
+    """One layer step captured into a HIP graph: a replay launches the step's
+    kernels without a host round trip per kernel.  Nothing is cached in the
+    graph but the launches -- every kernel reads the outlier state and the
+    activations from device memory on each replay, so a replay computes what
+    the same three eager calls would (a gate firing during a replay included).
+    The step allocates nothing and records no memory fills, so it captures
+    as is.  Arguments are those of ``LayerStep`` (without ``stream``)."""
+
+    def __init__(self, *args, **kwargs):
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            # built inside the capture so that it binds the capture stream
+            self.step = LayerStep(*args, **kwargs)
+            self.step()
+
+    def replay(self):
+        self.graph.replay()
+
+    __call__ = replay
+
+
 class MixQLinear:
     """Y = X W^T through the three library calls, with the outlier set cached
     across calls (the layer the MixQ article describes)."""
