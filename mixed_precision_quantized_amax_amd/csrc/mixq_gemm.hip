@@ -883,6 +883,7 @@ enum {
     kCfg256x128SP = 11,  // 4 waves of 128x64, cross-tile software pipeline
     kCfg256x256KP = 12,  // 4 waves of 128x128, 128-byte K pairs (whole-line loads)
     kCfg256x256KS = 13,  // as 12, issue order pinned slot by slot
+    kCfg128x128KP = 14,  // 4 waves of 64x64, 128-byte K pairs
 };
 
 int forced_cfg() {
@@ -894,19 +895,21 @@ int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     const int f = forced_cfg();
     if ((f == kCfg256x256P2 || f == kCfg256x128P2 || f == kCfg256x256AD || f == kCfg256x128AD ||
          f == kCfg256x256SP || f == kCfg256x128SP || f == kCfg256x256KP ||
-         f == kCfg256x256KS) &&
+         f == kCfg256x256KS || f == kCfg128x128KP) &&
         K % 128 != 0)
         return kCfg128x128;
     if ((f == kCfg256x256KP || f == kCfg256x256KS) && bits == 4) return kCfg256x256SP;
-    if (f >= 1 && f <= 13 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
+    if (f == kCfg128x128KP && bits == 4) return kCfg128x128;
+    if (f >= 1 && f <= 14 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
     // Large 256x256 tiles (software-pipelined when K allows) once they give
-    // about one tile per CU; 128x128 tiles for thinner products.
+    // about one tile per CU; 128x128 tiles (K pairs for INT8 weights) for
+    // thinner products.
     const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
     if (big >= 192) {
         if (K % 128 != 0) return kCfg256x256;
         return bits == 8 ? kCfg256x256KS : kCfg256x256SP;
     }
-    return kCfg128x128;
+    return bits == 8 && K % 128 == 0 ? kCfg128x128KP : kCfg128x128;
 }
 
 int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
@@ -923,6 +926,7 @@ int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
         case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 8, 2, 4>(a, debug, st);
         case kCfg256x256KP: return launch_cfg<256, 256, 2, 2, 8, 4, 5>(a, debug, st);
         case kCfg256x256KS: return launch_cfg<256, 256, 2, 2, 8, 4, 6>(a, debug, st);
+        case kCfg128x128KP: return launch_cfg<128, 128, 2, 2, 8, 4, 5>(a, debug, st);
         default: return launch_cfg<128, 128, 2, 2, 8, 2>(a, debug, st);
     }
 }
