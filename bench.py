@@ -92,7 +92,8 @@ def run_gpu(wl, steps: int, warmup: int):
     Xo = [torch.zeros(wl.M * ld, dtype=torch.float16, device=dev) for _ in range(copies)]
     Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    steps_c = [mixq.LayerStep(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y)
+    ws = mixq.gemm_workspace(wl.M, wl.N, wl.K, wl.bits, dev)  # split K (thin shapes only)
+    steps_c = [mixq.LayerStep(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws)
                for c in range(copies)]
 
     def step(i, ev=None):
@@ -113,7 +114,7 @@ def run_gpu(wl, steps: int, warmup: int):
     log(f"[bench] outlier channels detected: {count}; weight copies: {copies}")
     # one captured graph per buffer copy: a replay launches the step's four
     # kernels without a host round trip per kernel
-    graphs = [mixq.LayerGraph(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y)
+    graphs = [mixq.LayerGraph(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws)
               for c in range(copies)]
     for i in range(warmup):
         step(i)
@@ -183,12 +184,13 @@ def run_decode_sequence(wl, repeats: int = 3):
     sx = torch.empty(wl.M, dtype=torch.float32, device=dev)
     Xo = torch.zeros(wl.M * ld, dtype=torch.float16, device=dev)
     Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
+    ws = mixq.gemm_workspace(wl.M, wl.N, wl.K, wl.bits, dev)  # split K
     times, fired = [], 0
     for rep in range(repeats):
         state = mixq.OutlierState.create(wl.K, k_cap, dev)   # fresh, empty set
         pw = mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev)
         mixq.pack_weight(W, state, pw, mixq.PACK_FULL)
-        steps = [mixq.LayerStep(X, wl.tau, state, W, pw, Xq, sx, Xo, Y) for X in Xs]
+        steps = [mixq.LayerStep(X, wl.tau, state, W, pw, Xq, sx, Xo, Y, ws=ws) for X in Xs]
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)

@@ -212,6 +212,36 @@ int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
               const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
               int64_t ldy, int32_t *acc_debug, void *stream);
 
+/*
+ * mixq_gemm_ws -- mixq_gemm with a split-K workspace, for thin products (few
+ * tokens: the decode phase).  FP6 explainer, sections 2.2-2.3: such GEMMs
+ * leave most compute units idle unless K is split, the partial results being
+ * reduced through a workspace.
+ *
+ * When the product (INT8 weights, K a multiple of 256) has fewer 128 x 128
+ * output tiles than the device has compute units, each tile's K range is
+ * split in two blocks.  Both store their exact int32 partial tile in ws; the
+ * second to finish adds the other's and runs the epilogue.  No block waits
+ * for another.  Integer partial sums make acc and Y bit-identical to the
+ * unsplit product.  Otherwise, or when ws is NULL or smaller than required,
+ * the call is mixq_gemm.
+ *
+ *   ws        device memory of ws_bytes, 16-byte aligned; its first 4096 bytes
+ *             (tile counters) must be zero-filled once by the caller, after
+ *             which every completed call leaves them zero.  Calls sharing a
+ *             ws must not overlap (one stream, or serialized).
+ *   ws_bytes  at least mixq_gemm_workspace_bytes(M, N, K, bits) for the split
+ * Other arguments and errors: as mixq_gemm.
+ */
+int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
+                 const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
+                 int64_t ldy, int32_t *acc_debug, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes mixq_gemm_ws needs to split this product on a device with
+ * 256 compute units (MI355X): 4096 bytes of tile counters plus two 64 KiB
+ * partial tiles per 128 x 128 output tile; 0 when the product is not split. */
+size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
+
 /* Text of a status code (static storage). */
 const char *mixq_status_string(int status);
 

@@ -41,9 +41,42 @@ int check_device_cached() {
     return cache[dev];
 }
 
+int device_cu_count() {
+    static std::mutex mu;
+    static int cache[64];
+    static bool init = false;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!init) {
+        for (int i = 0; i < 64; ++i) cache[i] = -1;
+        init = true;
+    }
+    if (cache[dev] < 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            n = 0;
+        }
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 }  // namespace mixq
 
 extern "C" {
+
+size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
+    using namespace mixq;
+    const int S = split_plan(M, N, K, bits, 256);
+    if (S <= 1) return 0;
+    return (size_t)split_workspace_bytes(M, N, S);
+}
+
 
 int64_t mixq_outlier_ld(int32_t k_cap) { return k_cap <= 0 ? 0 : mixq::outlier_ld(k_cap); }
 

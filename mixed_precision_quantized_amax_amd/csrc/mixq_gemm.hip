@@ -60,6 +60,10 @@ struct GemmArgs {
     int64_t ldy;
     int32_t* acc_debug;
     int32_t tiles_m, tiles_n;
+    // split K (K-pair kernels): ksplit blocks per output tile, 1 or 2
+    int32_t ksplit;
+    int32_t* sync;  // [tiles] arrival counters, zero between calls
+    int32_t* part;  // [tiles][2] int32 partial tiles
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -165,11 +169,14 @@ void gemm_kernel(GemmArgs a) {
     int bid = blockIdx.x;
     const int T = gridDim.x;
     if ((T & 7) == 0) bid = (bid & 7) * (T >> 3) + (bid >> 3);
+    // the split blocks of a tile are consecutive ids (the same XCD after the remap)
+    const int split = bid % a.ksplit;
+    const int tbid = bid / a.ksplit;
     const int gm = a.tiles_m < 8 ? a.tiles_m : 8;
-    const int group = bid / (gm * a.tiles_n);
+    const int group = tbid / (gm * a.tiles_n);
     const int first_m = group * gm;
     const int gsize = min(gm, a.tiles_m - first_m);
-    const int within = bid - group * gm * a.tiles_n;
+    const int within = tbid - group * gm * a.tiles_n;
     const int tm = first_m + within % gsize;
     const int tn = within / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
@@ -276,7 +283,9 @@ void gemm_kernel(GemmArgs a) {
         static_assert(BM == BN && BM * kPR == kStageBytes, "pair buffer = one stage array");
         auto PA = [&](int c) { return c ? sS2 : sS0; };
         auto PB = [&](int c) { return c ? sS3 : sS1; };
-        const int KP = K / kPR;
+        // this block's K range: pairs pb .. pb + KP - 1
+        const int KP = K / kPR / a.ksplit;
+        const int pb = split * KP;
         // load lane -> row (i*NW + wave)*8 + lane/8 (so row & 7 == lane/8), LDS slot lane%8,
         // holding chunk (lane%8) ^ (lane/8); the LDS write of a wave instruction is linear
         const int lr = lane >> 3, ls = lane & 7;
@@ -302,7 +311,7 @@ void gemm_kernel(GemmArgs a) {
         auto gload = [&](const __amdgpu_buffer_rsrc_t& r, int p, Stg& S) {
 #pragma unroll
             for (int i = 0; i < kPI; ++i)
-                S[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i] + p * kPR, 0, 0);
+                S[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i] + (pb + p) * kPR, 0, 0);
         };
         auto lstore = [&](const Stg& S, uint8_t* buf) {
 #pragma unroll
@@ -377,7 +386,7 @@ void gemm_kernel(GemmArgs a) {
             };
             auto wl = [&](Stg& S, uint8_t* buf, const __amdgpu_buffer_rsrc_t& r, int pl, int w) {
                 *reinterpret_cast<v4i*>(&buf[wr + w * C::kNW * 8 * kPR]) = S[w];
-                S[w] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[w] + pl * kPR, 0, 0);
+                S[w] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[w] + (pb + pl) * kPR, 0, 0);
             };
             for (; p + 3 < KP; ++p) {
                 const int c = p & 1, n = c ^ 1;
@@ -427,6 +436,55 @@ void gemm_kernel(GemmArgs a) {
             if (p + 3 < KP) gload(rA, p + 3, SA);
         }
         __syncthreads();
+        if (BM == kSplitTile && a.ksplit > 1) {
+            // Split K in two: both blocks of the tile store their exact int32
+            // partial tile, then arrive on the tile counter; the second to
+            // arrive adds the other's partial and finishes the tile, the
+            // first leaves.  Nobody waits for anybody.  The partials are
+            // stored and loaded with device-scope (coherent) accesses, and
+            // each wave's stores are acknowledged before its block arrives,
+            // so the second block reads complete data.  Integer sums: the
+            // result does not depend on the arrival order.
+            constexpr int kF = C::kFM * C::kFN;
+            constexpr int64_t kSlot = (int64_t)C::kNW * kF * 16 * kWave;  // int32 per partial
+            const int S = a.ksplit;
+            int32_t* const slots = a.part + (int64_t)tbid * S * kSlot;
+            int32_t* const mine = slots + split * kSlot;
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        __hip_atomic_store(&mine[((wave * kF + i * C::kFN + j) * 16 + e) * kWave + lane],
+                                           acc[i][j][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            __shared__ int second;
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(a.sync + tbid, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                second = old == S - 1;
+                // every block has arrived: clear the counter for the next call
+                if (old == S - 1)
+                    __hip_atomic_store(a.sync + tbid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (!second) return;
+            for (int t = 0; t < S; ++t) {
+                if (t == split) continue;
+                const int32_t* const other = slots + t * kSlot;
+#pragma unroll
+                for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[i][j][e] += __hip_atomic_load(
+                                &other[((wave * kF + i * C::kFN + j) * 16 + e) * kWave + lane],
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     } else if constexpr (STAGES == 2) {
         // ---- register-staged, double-buffered LDS ------------------------------------
         // Global loads run PF tiles ahead of the multiply, in PF register sets.
@@ -857,7 +915,7 @@ template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1>
 int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
-    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * kWave);
+    const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit), block(WM * WN * kWave);
     if (debug)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true>), grid, block, 0,
                            st, a);
@@ -948,10 +1006,12 @@ int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
 }  // namespace
 }  // namespace mixq
 
-extern "C" int mixq_gemm(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
-                         const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,
-                         int64_t ldy, int32_t* acc_debug, void* stream) {
-    using namespace mixq;
+namespace mixq {
+namespace {
+
+int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
+              const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,
+              int64_t ldy, int32_t* acc_debug, void* ws, size_t ws_bytes, void* stream) {
     if (!Xq || !s_x || !state || !w || !Y) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !w->wq || !w->s_w) return MIXQ_ERR_INVALID_ARG;
     if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < w->N) return MIXQ_ERR_INVALID_ARG;
@@ -962,7 +1022,7 @@ extern "C" int mixq_gemm(const int8_t* Xq, const float* s_x, const uint16_t* X_o
     if (!valid_k(w->K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (M > (1 << 30) || w->N > (1 << 30)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (((uintptr_t)Xq & 15u) || ((uintptr_t)w->wq & 15u) || ((uintptr_t)X_out & 15u) ||
-        ((uintptr_t)w->w_out & 15u))
+        ((uintptr_t)w->w_out & 15u) || ((uintptr_t)ws & 15u))
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     int rc = check_device_cached();
     if (rc != MIXQ_OK) return rc;
@@ -983,7 +1043,38 @@ extern "C" int mixq_gemm(const int8_t* Xq, const float* s_x, const uint16_t* X_o
     a.ldy = ldy;
     a.acc_debug = acc_debug;
     a.tiles_m = a.tiles_n = 0;
+    a.ksplit = 1;
+    a.sync = nullptr;
+    a.part = nullptr;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    const int f = forced_cfg();
+    const int S = ws && (f == kCfgAuto || f == kCfg128x128KP) &&
+                          pick_cfg(M, w->N, w->K, w->bits) == kCfg128x128KP
+                      ? split_plan(M, w->N, w->K, w->bits, device_cu_count())
+                      : 1;
+    if (S > 1 && (int64_t)ws_bytes >= split_workspace_bytes(M, w->N, S)) {
+        a.ksplit = S;
+        a.sync = static_cast<int32_t*>(ws);
+        a.part = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + kSplitSyncBytes);
+        return launch_cfg<128, 128, 2, 2, 8, 4, 5>(a, acc_debug != nullptr, st);
+    }
     return w->bits == 8 ? launch_w8(a, acc_debug != nullptr, st)
                         : launch_w4(a, acc_debug != nullptr, st);
+}
+
+}  // namespace
+}  // namespace mixq
+
+extern "C" int mixq_gemm(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
+                         const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,
+                         int64_t ldy, int32_t* acc_debug, void* stream) {
+    return mixq::gemm_impl(Xq, s_x, X_out, state, w, M, Y, ldy, acc_debug, nullptr, 0, stream);
+}
+
+extern "C" int mixq_gemm_ws(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
+                            const mixq_act_state* state, const mixq_weight* w, int64_t M,
+                            float* Y, int64_t ldy, int32_t* acc_debug, void* ws, size_t ws_bytes,
+                            void* stream) {
+    return mixq::gemm_impl(Xq, s_x, X_out, state, w, M, Y, ldy, acc_debug, ws, ws_bytes, stream);
 }

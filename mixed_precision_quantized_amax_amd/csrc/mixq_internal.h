@@ -14,6 +14,28 @@ constexpr int kWave = 64;
 
 // ---- host side -------------------------------------------------------------
 int check_device_cached();  // MIXQ_OK / MIXQ_ERR_NO_DEVICE / MIXQ_ERR_UNSUPPORTED_DEVICE
+int device_cu_count();      // compute units of the current device (after the check)
+
+// Split-K plan of the thin-product GEMM (128x128 K-pair tiles): K is split
+// in two when the product has fewer tiles than the device has compute units
+// (INT8 weights, whole 128-byte K pairs in each half).  The kernel handles
+// any split count S (the last of S blocks to arrive reduces).
+constexpr int kSplitTile = 128;
+constexpr int64_t kSplitSyncBytes = 4096;                          // tile counters
+constexpr int64_t kSplitSlotBytes = (int64_t)kSplitTile * kSplitTile * 4;  // int32 partial tile
+inline int64_t split_tiles(int64_t M, int64_t N) {
+    return ((M + kSplitTile - 1) / kSplitTile) * ((N + kSplitTile - 1) / kSplitTile);
+}
+inline int split_plan(int64_t M, int64_t N, int64_t K, int bits, int cus) {
+    if (bits != 8 || K % 256 != 0 || M <= 0 || N <= 0) return 1;
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 192) return 1;  // the 256x256 path
+    const int64_t tiles = split_tiles(M, N);
+    if (tiles >= cus || tiles > kSplitSyncBytes / 4) return 1;
+    return 2;  // (four-way splits measured slower: the last block reads three partials)
+}
+inline int64_t split_workspace_bytes(int64_t M, int64_t N, int S) {
+    return kSplitSyncBytes + split_tiles(M, N) * S * kSplitSlotBytes;
+}
 
 inline bool valid_k(int64_t K) { return K > 0 && K % MIXQ_K_MULTIPLE == 0 && K <= MIXQ_K_MAX; }
 

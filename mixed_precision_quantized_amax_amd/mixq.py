@@ -75,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.mixq_gemm.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
                                 P, I64, P, P]
         L.mixq_gemm.restype = ctypes.c_int
+        L.mixq_gemm_ws.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
+                                   P, I64, P, P, ctypes.c_size_t, P]
+        L.mixq_gemm_ws.restype = ctypes.c_int
+        L.mixq_gemm_workspace_bytes.argtypes = [I64, I64, I64, I32]
+        L.mixq_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.mixq_status_string.argtypes = [ctypes.c_int]
         L.mixq_status_string.restype = ctypes.c_char_p
         L.mixq_check_device.argtypes = []
@@ -194,14 +199,34 @@ def pack_weight(W: torch.Tensor, state: OutlierState, pw: PackedWeight,
     _check("mixq_pack_weight", rc)
 
 
+def gemm_workspace_bytes(M: int, N: int, K: int, bits: int) -> int:
+    return int(lib().mixq_gemm_workspace_bytes(M, N, K, bits))
+
+
+def gemm_workspace(M: int, N: int, K: int, bits: int, device=None) -> torch.Tensor | None:
+    """Zero-filled split-K workspace for ``gemm(..., ws=...)``, or None when
+    the product is not split (then no workspace is needed)."""
+    n = gemm_workspace_bytes(M, N, K, bits)
+    if n == 0:
+        return None
+    return torch.zeros((n + 15) // 16 * 4, dtype=torch.int32, device=device or "cuda")
+
+
 def gemm(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None, state: OutlierState,
-         pw: PackedWeight, Y: torch.Tensor, acc_debug: torch.Tensor | None = None) -> None:
+         pw: PackedWeight, Y: torch.Tensor, acc_debug: torch.Tensor | None = None,
+         ws: torch.Tensor | None = None) -> None:
     M = Xq.shape[0]
     st = state.c()
     w = pw.c()
-    rc = lib().mixq_gemm(_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(st), ctypes.byref(w), M,
-                         _ptr(Y), Y.stride(0), _ptr(acc_debug), _stream(Y.device))
-    _check("mixq_gemm", rc)
+    if ws is None:
+        rc = lib().mixq_gemm(_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(st), ctypes.byref(w),
+                             M, _ptr(Y), Y.stride(0), _ptr(acc_debug), _stream(Y.device))
+        _check("mixq_gemm", rc)
+    else:
+        rc = lib().mixq_gemm_ws(_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(st),
+                                ctypes.byref(w), M, _ptr(Y), Y.stride(0), _ptr(acc_debug),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(Y.device))
+        _check("mixq_gemm_ws", rc)
 
 
 class LayerStep:
@@ -212,12 +237,13 @@ class LayerStep:
     def __init__(self, X: torch.Tensor, tau: float, state: OutlierState, W: torch.Tensor,
                  pw: PackedWeight, Xq: torch.Tensor, s_x: torch.Tensor,
                  X_out: torch.Tensor | None, Y: torch.Tensor,
-                 acc_debug: torch.Tensor | None = None, stream=None):
+                 acc_debug: torch.Tensor | None = None, stream=None,
+                 ws: torch.Tensor | None = None):
         L = lib()
         dev = X.device
         s = ctypes.c_void_p(stream if stream is not None
                             else torch.cuda.current_stream(dev).cuda_stream)
-        self._keep = (X, W, Xq, s_x, X_out, Y, acc_debug, state, pw)
+        self._keep = (X, W, Xq, s_x, X_out, Y, acc_debug, state, pw, ws)
         self._st = state.c()
         self._w = pw.c()
         M = X.shape[0]
@@ -230,7 +256,11 @@ class LayerStep:
               ctypes.byref(self._w), s)),
             ("mixq_gemm", L.mixq_gemm,
              (_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(self._st), ctypes.byref(self._w),
-              M, _ptr(Y), Y.stride(0), _ptr(acc_debug), s)),
+              M, _ptr(Y), Y.stride(0), _ptr(acc_debug), s)) if ws is None else
+            ("mixq_gemm_ws", L.mixq_gemm_ws,
+             (_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(self._st), ctypes.byref(self._w),
+              M, _ptr(Y), Y.stride(0), _ptr(acc_debug), _ptr(ws),
+              ws.numel() * ws.element_size(), s)),
         ]
 
     def act(self):
@@ -295,18 +325,19 @@ class MixQLinear:
             ld = outlier_ld(self.k_cap)
             self._bufs[M] = (torch.empty(M, self.K, dtype=torch.int8, device=dev),
                              torch.empty(M, dtype=torch.float32, device=dev),
-                             torch.zeros(max(M * ld, 1), dtype=torch.float16, device=dev))
+                             torch.zeros(max(M * ld, 1), dtype=torch.float16, device=dev),
+                             gemm_workspace(M, self.N, self.K, self.bits, dev))
         return self._bufs[M]
 
     def forward(self, X: torch.Tensor, Y: torch.Tensor | None = None,
                 acc_debug: torch.Tensor | None = None) -> torch.Tensor:
         M = X.shape[0]
-        Xq, s_x, X_out = self.buffers(M)
+        Xq, s_x, X_out, ws = self.buffers(M)
         if Y is None:
             Y = torch.empty(M, self.N, dtype=torch.float32, device=X.device)
         quantize_act(X, self.tau, self.state, Xq, s_x, X_out)
         pack_weight(self.W, self.state, self.pw, PACK_OUTLIER_COLS)
-        gemm(Xq, s_x, X_out, self.state, self.pw, Y, acc_debug)
+        gemm(Xq, s_x, X_out, self.state, self.pw, Y, acc_debug, ws)
         return Y
 
     __call__ = forward

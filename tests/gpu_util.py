@@ -32,8 +32,10 @@ def set_from_bitmap(bitmap: np.ndarray, K: int) -> np.ndarray:
 class GpuLayer:
     """One layer on the GPU: state, packed weight and output buffers."""
 
-    def __init__(self, W: np.ndarray, bits: int, tau: float, k_cap: int, M: int):
+    def __init__(self, W: np.ndarray, bits: int, tau: float, k_cap: int, M: int,
+                 split: bool = True):
         self.N, self.K = W.shape
+        self.split = split  # pass a split-K workspace to the GEMM when the shape uses one
         self.bits, self.tau, self.k_cap = bits, tau, k_cap
         self.Wd = to_dev(W.view(np.float16))
         self.state = mixq.OutlierState.create(self.K, k_cap)
@@ -49,6 +51,7 @@ class GpuLayer:
         self.X_out = torch.full((max(M * self.ld, 1),), float("nan"), dtype=torch.float16,
                                 device="cuda") if self.ld else None
         self.Y = torch.full((M, self.N), float("nan"), dtype=torch.float32, device="cuda")
+        self.ws = mixq.gemm_workspace(M, self.N, self.K, self.bits) if self.split else None
 
     def quantize(self, X: np.ndarray):
         Xd = to_dev(X.view(np.float16))
@@ -58,7 +61,7 @@ class GpuLayer:
         mixq.pack_weight(self.Wd, self.state, self.pw, mixq.PACK_OUTLIER_COLS)
 
     def gemm(self, acc_debug=None):
-        mixq.gemm(self.Xq, self.s_x, self.X_out, self.state, self.pw, self.Y, acc_debug)
+        mixq.gemm(self.Xq, self.s_x, self.X_out, self.state, self.pw, self.Y, acc_debug, self.ws)
 
     def step(self, X, acc=False):
         self.quantize(X)

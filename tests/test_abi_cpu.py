@@ -115,3 +115,35 @@ def test_gemm_validation(args, code):
                               ctypes.byref(w), args.get("M", 4), ctypes.c_void_p(args.get("Y", 0x50000)),
                               args.get("ldy", 16), None, None)
     assert rc == code
+
+
+def test_gemm_workspace_bytes():
+    """Split-K plan (256 compute units): only thin INT8 products with K a
+    multiple of 256; 4 KiB of counters plus two 64 KiB partial tiles per
+    128 x 128 output tile."""
+    L = mixq.lib()
+    slot = 128 * 128 * 4
+    assert L.mixq_gemm_workspace_bytes(2048, 8192, 8192, 8) == 0      # 256x256 path
+    assert L.mixq_gemm_workspace_bytes(256, 8192, 8192, 8) == 4096 + 128 * 2 * slot
+    assert L.mixq_gemm_workspace_bytes(512, 11008, 4096, 8) == 0      # 344 tiles >= 256
+    assert L.mixq_gemm_workspace_bytes(512, 28672, 8192, 8) == 0      # 256x256 path
+    assert L.mixq_gemm_workspace_bytes(64, 1024, 4096, 8) == 4096 + 8 * 2 * slot
+    assert L.mixq_gemm_workspace_bytes(256, 8192, 8192, 4) == 0       # INT4: no split
+    assert L.mixq_gemm_workspace_bytes(256, 8192, 8192 - 128, 8) == 0  # K % 256 != 0
+    assert L.mixq_gemm_workspace_bytes(0, 8192, 8192, 8) == 0
+
+
+def test_gemm_ws_validation():
+    w = _weight()
+    st = _state()
+    f = mixq.lib().mixq_gemm_ws
+    args = [ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+            ctypes.byref(st), ctypes.byref(w), 4, ctypes.c_void_p(0x50000), 16, None]
+    assert f(*args, ctypes.c_void_p(0x60008), 1 << 20, None) == 2    # misaligned workspace
+    bad = list(args)
+    bad[6] = None
+    assert f(*bad, ctypes.c_void_p(0x60000), 1 << 20, None) == 1     # Y null
+    import torch
+    if not torch.cuda.is_available():
+        assert f(*args, ctypes.c_void_p(0x60000), 1 << 20, None) == 4
+        assert f(*args, None, 0, None) == 4

@@ -37,7 +37,7 @@ def run_pair(inputs, W, bits, tau, k_cap):
     graphed = GpuLayer(W, bits, tau, k_cap, M)
     Xd = torch.empty(M, K, dtype=torch.float16, device="cuda")
     lg = mixq.LayerGraph(Xd, tau, graphed.state, graphed.Wd, graphed.pw, graphed.Xq,
-                         graphed.s_x, graphed.X_out, graphed.Y)
+                         graphed.s_x, graphed.X_out, graphed.Y, ws=graphed.ws)
     flags = []
     for t, X in enumerate(inputs):
         say(f"[graph] replay {t} M={M} K={K} N={W.shape[0]}")

@@ -265,3 +265,25 @@ def test_thresholds_between_fp16_values(orc, tau):
     X = X.astype(np.float16)
     W = (rng.standard_normal((72, 256)) * 0.05).astype(np.float16)
     full_compare(orc, X, W, 8, tau, 256, tag=f"tau={tau}")
+
+
+@pytest.mark.parametrize("M,K,N,n_out", [(200, 1024, 512, 5), (256, 2048, 256, 3), (300, 1024, 700, 9),
+                                         (64, 4096, 1024, 0), (513, 2048, 300, 4), (100, 256, 384, 2)])
+def test_split_k(orc, M, K, N, n_out):
+    """Thin products split K over two blocks per 128 x 128 tile, which meet
+    through int32 partial tiles in the workspace: everything equals the
+    oracle, Y equals the unsplit kernel's bit for bit, and the tile counters
+    are left at zero for the next call."""
+    assert mixq.gemm_workspace_bytes(M, N, K, 8) > 0, "shape expected to split"
+    X, W, _ = workloads.random_case(seed=M + K + N, M=M, K=K, N=N, n_out=n_out)
+    g, _ = full_compare(orc, X, W, 8, 6.0, 64, tag=f"splitk M={M} K={K} N={N}")
+    assert g.ws is not None
+    h = GpuLayer(W, 8, 6.0, 64, M, split=False)
+    h.step(X)
+    yh = h.Y.cpu().numpy().view(np.uint32)
+    assert np.array_equal(g.Y.cpu().numpy().view(np.uint32), yh)
+    for _ in range(3):  # repeated calls reuse the counters
+        g.gemm()
+    torch.cuda.synchronize()
+    assert np.array_equal(g.Y.cpu().numpy().view(np.uint32), yh)
+    assert int(g.ws[:1024].abs().sum().cpu()) == 0, "tile counters not cleared"
