@@ -113,6 +113,11 @@ class Oracle:
         n = self.lib.orc_outlier_list(_ptr(s), s.size, _ptr(idx))
         return idx[:n].copy()
 
+    # -- the operation before the layer ------------------------------------------
+    def rmsnorm(self, H, gamma, eps: float):
+        """Returns (X fp16 [M, K], rstd fp32 [M]); see ``rmsnorm`` below."""
+        return rmsnorm(H, gamma, eps)
+
     # -- quantization ----------------------------------------------------------
     def quantize_act(self, X, in_set: np.ndarray, ldo: int):
         Xb = _bits(X)
@@ -181,6 +186,52 @@ class Oracle:
         if rc != 0:
             raise OverflowError("integer accumulator exceeds int32")
         return acc, Y
+
+
+def rmsnorm(H, gamma, eps: float):
+    """RMSNorm of fp16 token rows, the operation that precedes a LLaMA linear
+    layer and into which the MixQ article (section "MixQ的解决方案", the
+    paragraph after the amax test) says the amax can be fused.
+
+    The pages do not define the normalisation; the reading taken here is the
+    common LLaMA one, with every rounding stated so that the result is unique:
+
+      S      = sum_k h_k^2, exact (each fp16 h is an integer multiple of 2^-24,
+               so |h| * 2^24 is an integer below 2^40 and S * 2^48 is an
+               integer, summed here with Python integers), rounded once to
+               binary64;
+      ms     = fp32(S / K)              (binary64 division, then RNE to fp32)
+      rstd   = 1 / sqrt(ms + eps)       (three binary32 operations; a zero
+                                         denominator, i.e. an all-zero row
+                                         with eps = 0, gives rstd = 0)
+      n      = fp16(fp32(h * rstd))     (binary32 product, RNE to fp16)
+      x      = fp16(n * gamma)          (the product of two fp16 values is exact
+                                         in binary32; one RNE to fp16)
+
+    H: fp16 [M, K] (or its bit pattern); gamma: fp16 [K]; eps >= 0.
+    """
+    Hh = H.view(np.float16) if H.dtype == np.uint16 else np.asarray(H, np.float16)
+    g = gamma.view(np.float16) if gamma.dtype == np.uint16 else np.asarray(gamma, np.float16)
+    M, K = Hh.shape
+    assert g.shape == (K,) and K <= 1 << 15
+    v = (np.abs(Hh.astype(np.float64)) * 2.0 ** 24).astype(np.int64)  # exact integers < 2^40
+    vh, vl = v >> 20, v & ((1 << 20) - 1)
+    # v^2 = vh^2 2^40 + 2 vh vl 2^20 + vl^2; each partial sum stays below 2^55
+    A = (vh * vh).sum(axis=1)
+    B = (vh * vl).sum(axis=1)
+    C = (vl * vl).sum(axis=1)
+    rstd = np.zeros(M, np.float32)
+    e32 = np.float32(eps)
+    for m in range(M):
+        s_units = (int(A[m]) << 40) + (int(B[m]) << 21) + int(C[m])  # S * 2^48, exact
+        S = float(s_units) * 2.0 ** -48  # int -> float rounds to nearest even; the
+        #                                   power-of-two factor is exact
+        ms = np.float32(S / K)
+        t = ms + e32
+        rstd[m] = np.float32(0.0) if t == 0 else np.float32(1.0) / np.sqrt(t)
+    n = (Hh.astype(np.float32) * rstd[:, None]).astype(np.float16)
+    X = (n.astype(np.float32) * g.astype(np.float32)).astype(np.float16)
+    return X, rstd
 
 
 @dataclass

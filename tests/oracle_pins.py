@@ -436,9 +436,182 @@ def pin_sampled_output(o):
     assert np.abs(Y - want).max() <= 1e-12 * np.abs(want).max()
 
 
+# ----------------------------------------------------------------------------
+# the RMSNorm before the layer (fused with the amax pass on the GPU)
+# ----------------------------------------------------------------------------
+def _norm_rows(seed, M, K, wide=True):
+    """fp16 rows; ``wide`` mixes values near the fp16 maximum, subnormals and
+    N(0,1) draws in one row, where a rounded running sum of squares would lose
+    the small terms."""
+    r = _rng(seed, M, K, 77)
+    H = r.standard_normal((M, K))
+    if wide:
+        kind = r.integers(0, 4, (M, K))
+        H = np.where(kind == 0, r.uniform(1000, 60000, (M, K)) * r.choice([-1, 1], (M, K)), H)
+        H = np.where(kind == 1, r.integers(1, 1024, (M, K)) * 2.0 ** -24, H)
+    return H.astype(np.float16)
+
+
+def _gamma(seed, K):
+    return (1.0 + 0.25 * _rng(seed, K, 78).standard_normal(K)).astype(np.float16)
+
+
+def pin_rmsnorm_fsum(o):
+    """rstd against a second route to the exactly rounded sum of squares:
+    math.fsum returns the correctly rounded sum of the (exact) binary64
+    squares, whatever their order."""
+    import math
+    for seed, (M, K) in enumerate([(5, 64), (4, 256), (3, 1024), (2, 4096)]):
+        for wide in (False, True):
+            H = _norm_rows(seed, M, K, wide)
+            X, rstd = o.rmsnorm(H, _gamma(seed, K), 1e-5)
+            for m in range(M):
+                S = math.fsum(float(h) ** 2 for h in H[m].astype(np.float64))
+                ms = np.float32(S / K)
+                want = np.float32(1.0) / np.sqrt(ms + np.float32(1e-5))
+                assert rstd[m].view(np.uint32) == want.view(np.uint32), (seed, wide, m)
+
+
+def pin_rmsnorm_bound(o):
+    """Each x within the rounding bound of h * gamma / sqrt(mean(h^2) + eps)
+    computed in FP64: two fp16 roundings (2^-11 each), a few binary32 ones,
+    plus fp16 subnormal spacing."""
+    for seed, (M, K) in enumerate([(6, 64), (4, 512), (2, 2048)]):
+        for wide in (False, True):
+            H = _norm_rows(seed + 10, M, K, wide)
+            g = _gamma(seed, K)
+            X, _ = o.rmsnorm(H, g, 1e-5)
+            h = H.astype(np.float64)
+            true = h / np.sqrt((h * h).mean(axis=1, keepdims=True) + float(np.float32(1e-5)))
+            true *= g.astype(np.float64)
+            err = np.abs(X.astype(np.float64) - true)
+            tol = np.abs(true) * (2.0 ** -10 + 2.0 ** -18) + 2.0 ** -24 * (np.abs(g) + 1.0)
+            assert (err <= tol).all(), (seed, wide, (err / tol).max())
+
+
+def pin_rmsnorm_invariants(o):
+    """With eps = 0: scaling a row by 2^p leaves x unchanged (every rounding
+    commutes with binary scaling); negating it negates x; permuting channels
+    of H and gamma together permutes x (the sum of squares is exact, so its
+    order does not matter -- also on the wide rows)."""
+    for seed, (M, K) in enumerate([(4, 64), (3, 512), (2, 2048)]):
+        H = _norm_rows(seed + 20, M, K, wide=False).astype(np.float64)
+        H = (np.sign(H) * np.maximum(np.abs(H), 2.0 ** -8)).astype(np.float16)  # no subnormals
+        g = _gamma(seed, K)
+        X, rstd = o.rmsnorm(H, g, 0.0)
+        for p in (-3, 2):
+            Hs = (H.astype(np.float64) * 2.0 ** p).astype(np.float16)
+            assert (Hs.astype(np.float64) == H.astype(np.float64) * 2.0 ** p).all()
+            Xs, rs = o.rmsnorm(Hs, g, 0.0)
+            assert (Xs.view(np.uint16) == X.view(np.uint16)).all()
+            assert (rs.astype(np.float64) == rstd.astype(np.float64) * 2.0 ** -p).all()
+        Xn, rn = o.rmsnorm(-H, g, 0.0)
+        assert (Xn.astype(np.float64) == -X.astype(np.float64)).all() and (rn == rstd).all()
+        for wide in (False, True):
+            Hw = _norm_rows(seed + 30, M, K, wide)
+            perm = _rng(seed, 79).permutation(K)
+            A, ra = o.rmsnorm(Hw, g, 1e-5)
+            B, rb = o.rmsnorm(np.ascontiguousarray(Hw[:, perm]), np.ascontiguousarray(g[perm]),
+                              1e-5)
+            assert (ra.view(np.uint32) == rb.view(np.uint32)).all()
+            assert (B.view(np.uint16) == A[:, perm].view(np.uint16)).all()
+
+
+def _round_fmt(q, p, emin):
+    """Nearest binary floating-point value to the rational q (ties to even),
+    p significand bits, minimum normal exponent emin; no overflow."""
+    q = Fraction(q)
+    if q == 0:
+        return Fraction(0)
+    sgn, a = (-1 if q < 0 else 1), abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - (p - 1))
+    k = a / ulp
+    fl = k.numerator // k.denominator
+    rem = k - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * ulp
+
+
+def _r64(q):
+    return _round_fmt(q, 53, -1022)
+
+
+def _r32(q):
+    return _round_fmt(q, 24, -126)
+
+
+def _r16(q):
+    return _round_fmt(q, 11, -14)
+
+
+def _sqrt32(t):
+    """Correctly rounded binary32 square root of the binary32 value t >= 0,
+    decided by exact comparisons of t with squared midpoints."""
+    t = Fraction(t)
+    if t == 0:
+        return Fraction(0)
+    y = Fraction(float(np.sqrt(np.float32(float(t)))))  # a guess; checked below
+    while True:
+        up = Fraction(float(np.nextafter(np.float32(float(y)), np.float32(np.inf))))
+        dn = Fraction(float(np.nextafter(np.float32(float(y)), np.float32(0))))
+        if ((y + up) / 2) ** 2 < t:
+            y = up
+        elif ((y + dn) / 2) ** 2 > t:
+            y = dn
+        else:
+            # ties cannot occur: a midpoint squared has more bits than t
+            return y
+
+
+def pin_rmsnorm_exact_rationals(o):
+    """Every step of the normalisation redone with exact rationals and the
+    IEEE round-to-nearest-even rule written out: the exact sum of squares
+    rounded to binary64, the division by K, the binary32 mean square, eps,
+    square root and reciprocal, the binary32 product with h rounded to fp16,
+    then the product with gamma rounded to fp16."""
+    for seed, (M, K, eps) in enumerate([(3, 64, 1e-5), (2, 64, 0.0), (2, 128, 1e-6)]):
+        H = _norm_rows(seed + 40, M, K, wide=(seed != 1))
+        g = _gamma(seed + 40, K)
+        X, rstd = o.rmsnorm(H, g, eps)
+        e32 = Fraction(float(np.float32(eps)))
+        for m in range(M):
+            hs = [Fraction(float(h)) for h in H[m].astype(np.float64)]
+            S = _r64(sum(h * h for h in hs))
+            ms = _r32(_r64(S / K))
+            t = _r32(ms + e32)
+            r = Fraction(0) if t == 0 else _r32(1 / _sqrt32(t))
+            assert Fraction(float(rstd[m])) == r, (seed, m)
+            for k in range(K):
+                n = _r16(_r32(hs[k] * r))
+                x = _r16(n * Fraction(float(g[k])))
+                assert Fraction(float(X[m, k])) == x, (seed, m, k)
+
+
+def pin_rmsnorm_closed_form(o):
+    """A row of one power of two c (any sign) has mean square c^2 exactly,
+    so with eps = 0 rstd = 1/|c| and x = sign(c) * gamma; an all-zero row
+    gives rstd = 0 and x = 0."""
+    K = 128
+    g = _gamma(3, K)
+    rows = [np.full(K, c) for c in (2.0 ** -20, -0.5, 1.0, 64.0, -1024.0)]
+    H = np.array(rows + [np.zeros(K)]).astype(np.float16)
+    X, rstd = o.rmsnorm(H, g, 0.0)
+    for m, c in enumerate((2.0 ** -20, -0.5, 1.0, 64.0, -1024.0)):
+        assert float(rstd[m]) == 1.0 / abs(c)
+        assert (X[m].astype(np.float64) == np.sign(c) * g.astype(np.float64)).all()
+    assert rstd[-1] == 0 and not X[-1].astype(np.float64).any()
+
+
 ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode,
             pin_set_bruteforce, pin_quant_error_bound, pin_nearest_code, pin_weight_bound,
             pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
             pin_output_vs_truth_bound, pin_no_outlier_textbook, pin_all_outlier,
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
-            pin_decode_sequence, pin_sampled_output]
+            pin_decode_sequence, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
+            pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals]

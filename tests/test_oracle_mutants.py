@@ -88,3 +88,51 @@ def test_mutant_is_caught(workdir, name, old, new, occ):
         except (AssertionError, OverflowError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught mutant {name}"
+
+
+# Mistakes planted in the oracle's RMSNorm (Python source of
+# ``oracle.mixq_oracle.rmsnorm``): (name, text to replace, replacement)
+RMS_MUTANTS = [
+    ("norm_fp32_running_sum", "S = float(s_units) * 2.0 ** -48",
+     "S = float((Hh[m].astype(np.float32) ** 2).sum(dtype=np.float32))"),
+    ("norm_limb_shift", "(int(B[m]) << 21)", "(int(B[m]) << 20)"),
+    ("norm_mean_over_k_plus_1", "ms = np.float32(S / K)", "ms = np.float32(S / (K + 1))"),
+    ("norm_eps_outside_sqrt", "np.float32(1.0) / np.sqrt(t)",
+     "np.float32(1.0) / (np.sqrt(ms) + e32)"),
+    ("norm_no_sqrt", "np.float32(1.0) / np.sqrt(t)", "np.float32(1.0) / t"),
+    ("norm_zero_row_rule", "np.float32(0.0) if t == 0", "np.float32(1.0) if t == 0"),
+    ("norm_single_rounding", "n = (Hh.astype(np.float32) * rstd[:, None]).astype(np.float16)",
+     "n = Hh.astype(np.float32) * rstd[:, None]"),
+    ("norm_no_gamma", "X = (n.astype(np.float32) * g.astype(np.float32)).astype(np.float16)",
+     "X = n.astype(np.float16)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", RMS_MUTANTS, ids=[m[0] for m in RMS_MUTANTS])
+def test_rmsnorm_mutant_is_caught(name, old, new):
+    import inspect
+    import textwrap
+
+    import numpy as np
+
+    from oracle import mixq_oracle
+
+    src = textwrap.dedent(inspect.getsource(mixq_oracle.rmsnorm))
+    assert src.count(old) == 1, f"mutation site not found: {old!r}"
+    ns = {"np": np}
+    exec(compile(src.replace(old, new), f"<{name}>", "exec"), ns)
+
+    class Mutant(Oracle):
+        def rmsnorm(self, H, gamma, eps):
+            return ns["rmsnorm"](H, gamma, eps)
+
+    o = Mutant()
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        if "rmsnorm" not in pin.__name__:
+            continue
+        try:
+            pin(o)
+        except (AssertionError, OverflowError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
