@@ -165,6 +165,76 @@ def run_gpu(wl, steps: int, warmup: int):
                 count=count, flag=flag, copies=copies)
 
 
+def norm_act_bytes(wl, k: int) -> int:
+    """Bytes the fused RMSNorm + activation pass must move at least once:
+    H in, gamma, Xq out, s_x and rstd, the padded outlier matrix."""
+    kp = (k + 31) // 32 * 32
+    return 3 * wl.M * wl.K + 2 * wl.K + 8 * wl.M + 2 * wl.M * kp
+
+
+def run_fused_norm(wl, steps: int, warmup: int, eps: float = 1e-5):
+    """The activation side with the RMSNorm before the layer fused in
+    (mixq_rmsnorm_quantize_act), against the same work unfused: torch's
+    rms_norm writing the normalised fp16 tokens, then mixq_quantize_act.
+    Steady state: the outlier set is detected by the first call and cached."""
+    import torch
+    import torch.nn.functional as F
+    from mixed_precision_quantized_amax_amd import mixq, workloads
+
+    dev = torch.device("cuda", 0)
+    H0 = torch.from_numpy(workloads.make_activation(wl)).to(dev)
+    gamma = torch.from_numpy(workloads.make_norm_gamma(wl)).to(dev)
+    k_cap = 256
+    copies = int(min(16, max(2, math.ceil(CACHE_DEFEAT_BYTES / (3 * wl.M * wl.K)))))
+    ld = mixq.outlier_ld(k_cap)
+    Hs = [H0.clone() for _ in range(copies)]
+    Xq = [torch.empty(wl.M, wl.K, dtype=torch.int8, device=dev) for _ in range(copies)]
+    sx = [torch.empty(wl.M, dtype=torch.float32, device=dev) for _ in range(copies)]
+    Xo = [torch.zeros(wl.M * ld, dtype=torch.float16, device=dev) for _ in range(copies)]
+    rs = [torch.empty(wl.M, dtype=torch.float32, device=dev) for _ in range(copies)]
+    st_f = mixq.OutlierState.create(wl.K, k_cap, dev)
+    st_u = mixq.OutlierState.create(wl.K, k_cap, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused(i):
+        c = i % copies
+        mixq.rmsnorm_quantize_act(Hs[c], gamma, eps, wl.tau, st_f, Xq[c], sx[c], Xo[c], rs[c])
+
+    def unfused(i):
+        c = i % copies
+        Xn = F.rms_norm(Hs[c], (wl.K,), gamma, eps)
+        mixq.quantize_act(Xn, wl.tau, st_u, Xq[c], sx[c], Xo[c])
+
+    for i in range(warmup):
+        fused(i)
+        unfused(i)
+    torch.cuda.synchronize()
+    count = int(st_f.count.cpu()[0])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    flag = int(st_f.flag.cpu()[0])
+    us = res["fused"] * 1e3
+    gbs = norm_act_bytes(wl, count) / (res["fused"] / 1e3) / 1e9
+    log(f"[bench] fused rmsnorm+act {us:.2f} us ({gbs:.0f} GB/s), unfused "
+        f"{res['unfused'] * 1e3:.2f} us; set {count}, last flag {flag}")
+    return {"us": round(us, 2), "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": norm_act_bytes(wl, count), "outlier_channels": count,
+            "last_flag": flag, "eps": eps,
+            "unfused_us": round(res["unfused"] * 1e3, 2),
+            "unfused": "torch rms_norm (fp16 out) + mixq_quantize_act",
+            "kernels": "gate_quant_kernel (RMSNorm prologue) + requant_kernel (no-op unless "
+                       "the gate fires)"}
+
+
 def run_decode_sequence(wl, repeats: int = 3):
     """The outlier-locality decode sequence: every step runs the whole layer on
     a new batch, the cached set carrying over; the set is re-detected only on
@@ -323,6 +393,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
     }
+    out["fused_rmsnorm_act"] = run_fused_norm(wl, args.steps, min(args.warmup, 50))
     if args.all:
         others = {}
         for name in ("llama7b_up", "llama70b_up", "prefill_w4"):

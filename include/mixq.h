@@ -69,6 +69,7 @@ enum {
 #define MIXQ_K_MULTIPLE 64           /* K must be a multiple of this            */
 #define MIXQ_K_MAX 65536             /* largest supported K                     */
 #define MIXQ_OUTLIER_ALIGN 32        /* outlier matrices padded to this many k  */
+#define MIXQ_NORM_K_MAX 32768        /* largest K of mixq_rmsnorm_quantize_act  */
 
 /* flag bits written by mixq_quantize_act into *state->flag */
 #define MIXQ_FLAG_FIRED 1            /* gate fired, set grew                    */
@@ -162,6 +163,39 @@ size_t mixq_packed_weight_bytes(int64_t N, int64_t K, int32_t bits);
 int mixq_quantize_act(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, float threshold,
                       const mixq_act_state *state, int8_t *Xq, float *s_x, uint16_t *X_out,
                       void *stream);
+
+/*
+ * mixq_rmsnorm_quantize_act -- mixq_quantize_act applied to the RMS-normalised
+ * tokens, in the same pass over memory: the amax that the quantization needs
+ * is fused into the operation before the layer (MixQ article, "MixQ的解决方案",
+ * the paragraph after the amax test).  For a LLaMA linear that operation is
+ * RMSNorm; the normalised X is never written to memory.
+ *
+ * For each token m, with every rounding fixed so that the result is unique:
+ *   S = sum_k H[m,k]^2 exactly, rounded once to binary64;
+ *   ms = fp32(S / K);  rstd[m] = 1 / sqrt(ms + eps) in binary32 (0 when
+ *   ms + eps == 0, i.e. an all-zero token with eps = 0);
+ *   X[m,k] = fp16(fp16(H[m,k] * rstd[m]) * gamma[k])  (binary32 product
+ *   rounded to fp16, then the fp16 product rounded to fp16);
+ * then everything mixq_quantize_act does, on X: gate, detection, Xq, s_x and
+ * X_out (which holds normalised values).
+ *
+ *   H        fp16 [M, ldh] device, row-major, read-only; finite, and every
+ *            normalised value must be finite in fp16
+ *   M, K     as mixq_quantize_act, and K <= MIXQ_NORM_K_MAX
+ *   ldh      row stride of H in elements, >= K
+ *   gamma    fp16 [K] device, 16-byte aligned, read-only
+ *   eps      finite, >= 0
+ *   threshold, state, Xq, s_x, X_out   as mixq_quantize_act
+ *   rstd     fp32 [M] device, written
+ * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for a null gamma or
+ *         rstd or a bad eps; MIXQ_ERR_UNSUPPORTED_SHAPE also for K above
+ *         MIXQ_NORM_K_MAX or a misaligned gamma.
+ */
+int mixq_rmsnorm_quantize_act(const uint16_t *H, int64_t M, int64_t K, int64_t ldh,
+                              const uint16_t *gamma, float eps, float threshold,
+                              const mixq_act_state *state, int8_t *Xq, float *s_x,
+                              uint16_t *X_out, float *rstd, void *stream);
 
 /*
  * mixq_pack_weight -- per-output-channel symmetric quantization of W and the

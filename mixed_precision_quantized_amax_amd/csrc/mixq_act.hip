@@ -52,6 +52,10 @@ struct ActArgs {
     float* s_x;
     uint16_t* X_out;
     int32_t ld_out;
+    // RMSNorm prologue (gamma null: X is quantized as given)
+    const uint16_t* gamma;
+    float eps;
+    float* rstd;
 };
 
 // LDS table: for the 8 cached-channel bits of a chunk (8 halves = 4 dwords),
@@ -102,6 +106,84 @@ __device__ __forceinline__ uint32_t pack4(uint32_t u0, uint32_t u1, uint32_t u2,
     return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 
+// ---- RMSNorm prologue ------------------------------------------------------------
+// The token's sum of squares is kept exact as an unevaluated pair hi + lo of
+// doubles.  Every fp16 value is a multiple of 2^-24, so every square, partial
+// sum and rounding error below is a multiple of 2^-48, and a square is exact
+// in binary32 (22 significant bits, no underflow).  two_sum is Knuth's
+// error-free transform: hi + lo does not change.  lo, the running sum of the
+// rounding errors, is itself exact while |lo| < 2^5 (53 bits of 2^-48 steps):
+// with |h| < 2^16, K <= 2^15 and at most K/256 squares per lane, a lane's
+// partial stays below 2^39, so each of its errors is at most 2^-15 and their
+// sum below 2^-8; the 255 combines of lane and wave partials add at most
+// 2^-7 each.  So |lo| < 2, the pair is the exact sum, and fl(hi + lo) is that
+// sum rounded once to binary64 -- whatever the order of accumulation.
+__device__ __forceinline__ void two_sum(double& hi, double& lo, double b) {
+    const double s = hi + b;
+    const double bb = s - hi;
+    const double err = (hi - (s - bb)) + (b - bb);
+    lo += err;
+    hi = s;
+}
+
+__device__ __forceinline__ void pair_add(double& hi, double& lo, double hi2, double lo2) {
+    two_sum(hi, lo, hi2);
+    lo += lo2;
+}
+
+__device__ __forceinline__ void sumsq_chunk(const uint4& v, double& hi, double& lo) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float f = half_bits_to_float((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
+        two_sum(hi, lo, (double)(f * f));
+    }
+}
+
+// Butterfly over the wave; every lane ends with the same exact pair.
+__device__ __forceinline__ void wave_pair_sum(double& hi, double& lo) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const double h2 = __shfl_xor(hi, o, kWave);
+        const double l2 = __shfl_xor(lo, o, kWave);
+        pair_add(hi, lo, h2, l2);
+    }
+}
+
+// rstd = 1 / sqrt(fp32(S / K) + eps): the exact sum rounded to binary64, one
+// binary64 division, then binary32 add, square root and division (all
+// correctly rounded).  A zero denominator (all-zero token, eps = 0) gives 0.
+__device__ __forceinline__ float rstd_of(double hi, double lo, int K, float eps) {
+    const double S = hi + lo;
+    const float ms = (float)(S / (double)K);
+    const float t = ms + eps;
+    return t == 0.0f ? 0.0f : 1.0f / __builtin_sqrtf(t);
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// x = fp16(fp16(h * r) * gamma) for the two halves of a dword: the binary32
+// product rounded to fp16, then the fp16 product (exact in binary32) rounded.
+// The empty asm pins the binary32 products: without it the compiler may fold
+// product and narrowing into one mixed-precision fma (v_fma_mixlo_f16), which
+// rounds once instead of twice and so differs at rare ties.
+__device__ __forceinline__ uint32_t norm2(uint32_t hw, uint32_t gw, float r) {
+    float p0 = half_bits_to_float((uint16_t)hw) * r;
+    float p1 = half_bits_to_float((uint16_t)(hw >> 16)) * r;
+    asm volatile("" : "+v"(p0), "+v"(p1));
+    const half2v n = {(_Float16)p0, (_Float16)p1};
+    return __builtin_bit_cast(uint32_t, n * __builtin_bit_cast(half2v, gw));
+}
+
+__device__ __forceinline__ uint4 norm_chunk(const uint4& v, const uint4& g, float r) {
+    return make_uint4(norm2(v.x, g.x, r), norm2(v.y, g.y, r), norm2(v.z, g.z, r),
+                      norm2(v.w, g.w, r));
+}
+
+__device__ __forceinline__ uint16_t norm1(uint16_t h, uint16_t g, float r) {
+    return (uint16_t)norm2(h, g, r);
+}
+
 // One token processed by one wave.  Chunk = 8 consecutive channels (16 B);
 // lane l owns chunks l, l+64, ... of each segment of 64*CPT chunks, so every
 // load instruction of the wave reads 1 KB of the row contiguously.
@@ -115,7 +197,9 @@ __device__ __forceinline__ uint32_t pack4(uint32_t u0, uint32_t u1, uint32_t u2,
 //   committed set) with one coalesced pass per row; otherwise from the
 //   bitmap and rank table (the set being formed, whose list does not exist
 //   yet).
-template <int CPT, bool GATHER_IDX>
+//   NORM: the row is RMS-normalised as it is loaded, with the token's stored
+//   rstd (requant only; the steady-state pass computed it).
+template <int CPT, bool GATHER_IDX, bool NORM = false>
 __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_words,
                          const int32_t* rank, int set_size, const uint4* lut, uint32_t* newbits) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -123,16 +207,21 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
     const int seg_chunks = kWave * CPT;
     const int nseg = (a.nchunks + seg_chunks - 1) / seg_chunks;
 
+    static_assert(!(NORM && GATHER_IDX), "the normalised gather reads the set from the bitmap");
     uint4 xv[CPT];
     uint32_t wv[CPT];
     int32_t rk[CPT];  // rank of the first channel of the chunk's bitmap word
     uint32_t amx = 0;  // packed max of |x| bits (two halves)
+    const float rn = NORM ? a.rstd[row] : 0.0f;
     auto load_seg = [&](int s) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = s * seg_chunks + i * kWave + lane;
             if (c < a.nchunks) {
                 xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
+                if constexpr (NORM)
+                    xv[i] = norm_chunk(xv[i], *reinterpret_cast<const uint4*>(a.gamma + (int64_t)c * 8),
+                                       rn);
                 wv[i] = set_words[c >> 2];
                 rk[i] = GATHER_IDX ? 0 : rank[c >> 2];
             } else {
@@ -245,19 +334,32 @@ constexpr int kGateThreads = 256;
 // bitmap is staged in LDS; the outlier gather reads the committed channel
 // list and issues its loads together with the row's, so their latency hides
 // behind the amax.
-template <int CPT, int W>
+//
+// NORM: the pass starts with the RMSNorm of the token (the operation before
+// the layer, fused as the MixQ article allows for the amax): its exact sum
+// of squares is combined through LDS like the amax, the part in registers is
+// normalised in place, rstd is stored for the re-quantize pass.  The whole
+// part must fit in registers (one segment: K <= 32768).
+template <int CPT, int W, bool NORM>
 __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     constexpr int kRB = kGateThreads / kWave / W;  // tokens per block and round
-    extern __shared__ uint32_t dyn[];              // newbits[words], sbits[words]
+    extern __shared__ uint32_t dyn[];  // newbits[words], sbits[words], NORM: gamma[K]
     uint32_t* const newbits = dyn;
     uint32_t* const sbits = dyn + a.words;
+    const uint16_t* const sgam = reinterpret_cast<const uint16_t*>(dyn + 2 * a.words);
     __shared__ uint4 lut[kLutEntries];
     __shared__ uint32_t red[2][kRB][W];
+    __shared__ double rsum[NORM ? 2 : 1][kRB][W][2];
     __shared__ int any_det;
     build_keep_lut(lut);
     for (int w = threadIdx.x; w < a.words; w += kGateThreads) {
         newbits[w] = 0u;
         sbits[w] = a.bitmap[w];
+    }
+    if constexpr (NORM) {
+        uint4* const g4 = reinterpret_cast<uint4*>(dyn + 2 * a.words);
+        for (int c = threadIdx.x; c < a.nchunks; c += kGateThreads)
+            g4[c] = *reinterpret_cast<const uint4*>(a.gamma + (int64_t)c * 8);
     }
     if (threadIdx.x == 0) any_det = 0;
     const int set_size = *a.count;
@@ -275,6 +377,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     const bool gset = a.ld_out && gj < set_size;
     const int gch = gset ? a.idx[gj] : 0;
     auto chunk = [&](int s, int i) { return s * seg_chunks + (part * CPT + i) * kWave + lane; };
+    // gamma of this thread's first gather member (the rest of gamma is in LDS)
+    const uint16_t ggam = (NORM && gset) ? a.gamma[gch] : 0;
     typedef uint4 XV[CPT];
     typedef uint32_t WV[CPT];
     auto load_seg = [&](int64_t row, int s, XV& xv, WV& wv) {
@@ -303,6 +407,38 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         const uint16_t* xr = a.X + (valid ? row : 0) * a.ldx;
         uint16_t* orow = (a.ld_out && valid) ? a.X_out + row * (int64_t)a.ld_out : nullptr;
         auto keep_of = [&](int i, int c) -> uint4 { return lut[(wv[i] >> ((c & 3) * 8)) & 0xFFu]; };
+
+        float rn = 0.0f;
+        if constexpr (NORM) {
+            double hi = 0.0, lo = 0.0;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                sumsq_chunk(xv[i], hi, lo);
+                // one chunk's squares at a time: left to itself the scheduler
+                // widens all of them to doubles up front, which costs
+                // occupancy
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wave_pair_sum(hi, lo);
+            if (lane == 0) {
+                rsum[parity][slot][part][0] = hi;
+                rsum[parity][slot][part][1] = lo;
+            }
+            __syncthreads();
+            hi = rsum[parity][slot][0][0];
+            lo = rsum[parity][slot][0][1];
+#pragma unroll
+            for (int w = 1; w < W; ++w) pair_add(hi, lo, rsum[parity][slot][w][0], rsum[parity][slot][w][1]);
+            rn = rstd_of(hi, lo, a.K, a.eps);
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = chunk(0, i);
+                if (c < a.nchunks)
+                    xv[i] = norm_chunk(xv[i], *reinterpret_cast<const uint4*>(sgam + c * 8), rn);
+            }
+            gval = norm1(gval, ggam, rn);
+            if (valid && part == 0 && lane == 0) a.rstd[row] = rn;
+        }
 
         uint32_t amx = 0;
         for (int s = 0; s < nseg; ++s) {
@@ -379,7 +515,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         }
         if (orow) {
             if (gset) orow[gj] = gval;
-            for (int j = gj + W * kWave; j < set_size; j += W * kWave) orow[j] = xr[a.idx[j]];
+            for (int j = gj + W * kWave; j < set_size; j += W * kWave) {
+                const int ch = a.idx[j];
+                orow[j] = NORM ? norm1(xr[ch], a.gamma[ch], rn) : xr[ch];
+            }
             for (int j = set_size + gj; j < kpad; j += W * kWave) orow[j] = 0;
         }
     };
@@ -436,7 +575,7 @@ __device__ int scan_popcounts(const uint32_t* src, int words, int* prefix, int* 
 
 constexpr int kReqThreads = 256;
 
-template <int CPT>
+template <int CPT, bool NORM>
 __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
     if (*a.marker == 0u) {
         if (blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
@@ -459,7 +598,7 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
         const int64_t stride = (int64_t)gridDim.x * (kReqThreads / kWave);
         for (int64_t row = (int64_t)blockIdx.x * (kReqThreads / kWave) + wave; row < a.M;
              row += stride)
-            wave_row<CPT, false>(a, row, neww, prefix, total, lut, nullptr);
+            wave_row<CPT, false, NORM>(a, row, neww, prefix, total, lut, nullptr);
     }
     // arrival (fired calls only): the last block commits
     __syncthreads();
@@ -492,45 +631,54 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
 }
 
 constexpr int kGateWaves = 4;  // waves per token in the steady-state pass
+static_assert(MIXQ_NORM_K_MAX == kGateWaves * kWave * 16 * 8,
+              "the fused RMSNorm keeps a whole token in registers");
 
-template <int CPT_G, int CPT_R>
+template <int CPT_G, int CPT_R, bool NORM>
 int launch_act(const ActArgs& a, hipStream_t st) {
     constexpr int kRowsPerBlock = kGateThreads / kWave / kGateWaves;
     int64_t g1 = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
     // up to 1024 blocks: at M = 2048 each block takes two tokens, the second
     // one's loads in flight while the first is processed (measured: 1024
     // blocks 13.6 us, 2048 blocks 14.4 us, 512 blocks 16.4 us per call)
-    const int grid = (int)(g1 < 1024 ? g1 : 1024);
-    hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves>), dim3(grid), dim3(kGateThreads),
-                       (size_t)a.words * 8, st, a);
+    // with the RMSNorm prologue (159 VGPRs, three blocks per CU) at most as
+    // many blocks as are resident at once (measured at M = 2048: 768 blocks
+    // 25.9 us, 512 blocks 28.7 us, 1024 blocks 26.8 us per call)
+    const int gmax = NORM ? 768 : 1024;
+    const int grid = (int)(g1 < gmax ? g1 : gmax);
+    const size_t lds = (size_t)a.words * 8 + (NORM ? (size_t)a.K * 2 : 0);
+    hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM>), dim3(grid), dim3(kGateThreads),
+                       lds, st, a);
     int rc = launch_status();
     if (rc != MIXQ_OK) return rc;
     const int64_t rows_per_block = kReqThreads / kWave;
     int64_t g2 = (a.M + rows_per_block - 1) / rows_per_block;
     if (g2 > 128) g2 = 128;
-    hipLaunchKernelGGL(requant_kernel<CPT_R>, dim3((int)g2), dim3(kReqThreads),
+    hipLaunchKernelGGL((requant_kernel<CPT_R, NORM>), dim3((int)g2), dim3(kReqThreads),
                        (size_t)a.words * 8, st, a);
     return launch_status();
 }
 
-template <int CPT_G>
+template <int CPT_G, bool NORM>
 int launch_act_r(const ActArgs& a, int64_t K, hipStream_t st) {
     // requant: one wave per token, the whole row in registers up to K = 8192
     const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) return launch_act<CPT_G, 1>(a, st);
-    if (per_lane <= 2) return launch_act<CPT_G, 2>(a, st);
-    if (per_lane <= 4) return launch_act<CPT_G, 4>(a, st);
-    if (per_lane <= 8) return launch_act<CPT_G, 8>(a, st);
-    return launch_act<CPT_G, 16>(a, st);
+    if (per_lane <= 1) return launch_act<CPT_G, 1, NORM>(a, st);
+    if (per_lane <= 2) return launch_act<CPT_G, 2, NORM>(a, st);
+    if (per_lane <= 4) return launch_act<CPT_G, 4, NORM>(a, st);
+    if (per_lane <= 8) return launch_act<CPT_G, 8, NORM>(a, st);
+    return launch_act<CPT_G, 16, NORM>(a, st);
 }
 
 }  // namespace
 }  // namespace mixq
 
-extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
-                                 float threshold, const mixq_act_state* state, int8_t* Xq,
-                                 float* s_x, uint16_t* X_out, void* stream) {
-    using namespace mixq;
+namespace mixq {
+namespace {
+
+int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+             float eps, float* rstd, float threshold, const mixq_act_state* state, int8_t* Xq,
+             float* s_x, uint16_t* X_out, void* stream) {
     if (!X || !state || !Xq || !s_x) return MIXQ_ERR_INVALID_ARG;
     if (!state->idx && state->k_cap > 0) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !state->flag || !state->bitmap || !state->work)
@@ -539,8 +687,12 @@ extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_
     if (!(threshold >= 0.0f) || !isfinite(threshold)) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap < 0 || state->k_cap > K) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap > 0 && !X_out) return MIXQ_ERR_INVALID_ARG;
+    const bool norm = gamma != nullptr;
+    if (norm && (!rstd || !(eps >= 0.0f) || !isfinite(eps))) return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (ldx % 8 != 0 || ((uintptr_t)X & 15u) != 0 || ((uintptr_t)Xq & 15u) != 0)
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (norm && (K > MIXQ_NORM_K_MAX || ((uintptr_t)gamma & 15u) != 0))
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (M > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     int rc = check_device_cached();
@@ -569,14 +721,43 @@ extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_
     a.s_x = s_x;
     a.X_out = state->k_cap > 0 ? X_out : nullptr;
     a.ld_out = (int32_t)outlier_ld(state->k_cap);
+    a.gamma = gamma;
+    a.eps = eps;
+    a.rstd = rstd;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // steady-state pass: chunks per lane and segment, the whole row in
     // registers of its kGateWaves waves up to K = 32768
     const int64_t per_lane = (K / 8 + kWave * kGateWaves - 1) / (kWave * kGateWaves);
-    if (per_lane <= 1) return launch_act_r<1>(a, K, st);
-    if (per_lane <= 2) return launch_act_r<2>(a, K, st);
-    if (per_lane <= 4) return launch_act_r<4>(a, K, st);
-    if (per_lane <= 8) return launch_act_r<8>(a, K, st);
-    return launch_act_r<16>(a, K, st);
+    if (norm) {
+        if (per_lane <= 1) return launch_act_r<1, true>(a, K, st);
+        if (per_lane <= 2) return launch_act_r<2, true>(a, K, st);
+        if (per_lane <= 4) return launch_act_r<4, true>(a, K, st);
+        if (per_lane <= 8) return launch_act_r<8, true>(a, K, st);
+        return launch_act_r<16, true>(a, K, st);
+    }
+    if (per_lane <= 1) return launch_act_r<1, false>(a, K, st);
+    if (per_lane <= 2) return launch_act_r<2, false>(a, K, st);
+    if (per_lane <= 4) return launch_act_r<4, false>(a, K, st);
+    if (per_lane <= 8) return launch_act_r<8, false>(a, K, st);
+    return launch_act_r<16, false>(a, K, st);
+}
+
+}  // namespace
+}  // namespace mixq
+
+extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                 float threshold, const mixq_act_state* state, int8_t* Xq,
+                                 float* s_x, uint16_t* X_out, void* stream) {
+    return mixq::act_call(X, M, K, ldx, nullptr, 0.0f, nullptr, threshold, state, Xq, s_x, X_out,
+                          stream);
+}
+
+extern "C" int mixq_rmsnorm_quantize_act(const uint16_t* H, int64_t M, int64_t K, int64_t ldh,
+                                         const uint16_t* gamma, float eps, float threshold,
+                                         const mixq_act_state* state, int8_t* Xq, float* s_x,
+                                         uint16_t* X_out, float* rstd, void* stream) {
+    if (!gamma) return MIXQ_ERR_INVALID_ARG;
+    return mixq::act_call(H, M, K, ldh, gamma, eps, rstd, threshold, state, Xq, s_x, X_out,
+                          stream);
 }

@@ -69,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.mixq_quantize_act.argtypes = [P, I64, I64, I64, ctypes.c_float,
                                         ctypes.POINTER(ActState), P, P, P, P]
         L.mixq_quantize_act.restype = ctypes.c_int
+        L.mixq_rmsnorm_quantize_act.argtypes = [P, I64, I64, I64, P, ctypes.c_float,
+                                                ctypes.c_float, ctypes.POINTER(ActState), P, P,
+                                                P, P, P]
+        L.mixq_rmsnorm_quantize_act.restype = ctypes.c_int
         L.mixq_pack_weight.argtypes = [P, I64, I64, I32, ctypes.POINTER(ActState), I32,
                                        ctypes.POINTER(Weight), P]
         L.mixq_pack_weight.restype = ctypes.c_int
@@ -186,6 +190,23 @@ def quantize_act(X: torch.Tensor, tau: float, state: OutlierState, Xq: torch.Ten
     rc = lib().mixq_quantize_act(_ptr(X), M, state.K, X.stride(0), float(tau), ctypes.byref(st),
                                  _ptr(Xq), _ptr(s_x), _ptr(X_out), _stream(X.device))
     _check("mixq_quantize_act", rc)
+
+
+def rmsnorm_quantize_act(H: torch.Tensor, gamma: torch.Tensor, eps: float, tau: float,
+                         state: OutlierState, Xq: torch.Tensor, s_x: torch.Tensor,
+                         X_out: torch.Tensor | None, rstd: torch.Tensor) -> None:
+    """mixq_rmsnorm_quantize_act on the current stream: the RMSNorm of H
+    (fp16 [M, ldh], gamma fp16 [K]) fused into the activation pass; rstd fp32
+    [M] receives each token's 1/sqrt(mean square + eps)."""
+    assert H.dtype == torch.float16 and H.dim() == 2 and H.stride(1) == 1
+    assert gamma.dtype == torch.float16 and gamma.is_contiguous()
+    assert rstd.dtype == torch.float32
+    M = H.shape[0]
+    st = state.c()
+    rc = lib().mixq_rmsnorm_quantize_act(_ptr(H), M, state.K, H.stride(0), _ptr(gamma),
+                                         float(eps), float(tau), ctypes.byref(st), _ptr(Xq),
+                                         _ptr(s_x), _ptr(X_out), _ptr(rstd), _stream(H.device))
+    _check("mixq_rmsnorm_quantize_act", rc)
 
 
 def pack_weight(W: torch.Tensor, state: OutlierState, pw: PackedWeight,

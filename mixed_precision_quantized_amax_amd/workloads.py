@@ -16,7 +16,9 @@ Recipe (NumPy PCG64, ``default_rng``):
   4. W: normal float32 [N, K] with standard deviation ``w_std``;
   5. both cast to float16 (round to nearest even) at the end.
 For the decode sequence, a separate stream per step is derived from
-``SeedSequence([seed, 1 + step])``.
+``SeedSequence([seed, 1 + step])``.  For the RMSNorm fused in front of the
+layer, X serves as the hidden state and the norm's weight is drawn from its
+own stream (``make_norm_gamma``).
 """
 from __future__ import annotations
 
@@ -121,6 +123,21 @@ def make_activation(wl: Workload, seed: int | None = None, M: int | None = None)
     X = rng.standard_normal((m, wl.K), dtype=np.float32)
     _plant(rng, X, ch, wl)
     return _fp16(X)
+
+
+def make_norm_gamma(wl: Workload, seed: int | None = None) -> np.ndarray:
+    """RMSNorm weight fp16 [K] for feeding the workload's X as the hidden state
+    before the norm: g0 * (1 + 0.1 * N(0,1)), with g0 the expected root mean
+    square of one such token, so that the normalised tokens keep the spread
+    of X (unit scale, the planted channels above the threshold)."""
+    s = wl.seed if seed is None else seed
+    rng = np.random.default_rng(np.random.SeedSequence([s, 0x47]))
+    if wl.outlier_kind == "uniform":
+        second = (wl.hi ** 3 - wl.lo ** 3) / (3.0 * (wl.hi - wl.lo))  # E[U^2], U ~ U(lo, hi)
+    else:
+        second = wl.factor ** 2
+    g0 = np.sqrt(1.0 + wl.n_outliers / wl.K * (second - 1.0))
+    return _fp16(np.float32(g0) * (1.0 + 0.1 * rng.standard_normal(wl.K, dtype=np.float32)))
 
 
 @dataclass(frozen=True)

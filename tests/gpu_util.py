@@ -126,7 +126,12 @@ def compare_quant(g: GpuLayer, X: np.ndarray, o_res) -> None:
     assert np.array_equal(s_x.view(np.uint32), o_res.s_x.view(np.uint32))
     if g.ld:
         kp = kpad(g.count())
-        assert np.array_equal(g.x_out()[:, :kp], o_res.X_out[:, :kp])
+        got, want = g.x_out()[:, :kp], o_res.X_out[:, :kp]
+        bad = np.argwhere(got != want)
+        assert bad.shape[0] == 0, (f"{bad.shape[0]} X_out mismatches, first (row, col) "
+                                   f"{bad[:6].tolist()}: got {got[tuple(bad[:6].T)].tolist()} "
+                                   f"want {want[tuple(bad[:6].T)].tolist()}; rows "
+                                   f"{np.unique(bad[:, 0]).size}, cols {np.unique(bad[:, 1]).tolist()[:20]}")
 
 
 def check_y(Y: np.ndarray, Yref: np.ndarray) -> float:

@@ -71,11 +71,31 @@ def test_quantize_act_validation(kw, code):
     assert _quant(**kw) == code
 
 
+def _norm(H=0x10000, M=4, K=64, ldh=64, gamma=0x50000, eps=1e-5, tau=6.0, st=None, Xq=0x20000,
+          sx=0x30000, xo=0x40000, rstd=0x60000):
+    st = st or _state()
+    return mixq.lib().mixq_rmsnorm_quantize_act(
+        ctypes.c_void_p(H), M, K, ldh, ctypes.c_void_p(gamma), eps, tau, ctypes.byref(st),
+        ctypes.c_void_p(Xq), ctypes.c_void_p(sx), ctypes.c_void_p(xo), ctypes.c_void_p(rstd), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), 1), (dict(gamma=0), 1), (dict(rstd=0), 1), (dict(eps=float("nan")), 1),
+    (dict(eps=float("inf")), 1), (dict(eps=-1e-6), 1), (dict(tau=-1.0), 1), (dict(ldh=32), 1),
+    (dict(st=_state(k_cap=65)), 1), (dict(xo=0), 1),
+    (dict(K=32768 + 64, ldh=32768 + 64, st=_state(k_cap=8)), 2), (dict(gamma=0x50008), 2),
+    (dict(K=96, ldh=96), 2), (dict(H=0x10008), 2),
+])
+def test_rmsnorm_quantize_act_validation(kw, code):
+    assert _norm(**kw) == code
+
+
 def test_valid_arguments_need_a_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _quant() == 4                       # MIXQ_ERR_NO_DEVICE, nothing launched
+    assert _norm() == 4 and _norm(K=32768, ldh=32768) == 4 and _norm(eps=0.0) == 4
     assert mixq.lib().mixq_check_device() == 4
 
 

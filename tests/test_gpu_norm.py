@@ -1,0 +1,169 @@
+"""The RMSNorm fused into the activation pass (mixq_rmsnorm_quantize_act)
+against the oracle's RMSNorm followed by its activation side, bit for bit:
+rstd, the set (gate, detection, union, overflow), Xq, s_x and X_out; and the
+layer's product from those buffers against the oracle's Y."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import GpuLayer, check_y, compare_quant, say, to_dev
+from mixed_precision_quantized_amax_amd import mixq
+from oracle import Oracle, OracleLayer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return Oracle()
+
+
+class NormLayer(GpuLayer):
+    """GpuLayer whose activation side is the fused RMSNorm + quantize call."""
+
+    def __init__(self, W, gamma, eps, bits, tau, k_cap, M, ldh=None):
+        self.gamma = to_dev(gamma.view(np.float16))
+        self.eps = eps
+        self.ldh = ldh
+        super().__init__(W, bits, tau, k_cap, M)
+
+    def alloc(self, M):
+        super().alloc(M)
+        self.rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+
+    def quantize(self, H: np.ndarray):
+        M, K = H.shape
+        if self.ldh:
+            wide = np.zeros((M, self.ldh), np.float16)
+            wide[:, :K] = H
+            Hd = to_dev(wide)[:, :K]
+        else:
+            Hd = to_dev(H.view(np.float16))
+        mixq.rmsnorm_quantize_act(Hd, self.gamma, self.eps, self.tau, self.state, self.Xq,
+                                  self.s_x, self.X_out, self.rstd)
+
+
+def make_case(seed, M, K, n_out, wide=False):
+    """Hidden states N(0,1) with n_out planted channels U(20,100)*sign, and a
+    gamma around the expected root mean square of such a token, so that the
+    normalised values have the spread of the layer's usual inputs (unit scale,
+    the planted channels above the threshold)."""
+    r = np.random.default_rng(seed)
+    H = r.standard_normal((M, K))
+    ch = np.sort(r.choice(K, n_out, replace=False)) if n_out else np.zeros(0, int)
+    if n_out:
+        H[:, ch] = r.uniform(20, 100, (M, n_out)) * r.choice([-1, 1], (M, n_out))
+    if wide:
+        kind = r.integers(0, 5, (M, K))
+        H = np.where(kind == 0, r.integers(1, 1024, (M, K)) * 2.0 ** -24, H)
+        H = np.where(kind == 1, r.uniform(1000, 60000, (M, K)) * r.choice([-1, 1], (M, K)), H)
+    g0 = np.sqrt(1.0 + n_out / K * (100.0 ** 3 - 20.0 ** 3) / (3 * 80.0))
+    gamma = (g0 * (1.0 + 0.1 * r.standard_normal(K))).astype(np.float16)
+    return H.astype(np.float16), gamma
+
+
+def compare_norm(orc, g: NormLayer, o: OracleLayer, H, gamma, eps, products=True, tag=""):
+    M, K = H.shape
+    say(f"[norm] {tag} M={M} K={K} eps={eps} k_cap={g.k_cap} ldh={g.ldh}")
+    if products:
+        acc = g.step(H, acc=True)
+    else:
+        g.quantize(H)
+        torch.cuda.synchronize()
+    X, rstd = orc.rmsnorm(H, gamma, eps)
+    r = o.step(X, products=products)
+    got = g.rstd.cpu().numpy()
+    bad = np.nonzero(got.view(np.uint32) != rstd.view(np.uint32))[0]
+    assert bad.size == 0, f"{bad.size} rstd mismatches, first token {bad[:4].tolist()}"
+    compare_quant(g, X, r)
+    if products:
+        a = acc.cpu().numpy()
+        assert np.array_equal(a, r.acc)
+        err = check_y(g.Y.cpu().numpy(), r.Y)
+        say(f"[norm] {tag} ok: count={r.count} flag={r.flag} max|dY|/max|Y|={err:.2e}")
+    else:
+        say(f"[norm] {tag} ok: count={r.count} flag={r.flag}")
+    return r
+
+
+def layer_pair(orc, W, gamma, eps, tau, k_cap, M, ldh=None):
+    g = NormLayer(W, gamma, eps, 8, tau, k_cap, M, ldh=ldh)
+    o = OracleLayer(W=W, bits=8, tau=tau, k_cap=k_cap, ldo=mixq.outlier_ld(k_cap), oracle=orc)
+    return g, o
+
+
+@pytest.mark.parametrize("M,K,N,n_out,eps,wide", [
+    (1, 64, 32, 0, 1e-5, False), (37, 512, 96, 3, 1e-5, False), (130, 4096, 256, 20, 1e-6, False),
+    (64, 8192, 128, 82, 1e-5, False), (5, 32768, 64, 10, 1e-5, False),
+    (300, 1024, 200, 0, 0.0, False), (40, 2048, 64, 4, 1e-5, True), (3, 32768, 32, 0, 0.0, True),
+])
+def test_norm_random(orc, M, K, N, n_out, eps, wide):
+    H, gamma = make_case(M * 7 + K + n_out, M, K, n_out, wide)
+    W = (np.random.default_rng(K + N).standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = layer_pair(orc, W, gamma, eps, 6.0, min(K, 128), M)
+    compare_norm(orc, g, o, H, gamma, eps, tag=f"rand{'-wide' if wide else ''}")
+
+
+def test_norm_zero_rows(orc):
+    """All-zero tokens: with eps = 0 the denominator is 0 and rstd is 0; with
+    eps > 0 rstd = 1/sqrt(eps); either way the codes are 0 and the scale 1."""
+    H, gamma = make_case(3, 9, 256, 2)
+    H[[0, 4, 8]] = 0
+    W = (np.random.default_rng(3).standard_normal((48, 256)) * 0.05).astype(np.float16)
+    for eps in (0.0, 1e-5):
+        g, o = layer_pair(orc, W, gamma, eps, 6.0, 32, 9)
+        compare_norm(orc, g, o, H, gamma, eps, tag=f"zero-rows eps={eps}")
+        r = g.rstd.cpu().numpy()
+        assert (r[[0, 4, 8]] == (0.0 if eps == 0 else np.float32(1) / np.sqrt(np.float32(eps)))).all()
+        assert (g.s_x.cpu().numpy()[[0, 4, 8]] == 1.0).all()
+
+
+def test_norm_sequence(orc):
+    """Decode-like steps through one state: persistent channels, planted
+    transient ones (the gate fires and the fused re-quantize pass runs),
+    quiet steps; every step compared in full."""
+    M, K, N = 24, 1024, 64
+    rng = np.random.default_rng(11)
+    pers = np.sort(rng.choice(K, 6, replace=False))
+    gamma = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = layer_pair(orc, W, gamma, 1e-5, 6.0, 64, M)
+    flags = []
+    for st in range(8):
+        H = rng.standard_normal((M, K))
+        H[:, pers] = rng.uniform(20, 100, (M, pers.size))
+        if st in (2, 5):
+            H[rng.integers(0, M, 3), rng.integers(0, K, 3)] = 90.0
+        compare_norm(orc, g, o, H.astype(np.float16), gamma, 1e-5, tag=f"step{st}")
+        flags.append(g.flag())
+    assert flags[0] == 1 and flags[1] == 0 and flags[2] == 1 and flags[5] == 1
+
+
+def test_norm_overflow(orc):
+    """More outliers than k_cap: flag 2, the set unchanged, the call
+    quantized with the old set."""
+    H, gamma = make_case(21, 16, 512, 12)
+    W = (np.random.default_rng(21).standard_normal((32, 512)) * 0.05).astype(np.float16)
+    g, o = layer_pair(orc, W, gamma, 1e-5, 6.0, 4, 16)
+    r = compare_norm(orc, g, o, H, gamma, 1e-5, tag="overflow")
+    assert r.flag == 2 and g.flag() == 2 and g.count() == 0
+
+
+def test_norm_row_stride(orc):
+    H, gamma = make_case(31, 50, 640, 5)
+    W = (np.random.default_rng(31).standard_normal((40, 640)) * 0.05).astype(np.float16)
+    g, o = layer_pair(orc, W, gamma, 1e-5, 6.0, 64, 50, ldh=1024)
+    compare_norm(orc, g, o, H, gamma, 1e-5, tag="ldh")
+
+
+def test_norm_full_size(orc):
+    """The prefill shape (M = 2048, K = 8192, 82 planted channels): the whole
+    activation side in the launch configuration the benchmark uses."""
+    H, gamma = make_case(0, 2048, 8192, 82)
+    W = (np.random.default_rng(0).standard_normal((64, 8192)) * 0.02).astype(np.float16)
+    g, o = layer_pair(orc, W, gamma, 1e-5, 6.0, 256, 2048)
+    r = compare_norm(orc, g, o, H, gamma, 1e-5, products=False, tag="full")
+    assert r.count >= 60
+    # second call: the set is cached, the gate stays closed
+    r = compare_norm(orc, g, o, H, gamma, 1e-5, products=False, tag="full-cached")
+    assert r.flag == 0
