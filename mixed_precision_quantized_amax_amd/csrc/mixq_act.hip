@@ -118,11 +118,13 @@ __device__ __forceinline__ uint32_t pack4(uint32_t u0, uint32_t u1, uint32_t u2,
 // sum below 2^-8; the 255 combines of lane and wave partials add at most
 // 2^-7 each.  So |lo| < 2, the pair is the exact sum, and fl(hi + lo) is that
 // sum rounded once to binary64 -- whatever the order of accumulation.
+// All terms are non-negative, so ordering the two addends by max/min meets
+// the condition of Dekker's Fast2Sum (|a| >= |b|), which then gives the
+// exact rounding error in three operations.
 __device__ __forceinline__ void two_sum(double& hi, double& lo, double b) {
-    const double s = hi + b;
-    const double bb = s - hi;
-    const double err = (hi - (s - bb)) + (b - bb);
-    lo += err;
+    const double x = __builtin_fmax(hi, b), y = __builtin_fmin(hi, b);
+    const double s = x + y;
+    lo += y - (s - x);
     hi = s;
 }
 
@@ -135,8 +137,9 @@ __device__ __forceinline__ void sumsq_chunk(const uint4& v, double& hi, double& 
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+        // the square of an fp16 value is exact in binary32 (one fma from fp16)
         const float f = half_bits_to_float((uint16_t)(w[e >> 1] >> ((e & 1) * 16)));
-        two_sum(hi, lo, (double)(f * f));
+        two_sum(hi, lo, (double)__builtin_fmaf(f, f, 0.0f));
     }
 }
 
