@@ -441,23 +441,35 @@ void gemm_kernel(GemmArgs a) {
             // partial tile, then arrive on the tile counter; the second to
             // arrive adds the other's partial and finishes the tile, the
             // first leaves.  Nobody waits for anybody.  The partials are
-            // stored and loaded with device-scope (coherent) accesses, and
-            // each wave's stores are acknowledged before its block arrives,
-            // so the second block reads complete data.  Integer sums: the
-            // result does not depend on the arrival order.
+            // stored and loaded with device-scope coherent accesses (the sc1
+            // bit: what relaxed agent-scope atomics compile to), 16 bytes per
+            // lane -- dword-wide coherent loads took 15 us for a 64 KiB
+            // partial, these 1.3 us -- and each wave's stores are
+            // acknowledged before its block arrives, so the second block
+            // reads complete data.  Integer sums: the result does not depend
+            // on the arrival order.
             constexpr int kF = C::kFM * C::kFN;
             constexpr int64_t kSlot = (int64_t)C::kNW * kF * 16 * kWave;  // int32 per partial
+            constexpr int kCoherent = 16;  // buffer cache-policy bit sc1 (device scope)
             const int S = a.ksplit;
-            int32_t* const slots = a.part + (int64_t)tbid * S * kSlot;
-            int32_t* const mine = slots + split * kSlot;
+            // slot layout, 16-byte units: [wave][fragment][e / 4][lane]
+            const __amdgpu_buffer_rsrc_t rP =
+                make_rsrc(reinterpret_cast<const uint8_t*>(a.part + (int64_t)tbid * S * kSlot),
+                          (int64_t)S * kSlot * 4);
+            auto unit = [&](int t, int f, int q) {
+                return (int)((t * kSlot / 4 + (int64_t)((wave * kF + f) * 4 + q) * kWave + lane) * 16);
+            };
 #pragma unroll
             for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        __hip_atomic_store(&mine[((wave * kF + i * C::kFN + j) * 16 + e) * kWave + lane],
-                                           acc[i][j][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int q = 0; q < 4; ++q) {
+                        const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                       acc[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rP, unit(split, i * C::kFN + j, q), 0,
+                                                               kCoherent);
+                    }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             __shared__ int second;
@@ -473,16 +485,17 @@ void gemm_kernel(GemmArgs a) {
             if (!second) return;
             for (int t = 0; t < S; ++t) {
                 if (t == split) continue;
-                const int32_t* const other = slots + t * kSlot;
 #pragma unroll
                 for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
                     for (int j = 0; j < C::kFN; ++j)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            acc[i][j][e] += __hip_atomic_load(
-                                &other[((wave * kF + i * C::kFN + j) * 16 + e) * kWave + lane],
-                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        for (int q = 0; q < 4; ++q) {
+                            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+                                rP, unit(t, i * C::kFN + j, q), 0, kCoherent);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+                        }
             }
         }
     } else if constexpr (STAGES == 2) {
@@ -1049,8 +1062,8 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
     const int f = forced_cfg();
-    const int S = ws && (f == kCfgAuto || f == kCfg128x128KP) &&
-                          pick_cfg(M, w->N, w->K, w->bits) == kCfg128x128KP
+    const int pc = pick_cfg(M, w->N, w->K, w->bits);
+    const int S = ws && (f == kCfgAuto || f == kCfg128x128KP) && pc == kCfg128x128KP
                       ? split_plan(M, w->N, w->K, w->bits, device_cu_count())
                       : 1;
     if (S > 1 && (int64_t)ws_bytes >= split_workspace_bytes(M, w->N, S)) {
