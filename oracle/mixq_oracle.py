@@ -113,10 +113,14 @@ class Oracle:
         n = self.lib.orc_outlier_list(_ptr(s), s.size, _ptr(idx))
         return idx[:n].copy()
 
-    # -- the operation before the layer ------------------------------------------
+    # -- the operations before the layer -----------------------------------------
     def rmsnorm(self, H, gamma, eps: float):
         """Returns (X fp16 [M, K], rstd fp32 [M]); see ``rmsnorm`` below."""
         return rmsnorm(H, gamma, eps)
+
+    def residual_add(self, R, D):
+        """Returns H fp16; see ``residual_add`` below."""
+        return residual_add(R, D)
 
     # -- quantization ----------------------------------------------------------
     def quantize_act(self, X, in_set: np.ndarray, ldo: int):
@@ -186,6 +190,16 @@ class Oracle:
         if rc != 0:
             raise OverflowError("integer accumulator exceeds int32")
         return acc, Y
+
+
+def residual_add(R, D):
+    """The residual update before the norm of a LLaMA block, H = R + D in fp16:
+    the exact sum (two fp16 values are multiples of 2^-24 below 2^16, so their
+    sum is exact in binary64) rounded once to fp16, ties to even.  R, D: fp16
+    (or their bit patterns) of one shape; finite sums are a precondition."""
+    r = R.view(np.float16) if R.dtype == np.uint16 else np.asarray(R, np.float16)
+    d = D.view(np.float16) if D.dtype == np.uint16 else np.asarray(D, np.float16)
+    return (r.astype(np.float64) + d.astype(np.float64)).astype(np.float16)
 
 
 def rmsnorm(H, gamma, eps: float):

@@ -608,10 +608,39 @@ def pin_rmsnorm_closed_form(o):
     assert rstd[-1] == 0 and not X[-1].astype(np.float64).any()
 
 
+def pin_residual_add(o):
+    """H = R + D against exact rationals rounded to fp16 by the rule written
+    out (ties to even, subnormals included), on random pairs, pairs built to
+    land exactly halfway between fp16 values, and pairs with subnormal sums;
+    plus x + (-x) = +0, x + 0 = x and commutativity, bit for bit."""
+    r = _rng(91)
+    R = (r.standard_normal((6, 64)) * 4.0).astype(np.float16)
+    D = (r.standard_normal((6, 64)) * 0.5).astype(np.float16)
+    # halfway cases: a value of magnitude in [1, 2) (fp16 step 2^-10) plus 2^-11 or 3*2^-11
+    base = (1.0 + r.integers(0, 1024, 64) * 2.0 ** -10).astype(np.float16)
+    half = np.where(r.random(64) < 0.5, 2.0 ** -11, 3 * 2.0 ** -11).astype(np.float16)
+    sub = (r.integers(-1023, 1024, (2, 64)) * 2.0 ** -24).astype(np.float16)
+    cases = [(R, D), (base[None], half[None]), (sub[:1], sub[1:]),
+             (R, -R), (R, np.zeros_like(R))]
+    for a, b in cases:
+        got = o.residual_add(a, b)
+        for x, y, h in zip(a.ravel().astype(np.float64), b.ravel().astype(np.float64),
+                           got.ravel().astype(np.float64)):
+            assert Fraction(float(h)) == _r16(Fraction(x) + Fraction(y)), (x, y, h)
+        assert (o.residual_add(b, a).view(np.uint16) == got.view(np.uint16)).all()
+    z = o.residual_add(R, -R)
+    assert (z.view(np.uint16) == 0).all()  # +0, not -0
+    assert (o.residual_add(R, np.zeros_like(R)).view(np.uint16) == R.view(np.uint16)).all()
+    # the halfway cases do round to even: about half of them round up
+    hb = o.residual_add(base[None], half[None]).astype(np.float64)
+    assert 0 < (hb > base.astype(np.float64) + half.astype(np.float64)).sum() < 64
+
+
 ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode,
             pin_set_bruteforce, pin_quant_error_bound, pin_nearest_code, pin_weight_bound,
             pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
             pin_output_vs_truth_bound, pin_no_outlier_textbook, pin_all_outlier,
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
             pin_decode_sequence, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
-            pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals]
+            pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals,
+            pin_residual_add]

@@ -108,8 +108,26 @@ RMS_MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", RMS_MUTANTS, ids=[m[0] for m in RMS_MUTANTS])
-def test_rmsnorm_mutant_is_caught(name, old, new):
+_SUM = "return (r.astype(np.float64) + d.astype(np.float64)).astype(np.float16)"
+RES_MUTANTS = [
+    ("add_truncates", _SUM,
+     "s = r.astype(np.float64) + d.astype(np.float64)\n    t = s.astype(np.float16)\n"
+     "    return np.where(np.abs(t.astype(np.float64)) > np.abs(s), "
+     "np.nextafter(t, np.float16(0)), t)"),
+    ("add_ties_away", _SUM,
+     "s = r.astype(np.float64) + d.astype(np.float64)\n"
+     "    return (s + np.sign(s) * 2.0 ** -40).astype(np.float16)"),
+    ("add_flushes_subnormals", _SUM,
+     "t = (r.astype(np.float64) + d.astype(np.float64)).astype(np.float16)\n"
+     "    return np.where(np.abs(t) < 2.0 ** -14, t * np.float16(0), t)"),
+]
+
+
+@pytest.mark.parametrize("fn,name,old,new",
+                         [("rmsnorm", *m) for m in RMS_MUTANTS] +
+                         [("residual_add", *m) for m in RES_MUTANTS],
+                         ids=[m[0] for m in RMS_MUTANTS] + [m[0] for m in RES_MUTANTS])
+def test_prologue_mutant_is_caught(fn, name, old, new):
     import inspect
     import textwrap
 
@@ -117,19 +135,19 @@ def test_rmsnorm_mutant_is_caught(name, old, new):
 
     from oracle import mixq_oracle
 
-    src = textwrap.dedent(inspect.getsource(mixq_oracle.rmsnorm))
+    src = textwrap.dedent(inspect.getsource(getattr(mixq_oracle, fn)))
     assert src.count(old) == 1, f"mutation site not found: {old!r}"
     ns = {"np": np}
     exec(compile(src.replace(old, new), f"<{name}>", "exec"), ns)
 
     class Mutant(Oracle):
-        def rmsnorm(self, H, gamma, eps):
-            return ns["rmsnorm"](H, gamma, eps)
+        pass
 
+    setattr(Mutant, fn, lambda self, *args: ns[fn](*args))
     o = Mutant()
     failed = []
     for pin in oracle_pins.ALL_PINS:
-        if "rmsnorm" not in pin.__name__:
+        if fn not in pin.__name__ and not (fn == "rmsnorm" and "rmsnorm" in pin.__name__):
             continue
         try:
             pin(o)
