@@ -194,6 +194,10 @@ def run_fused_norm(wl, steps: int, warmup: int, eps: float = 1e-5):
     rs = [torch.empty(wl.M, dtype=torch.float32, device=dev) for _ in range(copies)]
     st_f = mixq.OutlierState.create(wl.K, k_cap, dev)
     st_u = mixq.OutlierState.create(wl.K, k_cap, dev)
+    st_r = mixq.OutlierState.create(wl.K, k_cap, dev)
+    # residual variant: H = R + D written to its own buffer (R = the copies above)
+    D0 = (torch.randn(wl.M, wl.K, generator=torch.Generator().manual_seed(7)) * 0.1).half().to(dev)
+    Ho = [torch.empty_like(H0) for _ in range(copies)]
     stream = torch.cuda.current_stream(dev)
 
     def fused(i):
@@ -205,15 +209,29 @@ def run_fused_norm(wl, steps: int, warmup: int, eps: float = 1e-5):
         Xn = F.rms_norm(Hs[c], (wl.K,), gamma, eps)
         mixq.quantize_act(Xn, wl.tau, st_u, Xq[c], sx[c], Xo[c])
 
+    def fused_add(i):
+        c = i % copies
+        mixq.add_rmsnorm_quantize_act(Hs[c], D0, Ho[c], gamma, eps, wl.tau, st_r, Xq[c], sx[c],
+                                      Xo[c], rs[c])
+
+    def unfused_add(i):
+        c = i % copies
+        torch.add(Hs[c], D0, out=Ho[c])
+        Xn = F.rms_norm(Ho[c], (wl.K,), gamma, eps)
+        mixq.quantize_act(Xn, wl.tau, st_u, Xq[c], sx[c], Xo[c])
+
     for i in range(warmup):
         fused(i)
         unfused(i)
+        fused_add(i)
+        unfused_add(i)
     torch.cuda.synchronize()
     count = int(st_f.count.cpu()[0])
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     res = {}
-    for name, fn in (("fused", fused), ("unfused", unfused)):
+    for name, fn in (("fused", fused), ("unfused", unfused), ("fused_add", fused_add),
+                     ("unfused_add", unfused_add)):
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(steps):
@@ -231,6 +249,10 @@ def run_fused_norm(wl, steps: int, warmup: int, eps: float = 1e-5):
             "last_flag": flag, "eps": eps,
             "unfused_us": round(res["unfused"] * 1e3, 2),
             "unfused": "torch rms_norm (fp16 out) + mixq_quantize_act",
+            "with_residual_add_us": round(res["fused_add"] * 1e3, 2),
+            "with_residual_add_gbs": round((norm_act_bytes(wl, count) + 4 * wl.M * wl.K)
+                                           / (res["fused_add"] / 1e3) / 1e9, 1),
+            "with_residual_add_unfused_us": round(res["unfused_add"] * 1e3, 2),
             "kernels": "gate_quant_kernel (RMSNorm prologue) + requant_kernel (no-op unless "
                        "the gate fires)"}
 

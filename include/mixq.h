@@ -198,6 +198,34 @@ int mixq_rmsnorm_quantize_act(const uint16_t *H, int64_t M, int64_t K, int64_t l
                               uint16_t *X_out, float *rstd, void *stream);
 
 /*
+ * mixq_add_rmsnorm_quantize_act -- the residual update of a LLaMA block
+ * followed by mixq_rmsnorm_quantize_act, in one pass over memory: the whole
+ * operation before the layer, into which the MixQ article ("MixQ的解决方案",
+ * the paragraph after the amax test) lets the amax be fused.
+ *
+ *   H[m,k] = fp16(R[m,k] + D[m,k])   (the exact sum rounded once, ties to
+ *                                     even), written out as the new residual;
+ *   then everything mixq_rmsnorm_quantize_act does, on H.
+ *
+ *   R, D     fp16 [M, ldr] and [M, ldd] device, row-major, read-only; finite
+ *            sums
+ *   H        fp16 [M, ldh] device, written; it must not overlap R or D (a
+ *            ping-pong pair of residual buffers replaces an in-place update)
+ *   ldr, ldd, ldh  row strides in elements, >= K, multiples of 8; R, D, H
+ *            16-byte aligned
+ *   M, K, gamma, eps, threshold, state, Xq, s_x, X_out, rstd
+ *            as mixq_rmsnorm_quantize_act
+ * Errors: as mixq_rmsnorm_quantize_act; MIXQ_ERR_INVALID_ARG also for a null
+ *         D or H, a stride below K, or H overlapping R or D;
+ *         MIXQ_ERR_UNSUPPORTED_SHAPE also for misaligned D or H or strides.
+ */
+int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t *D, int64_t ldd,
+                                  uint16_t *H, int64_t ldh, int64_t M, int64_t K,
+                                  const uint16_t *gamma, float eps, float threshold,
+                                  const mixq_act_state *state, int8_t *Xq, float *s_x,
+                                  uint16_t *X_out, float *rstd, void *stream);
+
+/*
  * mixq_pack_weight -- per-output-channel symmetric quantization of W and the
  * FP16 outlier columns (FP6 explainer, section 3; MixQ article, Fig. 11).
  *

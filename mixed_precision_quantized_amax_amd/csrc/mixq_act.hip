@@ -56,6 +56,11 @@ struct ActArgs {
     const uint16_t* gamma;
     float eps;
     float* rstd;
+    // residual add before the norm (D null: none): X is R, H = R + D is written
+    const uint16_t* D;
+    int64_t ldd;
+    uint16_t* H;
+    int64_t ldh;
 };
 
 // LDS table: for the 8 cached-channel bits of a chunk (8 halves = 4 dwords),
@@ -185,6 +190,16 @@ __device__ __forceinline__ uint4 norm_chunk(const uint4& v, const uint4& g, floa
 
 __device__ __forceinline__ uint16_t norm1(uint16_t h, uint16_t g, float r) {
     return (uint16_t)norm2(h, g, r);
+}
+
+// fp16 sums of two dwords of halves (v_pk_add_f16: the exact sum rounded to
+// fp16, ties to even)
+__device__ __forceinline__ uint32_t hadd2(uint32_t x, uint32_t y) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, x) + __builtin_bit_cast(half2v, y));
+}
+
+__device__ __forceinline__ uint4 hadd_chunk(const uint4& x, const uint4& y) {
+    return make_uint4(hadd2(x.x, y.x), hadd2(x.y, y.y), hadd2(x.z, y.z), hadd2(x.w, y.w));
 }
 
 // One token processed by one wave.  Chunk = 8 consecutive channels (16 B);
@@ -343,8 +358,11 @@ constexpr int kGateThreads = 256;
 // of squares is combined through LDS like the amax, the part in registers is
 // normalised in place, rstd is stored for the re-quantize pass.  The whole
 // part must fit in registers (one segment: K <= 32768).
-template <int CPT, int W, bool NORM>
+// RES: before that, the residual add H = R + D (X is R), H written out; one
+// token buffer (R and D both in flight) instead of two.
+template <int CPT, int W, bool NORM, bool RES = false>
 __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
+    static_assert(!RES || NORM, "the residual add comes with the norm");
     constexpr int kRB = kGateThreads / kWave / W;  // tokens per block and round
     extern __shared__ uint32_t dyn[];  // newbits[words], sbits[words], NORM: gamma[K]
     uint32_t* const newbits = dyn;
@@ -404,12 +422,36 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         load_seg(row, 0, xv, wv);
         if (gset && row < a.M) gv = a.X[row * a.ldx + gch];
     };
+    // RES: the matching D chunks and gather value
+    auto load_d = [&](int64_t row, XV& dv, uint16_t& gd) {
+        const bool valid = row < a.M;
+        const uint16_t* dr = a.D + (valid ? row : 0) * a.ldd;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = chunk(0, i);
+            dv[i] = (valid && c < a.nchunks) ? *reinterpret_cast<const uint4*>(dr + (int64_t)c * 8)
+                                             : make_uint4(0, 0, 0, 0);
+        }
+        if (gset && valid) gd = dr[gch];
+    };
     bool det = false;
-    auto process = [&](int64_t row, XV& xv, WV& wv, uint16_t gval, int parity) {
+    auto process = [&](int64_t row, XV& xv, WV& wv, uint16_t gval, int parity, const XV* dv,
+                       uint16_t gd) {
         const bool valid = row < a.M;
         const uint16_t* xr = a.X + (valid ? row : 0) * a.ldx;
         uint16_t* orow = (a.ld_out && valid) ? a.X_out + row * (int64_t)a.ld_out : nullptr;
         auto keep_of = [&](int i, int c) -> uint4 { return lut[(wv[i] >> ((c & 3) * 8)) & 0xFFu]; };
+
+        if constexpr (RES) {
+            uint16_t* hr = a.H + (valid ? row : 0) * a.ldh;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = chunk(0, i);
+                xv[i] = hadd_chunk(xv[i], (*dv)[i]);
+                if (valid && c < a.nchunks) *reinterpret_cast<uint4*>(hr + (int64_t)c * 8) = xv[i];
+            }
+            gval = (uint16_t)hadd2(gval, gd);
+        }
 
         float rn = 0.0f;
         if constexpr (NORM) {
@@ -520,7 +562,9 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
             if (gset) orow[gj] = gval;
             for (int j = gj + W * kWave; j < set_size; j += W * kWave) {
                 const int ch = a.idx[j];
-                orow[j] = NORM ? norm1(xr[ch], a.gamma[ch], rn) : xr[ch];
+                uint16_t v = xr[ch];
+                if constexpr (RES) v = (uint16_t)hadd2(v, a.D[row * a.ldd + ch]);
+                orow[j] = NORM ? norm1(v, a.gamma[ch], rn) : v;
             }
             for (int j = set_size + gj; j < kpad; j += W * kWave) orow[j] = 0;
         }
@@ -529,6 +573,18 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     // flight while the current one is processed.  The loop is block-uniform
     // (process has a barrier).
     const int64_t stride = (int64_t)gridDim.x * kRB;
+    if constexpr (RES) {
+        int par = 0;
+        for (int64_t r0 = (int64_t)blockIdx.x * kRB; r0 < a.M; r0 += stride) {
+            XV xa, da;
+            WV wa;
+            uint16_t ga = 0, gd = 0;
+            load_row(r0 + slot, xa, wa, ga);
+            load_d(r0 + slot, da, gd);
+            process(r0 + slot, xa, wa, ga, par, &da, gd);
+            par ^= 1;
+        }
+    } else {
     XV xa, xb;
     WV wa, wb;
     uint16_t ga = 0, gb2 = 0;
@@ -536,10 +592,11 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     if (r0 < a.M) load_row(r0 + slot, xa, wa, ga);
     for (; r0 < a.M; r0 += 2 * stride) {
         if (r0 + stride < a.M) load_row(r0 + stride + slot, xb, wb, gb2);
-        process(r0 + slot, xa, wa, ga, 0);
+        process(r0 + slot, xa, wa, ga, 0, nullptr, 0);
         if (r0 + stride >= a.M) break;
         if (r0 + 2 * stride < a.M) load_row(r0 + 2 * stride + slot, xa, wa, ga);
-        process(r0 + stride + slot, xb, wb, gb2, 1);
+        process(r0 + stride + slot, xb, wb, gb2, 1, nullptr, 0);
+    }
     }
     if (det && lane == 0) any_det = 1;
     __syncthreads();
@@ -637,7 +694,7 @@ constexpr int kGateWaves = 4;  // waves per token in the steady-state pass
 static_assert(MIXQ_NORM_K_MAX == kGateWaves * kWave * 16 * 8,
               "the fused RMSNorm keeps a whole token in registers");
 
-template <int CPT_G, int CPT_R, bool NORM>
+template <int CPT_G, int CPT_R, bool NORM, bool RES>
 int launch_act(const ActArgs& a, hipStream_t st) {
     constexpr int kRowsPerBlock = kGateThreads / kWave / kGateWaves;
     int64_t g1 = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -647,30 +704,36 @@ int launch_act(const ActArgs& a, hipStream_t st) {
     // with the RMSNorm prologue (159 VGPRs, three blocks per CU) at most as
     // many blocks as are resident at once (measured at M = 2048: 768 blocks
     // 25.9 us, 512 blocks 28.7 us, 1024 blocks 26.8 us per call)
-    const int gmax = NORM ? 768 : 1024;
+    const int gmax = NORM && !RES ? 768 : 1024;  // the residual variant: 108 VGPRs, four blocks per CU
     const int grid = (int)(g1 < gmax ? g1 : gmax);
     const size_t lds = (size_t)a.words * 8 + (NORM ? (size_t)a.K * 2 : 0);
-    hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM>), dim3(grid), dim3(kGateThreads),
-                       lds, st, a);
+    hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES>), dim3(grid),
+                       dim3(kGateThreads), lds, st, a);
     int rc = launch_status();
     if (rc != MIXQ_OK) return rc;
     const int64_t rows_per_block = kReqThreads / kWave;
     int64_t g2 = (a.M + rows_per_block - 1) / rows_per_block;
     if (g2 > 128) g2 = 128;
+    // with the residual add, the re-quantize pass reads the finished H
+    ActArgs ar = a;
+    if (RES) {
+        ar.X = a.H;
+        ar.ldx = a.ldh;
+    }
     hipLaunchKernelGGL((requant_kernel<CPT_R, NORM>), dim3((int)g2), dim3(kReqThreads),
-                       (size_t)a.words * 8, st, a);
+                       (size_t)a.words * 8, st, ar);
     return launch_status();
 }
 
-template <int CPT_G, bool NORM>
+template <int CPT_G, bool NORM, bool RES>
 int launch_act_r(const ActArgs& a, int64_t K, hipStream_t st) {
     // requant: one wave per token, the whole row in registers up to K = 8192
     const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) return launch_act<CPT_G, 1, NORM>(a, st);
-    if (per_lane <= 2) return launch_act<CPT_G, 2, NORM>(a, st);
-    if (per_lane <= 4) return launch_act<CPT_G, 4, NORM>(a, st);
-    if (per_lane <= 8) return launch_act<CPT_G, 8, NORM>(a, st);
-    return launch_act<CPT_G, 16, NORM>(a, st);
+    if (per_lane <= 1) return launch_act<CPT_G, 1, NORM, RES>(a, st);
+    if (per_lane <= 2) return launch_act<CPT_G, 2, NORM, RES>(a, st);
+    if (per_lane <= 4) return launch_act<CPT_G, 4, NORM, RES>(a, st);
+    if (per_lane <= 8) return launch_act<CPT_G, 8, NORM, RES>(a, st);
+    return launch_act<CPT_G, 16, NORM, RES>(a, st);
 }
 
 }  // namespace
@@ -679,9 +742,21 @@ int launch_act_r(const ActArgs& a, int64_t K, hipStream_t st) {
 namespace mixq {
 namespace {
 
+// Bytes a row-major fp16 matrix spans.
+inline uintptr_t span_end(const uint16_t* p, int64_t M, int64_t K, int64_t ld) {
+    return reinterpret_cast<uintptr_t>(p) + (uintptr_t)(((M - 1) * ld + K) * 2);
+}
+
+inline bool overlaps(const uint16_t* p, const uint16_t* q, int64_t M, int64_t K, int64_t ldp,
+                     int64_t ldq) {
+    return reinterpret_cast<uintptr_t>(p) < span_end(q, M, K, ldq) &&
+           reinterpret_cast<uintptr_t>(q) < span_end(p, M, K, ldp);
+}
+
 int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
              float eps, float* rstd, float threshold, const mixq_act_state* state, int8_t* Xq,
-             float* s_x, uint16_t* X_out, void* stream) {
+             float* s_x, uint16_t* X_out, void* stream, const uint16_t* D = nullptr,
+             int64_t ldd = 0, uint16_t* H = nullptr, int64_t ldh = 0) {
     if (!X || !state || !Xq || !s_x) return MIXQ_ERR_INVALID_ARG;
     if (!state->idx && state->k_cap > 0) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !state->flag || !state->bitmap || !state->work)
@@ -691,11 +766,20 @@ int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_
     if (state->k_cap < 0 || state->k_cap > K) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap > 0 && !X_out) return MIXQ_ERR_INVALID_ARG;
     const bool norm = gamma != nullptr;
+    const bool res = D != nullptr;
     if (norm && (!rstd || !(eps >= 0.0f) || !isfinite(eps))) return MIXQ_ERR_INVALID_ARG;
+    if (res && (!norm || !H || ldd < K || ldh < K)) return MIXQ_ERR_INVALID_ARG;
+    // H is written while X (R) and D are still read, by other waves
+    if (res && M > 0 && K > 0 && ldx >= K &&
+        (overlaps(H, X, M, K, ldh, ldx) || overlaps(H, D, M, K, ldh, ldd)))
+        return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (ldx % 8 != 0 || ((uintptr_t)X & 15u) != 0 || ((uintptr_t)Xq & 15u) != 0)
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (norm && (K > MIXQ_NORM_K_MAX || ((uintptr_t)gamma & 15u) != 0))
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (res && (ldd % 8 != 0 || ldh % 8 != 0 || ((uintptr_t)D & 15u) != 0 ||
+                ((uintptr_t)H & 15u) != 0))
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (M > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     int rc = check_device_cached();
@@ -727,23 +811,34 @@ int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_
     a.gamma = gamma;
     a.eps = eps;
     a.rstd = rstd;
+    a.D = D;
+    a.ldd = ldd;
+    a.H = H;
+    a.ldh = ldh;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // steady-state pass: chunks per lane and segment, the whole row in
     // registers of its kGateWaves waves up to K = 32768
     const int64_t per_lane = (K / 8 + kWave * kGateWaves - 1) / (kWave * kGateWaves);
-    if (norm) {
-        if (per_lane <= 1) return launch_act_r<1, true>(a, K, st);
-        if (per_lane <= 2) return launch_act_r<2, true>(a, K, st);
-        if (per_lane <= 4) return launch_act_r<4, true>(a, K, st);
-        if (per_lane <= 8) return launch_act_r<8, true>(a, K, st);
-        return launch_act_r<16, true>(a, K, st);
+    if (res) {
+        if (per_lane <= 1) return launch_act_r<1, true, true>(a, K, st);
+        if (per_lane <= 2) return launch_act_r<2, true, true>(a, K, st);
+        if (per_lane <= 4) return launch_act_r<4, true, true>(a, K, st);
+        if (per_lane <= 8) return launch_act_r<8, true, true>(a, K, st);
+        return launch_act_r<16, true, true>(a, K, st);
     }
-    if (per_lane <= 1) return launch_act_r<1, false>(a, K, st);
-    if (per_lane <= 2) return launch_act_r<2, false>(a, K, st);
-    if (per_lane <= 4) return launch_act_r<4, false>(a, K, st);
-    if (per_lane <= 8) return launch_act_r<8, false>(a, K, st);
-    return launch_act_r<16, false>(a, K, st);
+    if (norm) {
+        if (per_lane <= 1) return launch_act_r<1, true, false>(a, K, st);
+        if (per_lane <= 2) return launch_act_r<2, true, false>(a, K, st);
+        if (per_lane <= 4) return launch_act_r<4, true, false>(a, K, st);
+        if (per_lane <= 8) return launch_act_r<8, true, false>(a, K, st);
+        return launch_act_r<16, true, false>(a, K, st);
+    }
+    if (per_lane <= 1) return launch_act_r<1, false, false>(a, K, st);
+    if (per_lane <= 2) return launch_act_r<2, false, false>(a, K, st);
+    if (per_lane <= 4) return launch_act_r<4, false, false>(a, K, st);
+    if (per_lane <= 8) return launch_act_r<8, false, false>(a, K, st);
+    return launch_act_r<16, false, false>(a, K, st);
 }
 
 }  // namespace
@@ -763,4 +858,15 @@ extern "C" int mixq_rmsnorm_quantize_act(const uint16_t* H, int64_t M, int64_t K
     if (!gamma) return MIXQ_ERR_INVALID_ARG;
     return mixq::act_call(H, M, K, ldh, gamma, eps, rstd, threshold, state, Xq, s_x, X_out,
                           stream);
+}
+
+extern "C" int mixq_add_rmsnorm_quantize_act(const uint16_t* R, int64_t ldr, const uint16_t* D,
+                                             int64_t ldd, uint16_t* H, int64_t ldh, int64_t M,
+                                             int64_t K, const uint16_t* gamma, float eps,
+                                             float threshold, const mixq_act_state* state,
+                                             int8_t* Xq, float* s_x, uint16_t* X_out, float* rstd,
+                                             void* stream) {
+    if (!gamma || !D || !H) return MIXQ_ERR_INVALID_ARG;
+    return mixq::act_call(R, M, K, ldr, gamma, eps, rstd, threshold, state, Xq, s_x, X_out,
+                          stream, D, ldd, H, ldh);
 }

@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.c_float, ctypes.POINTER(ActState), P, P,
                                                 P, P, P]
         L.mixq_rmsnorm_quantize_act.restype = ctypes.c_int
+        L.mixq_add_rmsnorm_quantize_act.argtypes = [P, I64, P, I64, P, I64, I64, I64, P,
+                                                    ctypes.c_float, ctypes.c_float,
+                                                    ctypes.POINTER(ActState), P, P, P, P, P]
+        L.mixq_add_rmsnorm_quantize_act.restype = ctypes.c_int
         L.mixq_pack_weight.argtypes = [P, I64, I64, I32, ctypes.POINTER(ActState), I32,
                                        ctypes.POINTER(Weight), P]
         L.mixq_pack_weight.restype = ctypes.c_int
@@ -207,6 +211,26 @@ def rmsnorm_quantize_act(H: torch.Tensor, gamma: torch.Tensor, eps: float, tau: 
                                          float(eps), float(tau), ctypes.byref(st), _ptr(Xq),
                                          _ptr(s_x), _ptr(X_out), _ptr(rstd), _stream(H.device))
     _check("mixq_rmsnorm_quantize_act", rc)
+
+
+def add_rmsnorm_quantize_act(R: torch.Tensor, D: torch.Tensor, H: torch.Tensor,
+                             gamma: torch.Tensor, eps: float, tau: float, state: OutlierState,
+                             Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None,
+                             rstd: torch.Tensor) -> None:
+    """mixq_add_rmsnorm_quantize_act on the current stream: H = R + D (fp16,
+    written; it must not overlap R or D), then the RMSNorm of H fused into the
+    activation pass."""
+    for t in (R, D, H):
+        assert t.dtype == torch.float16 and t.dim() == 2 and t.stride(1) == 1
+    assert gamma.dtype == torch.float16 and gamma.is_contiguous()
+    assert rstd.dtype == torch.float32
+    M = R.shape[0]
+    st = state.c()
+    rc = lib().mixq_add_rmsnorm_quantize_act(
+        _ptr(R), R.stride(0), _ptr(D), D.stride(0), _ptr(H), H.stride(0), M, state.K,
+        _ptr(gamma), float(eps), float(tau), ctypes.byref(st), _ptr(Xq), _ptr(s_x), _ptr(X_out),
+        _ptr(rstd), _stream(R.device))
+    _check("mixq_add_rmsnorm_quantize_act", rc)
 
 
 def pack_weight(W: torch.Tensor, state: OutlierState, pw: PackedWeight,

@@ -90,12 +90,33 @@ def test_rmsnorm_quantize_act_validation(kw, code):
     assert _norm(**kw) == code
 
 
+def _addnorm(R=0x10000, ldr=64, D=0x70000, ldd=64, H=0x80000, ldh=64, M=4, K=64, gamma=0x50000,
+             eps=1e-5, tau=6.0, st=None, Xq=0x20000, sx=0x30000, xo=0x40000, rstd=0x60000):
+    st = st or _state()
+    v = ctypes.c_void_p
+    return mixq.lib().mixq_add_rmsnorm_quantize_act(
+        v(R), ldr, v(D), ldd, v(H), ldh, M, K, v(gamma), eps, tau, ctypes.byref(st), v(Xq), v(sx),
+        v(xo), v(rstd), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), 1), (dict(D=0), 1), (dict(H=0), 1), (dict(gamma=0), 1), (dict(rstd=0), 1),
+    (dict(ldd=32), 1), (dict(ldh=32), 1), (dict(eps=-1.0), 1),
+    (dict(H=0x10000), 1), (dict(H=0x10000 + 4 * 64 * 2 - 16), 1), (dict(H=0x70000), 1),
+    (dict(D=0x70008), 2), (dict(H=0x80008), 2), (dict(ldd=68), 2), (dict(ldh=68), 2),
+    (dict(K=32768 + 64, ldr=32768 + 64, ldd=32768 + 64, ldh=32768 + 64, D=0x100000, H=0x200000), 2),
+])
+def test_add_rmsnorm_quantize_act_validation(kw, code):
+    assert _addnorm(**kw) == code
+
+
 def test_valid_arguments_need_a_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _quant() == 4                       # MIXQ_ERR_NO_DEVICE, nothing launched
     assert _norm() == 4 and _norm(K=32768, ldh=32768) == 4 and _norm(eps=0.0) == 4
+    assert _addnorm() == 4 and _addnorm(H=0x10000 + 4 * 64 * 2) == 4  # adjacent, not overlapping
     assert mixq.lib().mixq_check_device() == 4
 
 

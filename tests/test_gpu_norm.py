@@ -167,3 +167,119 @@ def test_norm_full_size(orc):
     # second call: the set is cached, the gate stays closed
     r = compare_norm(orc, g, o, H, gamma, 1e-5, products=False, tag="full-cached")
     assert r.flag == 0
+
+
+# ---- the residual add before the norm (mixq_add_rmsnorm_quantize_act) ----------------
+class ResLayer(NormLayer):
+    """The activation side is the fused residual add + RMSNorm + quantize
+    call; ``quantize`` takes the pair (R, D) and H is written to ``self.H``."""
+
+    def __init__(self, *args, lds=None, **kw):
+        self.lds = lds  # (ldr, ldd, ldh) or None for K
+        super().__init__(*args, **kw)
+
+    def quantize(self, RD):
+        R, D = RD
+        M, K = R.shape
+        ldr, ldd, ldh = self.lds or (K, K, K)
+
+        def dev(a, ld):
+            wide = np.zeros((M, ld), np.float16)
+            wide[:, :K] = a
+            return to_dev(wide)[:, :K]
+
+        Rd, Dd = dev(R, ldr), dev(D, ldd)
+        self.Hbuf = torch.full((M, ldh), float("nan"), dtype=torch.float16, device="cuda")
+        H = self.Hbuf[:, :K]
+        mixq.add_rmsnorm_quantize_act(Rd, Dd, H, self.gamma, self.eps, self.tau, self.state,
+                                      self.Xq, self.s_x, self.X_out, self.rstd)
+
+
+def compare_res(orc, g: ResLayer, o: OracleLayer, R, D, gamma, eps, products=True, tag=""):
+    M, K = R.shape
+    say(f"[res] {tag} M={M} K={K} eps={eps} k_cap={g.k_cap} lds={g.lds}")
+    if products:
+        acc = g.step((R, D), acc=True)
+    else:
+        g.quantize((R, D))
+        torch.cuda.synchronize()
+    H = orc.residual_add(R, D)
+    got_h = g.Hbuf[:, :K].cpu().numpy()
+    bad = np.argwhere(got_h.view(np.uint16) != H.view(np.uint16))
+    assert bad.shape[0] == 0, f"{bad.shape[0]} H mismatches, first {bad[:4].tolist()}"
+    if g.lds:  # the padding of H's rows is not written
+        assert np.isnan(g.Hbuf[:, K:].cpu().numpy().astype(np.float32)).all()
+    X, rstd = orc.rmsnorm(H, gamma, eps)
+    r = o.step(X, products=products)
+    assert np.array_equal(g.rstd.cpu().numpy().view(np.uint32), rstd.view(np.uint32))
+    compare_quant(g, X, r)
+    if products:
+        assert np.array_equal(acc.cpu().numpy(), r.acc)
+        err = check_y(g.Y.cpu().numpy(), r.Y)
+        say(f"[res] {tag} ok: count={r.count} flag={r.flag} max|dY|/max|Y|={err:.2e}")
+    return r
+
+
+def res_pair(orc, W, gamma, eps, tau, k_cap, M, lds=None):
+    g = ResLayer(W, gamma, eps, 8, tau, k_cap, M, lds=lds)
+    o = OracleLayer(W=W, bits=8, tau=tau, k_cap=k_cap, ldo=mixq.outlier_ld(k_cap), oracle=orc)
+    return g, o
+
+
+def split_case(H, seed):
+    """R and D whose fp16 sum is near H: D is a small update, R = H - D in fp16;
+    some entries of D cancel R exactly (H = 0) and some sums are subnormal."""
+    r = np.random.default_rng(seed)
+    D = (r.standard_normal(H.shape) * 0.3).astype(np.float16)
+    R = (H.astype(np.float64) - D.astype(np.float64)).astype(np.float16)
+    cancel = r.random(H.shape) < 0.01
+    D[cancel] = -R[cancel]
+    tiny = r.random(H.shape) < 0.01
+    R[tiny] = (r.integers(-512, 512, tiny.sum()) * 2.0 ** -24).astype(np.float16)
+    D[tiny] = (r.integers(-512, 512, tiny.sum()) * 2.0 ** -24).astype(np.float16)
+    return R, D
+
+
+@pytest.mark.parametrize("M,K,N,n_out,lds", [
+    (1, 64, 32, 0, None), (37, 512, 96, 3, None), (130, 4096, 256, 20, (4104, 4096, 4112)),
+    (64, 8192, 128, 82, None), (5, 32768, 64, 10, None),
+])
+def test_res_random(orc, M, K, N, n_out, lds):
+    Hs, gamma = make_case(M * 5 + K + n_out, M, K, n_out)
+    R, D = split_case(Hs, M + K)
+    W = (np.random.default_rng(K + N + 1).standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = res_pair(orc, W, gamma, 1e-5, 6.0, min(K, 128), M, lds=lds)
+    compare_res(orc, g, o, R, D, gamma, 1e-5, tag="rand")
+
+
+def test_res_sequence(orc):
+    """Decode-like steps through one state with row strides above K: the gate
+    fires on planted transients, so the re-quantize pass reads the written H."""
+    M, K, N = 24, 1024, 64
+    rng = np.random.default_rng(17)
+    pers = np.sort(rng.choice(K, 6, replace=False))
+    gamma = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    g, o = res_pair(orc, W, gamma, 1e-5, 6.0, 64, M, lds=(1032, 1040, 1096))
+    flags = []
+    for st in range(6):
+        H = rng.standard_normal((M, K))
+        H[:, pers] = rng.uniform(20, 100, (M, pers.size))
+        if st in (2, 4):
+            H[rng.integers(0, M, 3), rng.integers(0, K, 3)] = 90.0
+        R, D = split_case(H.astype(np.float16), st)
+        compare_res(orc, g, o, R, D, gamma, 1e-5, tag=f"step{st}")
+        flags.append(g.flag())
+    assert flags[0] == 1 and flags[1] == 0 and flags[2] == 1 and flags[4] == 1
+
+
+def test_res_full_size(orc):
+    """The prefill shape, set detected then cached, activation side only."""
+    Hs, gamma = make_case(0, 2048, 8192, 82)
+    R, D = split_case(Hs, 5)
+    W = (np.random.default_rng(0).standard_normal((64, 8192)) * 0.02).astype(np.float16)
+    g, o = res_pair(orc, W, gamma, 1e-5, 6.0, 256, 2048)
+    r = compare_res(orc, g, o, R, D, gamma, 1e-5, products=False, tag="full")
+    assert r.count >= 60
+    r = compare_res(orc, g, o, R, D, gamma, 1e-5, products=False, tag="full-cached")
+    assert r.flag == 0
