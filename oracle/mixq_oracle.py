@@ -122,6 +122,11 @@ class Oracle:
         """Returns H fp16; see ``residual_add`` below."""
         return residual_add(R, D)
 
+    # -- the operation after the layer ---------------------------------------------
+    def swiglu(self, Y):
+        """Returns silu(gate) * up in float64; see ``swiglu`` below."""
+        return swiglu(Y)
+
     # -- quantization ----------------------------------------------------------
     def quantize_act(self, X, in_set: np.ndarray, ldo: int):
         Xb = _bits(X)
@@ -190,6 +195,20 @@ class Oracle:
         if rc != 0:
             raise OverflowError("integer accumulator exceeds int32")
         return acc, Y
+
+
+def swiglu(Y):
+    """The gated activation that consumes a fused gate-and-up projection of a
+    LLaMA MLP: Y [M, 2I] holds the gate outputs in its first I columns and
+    the up outputs in the last I; the result is silu(gate) * up, with
+    silu(g) = g / (1 + e^-g), in float64 on the layer output as the oracle
+    computes it (a float tolerance applies to it, like to Y itself)."""
+    Y = np.asarray(Y, np.float64)
+    M, N2 = Y.shape
+    assert N2 % 2 == 0
+    g, u = Y[:, : N2 // 2], Y[:, N2 // 2:]
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
 
 
 def residual_add(R, D):

@@ -636,6 +636,31 @@ def pin_residual_add(o):
     assert 0 < (hb > base.astype(np.float64) + half.astype(np.float64)).sum() < 64
 
 
+def pin_swiglu(o):
+    """silu(g) * u against SciPy's logistic function (an independent
+    routine): silu(g) = g * expit(g); plus silu(0) = 0, up = 0 gives 0,
+    silu(g) - silu(-g) = g, large negative gates give -0 and no NaN, and the
+    halves are taken in the documented order (gate first)."""
+    from scipy.special import expit
+    r = _rng(93)
+    Y = r.standard_normal((7, 64)) * 4.0
+    Y[0, :32] = 0.0
+    Y[1, 32:] = 0.0
+    Y[2, :4] = [-1000.0, -80.0, 80.0, 1000.0]
+    got = o.swiglu(Y)
+    g, u = Y[:, :32], Y[:, 32:]
+    want = g * expit(g) * u
+    assert np.isfinite(got).all()
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-300)
+    assert (got[0] == 0).all() and (got[1] == 0).all()
+    x = r.standard_normal(50) * 5
+    s1 = o.swiglu(np.stack([x, np.ones(50)], axis=1).reshape(50, 2))[:, 0]
+    s2 = o.swiglu(np.stack([-x, np.ones(50)], axis=1).reshape(50, 2))[:, 0]
+    assert np.allclose(s1 - s2, x, rtol=1e-12, atol=1e-12)
+    # gate first: swapping the halves changes the result
+    assert not np.allclose(o.swiglu(np.concatenate([u, g], axis=1)), got)
+
+
 ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode,
             pin_set_bruteforce, pin_quant_error_bound, pin_nearest_code, pin_weight_bound,
             pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
@@ -643,4 +668,4 @@ ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
             pin_decode_sequence, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
             pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals,
-            pin_residual_add]
+            pin_residual_add, pin_swiglu]

@@ -123,10 +123,21 @@ RES_MUTANTS = [
 ]
 
 
+SWIGLU_MUTANTS = [
+    ("swiglu_halves_swapped", "g, u = Y[:, : N2 // 2], Y[:, N2 // 2:]",
+     "u, g = Y[:, : N2 // 2], Y[:, N2 // 2:]"),
+    ("swiglu_sign", "return g / (1.0 + np.exp(-g)) * u", "return g / (1.0 + np.exp(g)) * u"),
+    ("swiglu_no_gate_factor", "return g / (1.0 + np.exp(-g)) * u",
+     "return 1.0 / (1.0 + np.exp(-g)) * u"),
+]
+
+
 @pytest.mark.parametrize("fn,name,old,new",
                          [("rmsnorm", *m) for m in RMS_MUTANTS] +
-                         [("residual_add", *m) for m in RES_MUTANTS],
-                         ids=[m[0] for m in RMS_MUTANTS] + [m[0] for m in RES_MUTANTS])
+                         [("residual_add", *m) for m in RES_MUTANTS] +
+                         [("swiglu", *m) for m in SWIGLU_MUTANTS],
+                         ids=[m[0] for m in RMS_MUTANTS] + [m[0] for m in RES_MUTANTS] +
+                         [m[0] for m in SWIGLU_MUTANTS])
 def test_prologue_mutant_is_caught(fn, name, old, new):
     import inspect
     import textwrap
