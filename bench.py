@@ -257,6 +257,74 @@ def run_fused_norm(wl, steps: int, warmup: int, eps: float = 1e-5):
                        "the gate fires)"}
 
 
+def run_swiglu(wl, steps: int, warmup: int):
+    """The workload's weight read as a fused gate-and-up projection ([W_gate;
+    W_up], I = N/2): the GEMM with the SwiGLU epilogue (fp16 silu(gate) * up,
+    mixq_gemm_ex) against the same GEMM writing fp32 followed by torch's
+    silu, multiply and cast to fp16."""
+    import torch
+    import torch.nn.functional as F
+    from mixed_precision_quantized_amax_amd import mixq, workloads
+
+    dev = torch.device("cuda", 0)
+    W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
+    X = torch.from_numpy(workloads.make_activation(wl)).to(dev)
+    k_cap = 256
+    wq_bytes = wl.N * wl.K * wl.bits // 8
+    copies = int(min(8, max(2, math.ceil(CACHE_DEFEAT_BYTES / wq_bytes))))
+    st = mixq.OutlierState.create(wl.K, k_cap, dev)
+    packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev, gated=True)
+             for _ in range(copies)]
+    for p in packs:
+        mixq.pack_weight(W, st, p, mixq.PACK_FULL)
+    ld = mixq.outlier_ld(k_cap)
+    Xq = torch.empty(wl.M, wl.K, dtype=torch.int8, device=dev)
+    sx = torch.empty(wl.M, dtype=torch.float32, device=dev)
+    Xo = torch.zeros(wl.M * ld, dtype=torch.float16, device=dev)
+    mixq.quantize_act(X, wl.tau, st, Xq, sx, Xo)
+    for p in packs:
+        mixq.pack_weight(W, st, p, mixq.PACK_OUTLIER_COLS)
+    I = wl.N // 2
+    Yh = torch.empty(wl.M, I, dtype=torch.float16, device=dev)
+    Y32 = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
+    ws = mixq.gemm_workspace(wl.M, wl.N, wl.K, wl.bits, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused(i):
+        mixq.gemm_ex(Xq, sx, Xo, st, packs[i % copies], Yh, mixq.OUT_SWIGLU_F16, None, ws)
+
+    def plain(i):
+        mixq.gemm_ex(Xq, sx, Xo, st, packs[i % copies], Y32, mixq.OUT_F32, None, ws)
+
+    def unfused(i):
+        plain(i)
+        Yh.copy_(F.silu(Y32[:, :I]) * Y32[:, I:])
+
+    for i in range(warmup):
+        fused(i)
+        unfused(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("fused", fused), ("plain", plain), ("unfused", unfused)):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps * 1e3
+    tops = wl.ops / (res["fused"] * 1e-6) / 1e12
+    log(f"[bench] SwiGLU GEMM {res['fused']:.1f} us ({tops:.0f} TOPS); fp32 GEMM "
+        f"{res['plain']:.1f} us; fp32 GEMM + torch silu*up {res['unfused']:.1f} us")
+    return {"gemm_swiglu_us": round(res["fused"], 2), "gemm_swiglu_tops": round(tops, 1),
+            "gemm_f32_us": round(res["plain"], 2),
+            "unfused_us": round(res["unfused"], 2),
+            "unfused": "the same GEMM writing fp32, then torch silu(gate) * up cast to fp16",
+            "shape": f"M={wl.M}, K={wl.K}, gate and up rows {I} each (N = {wl.N})"}
+
+
 def run_decode_sequence(wl, repeats: int = 3):
     """The outlier-locality decode sequence: every step runs the whole layer on
     a new batch, the cached set carrying over; the set is re-detected only on
@@ -416,6 +484,7 @@ def main():
                      "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
     }
     out["fused_rmsnorm_act"] = run_fused_norm(wl, args.steps, min(args.warmup, 50))
+    out["swiglu_gate_up"] = run_swiglu(wl, max(20, args.steps // 2), min(args.warmup, 50))
     if args.all:
         others = {}
         for name in ("llama7b_up", "llama70b_up", "prefill_w4"):

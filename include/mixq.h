@@ -76,6 +76,11 @@ enum {
 #define MIXQ_FLAG_OVERFLOW 2         /* gate fired, but |set| would exceed k_cap;
                                         set left unchanged                      */
 
+/* output modes of mixq_gemm_ex */
+#define MIXQ_OUT_F32 0               /* Y fp32 [M, N]                            */
+#define MIXQ_OUT_SWIGLU_F16 1        /* gated weight: Y fp16 [M, N/2] =
+                                        silu(gate) * up                          */
+
 /* mixq_pack_weight modes */
 #define MIXQ_PACK_FULL 0             /* quantize all of W and gather outliers   */
 #define MIXQ_PACK_OUTLIER_COLS 1     /* only re-gather the outlier columns, and
@@ -120,6 +125,13 @@ typedef struct mixq_weight {
     int32_t bits;      /* 8 or 4                                                  */
     int64_t N, K;
     int32_t k_cap;     /* must equal the k_cap of the states it is used with      */
+    int32_t gated;     /* 0: rows of W in order.  1: W = [W_gate; W_up] ([2I, K],
+                          I = N/2, N a multiple of 64), packed with 32-row blocks
+                          of gate and up rows interleaved (packed row p holds W
+                          row 32*(p/64) + p%64 for p%64 < 32, else
+                          I + 32*(p/64) + p%64 - 32); wq, s_w and w_out all
+                          follow the packed order.  Needed by
+                          MIXQ_OUT_SWIGLU_F16.                                    */
 } mixq_weight;
 
 /* ---- size helpers (pure host functions) ---------------------------------- */
@@ -243,8 +255,11 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *          w_out only, decided on the device (no host sync): it runs when
  *          *state->count differs from *w->k_out, and is a no-op otherwise.
  *          Call it after each mixq_quantize_act and before mixq_gemm.
- *   w      the packed weight; w->N, w->K, w->bits, w->k_cap must match
- * Errors: as mixq_quantize_act.
+ *   w      the packed weight; w->N, w->K, w->bits, w->k_cap must match;
+ *          w->gated selects the row order (see mixq_weight) and must be the
+ *          same in the FULL call and every OUTLIER_COLS call
+ * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for w->gated not 0
+ *         or 1, MIXQ_ERR_UNSUPPORTED_SHAPE for a gated N not a multiple of 64.
  */
 int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
                      const mixq_act_state *state, int32_t mode, const mixq_weight *w,
@@ -298,6 +313,31 @@ int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
 int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
                  int64_t ldy, int32_t *acc_debug, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * mixq_gemm_ex -- mixq_gemm_ws with a choice of output.  MIXQ_OUT_F32 is
+ * mixq_gemm_ws.  MIXQ_OUT_SWIGLU_F16 is for the fused gate-and-up
+ * projection of a LLaMA MLP (the gated linear layer the FP6 explainer's
+ * section 3 runs as one double-output kernel): w must be packed gated, and
+ * the epilogue writes, for each token m and output j < N/2,
+ *   Y[m, j] = fp16( silu(g) * u ),  silu(g) = g / (1 + e^-g),
+ * where g and u are the layer outputs (dequantized integer product plus
+ * outlier product, in fp32) of gate row j and up row j -- the same values
+ * MIXQ_OUT_F32 writes, taken in pairs in the epilogue.  The fp32 gate and up
+ * outputs never reach memory.
+ *
+ *   Y         MIXQ_OUT_F32: fp32 [M, ldy], ldy >= N.
+ *             MIXQ_OUT_SWIGLU_F16: fp16 [M, ldy], ldy >= N/2.
+ *   out_mode  MIXQ_OUT_F32 or MIXQ_OUT_SWIGLU_F16
+ *   acc_debug as mixq_gemm, in the packed (interleaved) column order
+ * Other arguments: as mixq_gemm_ws (ws may be NULL).
+ * Errors: as mixq_gemm; MIXQ_ERR_INVALID_ARG also for an unknown out_mode,
+ *         MIXQ_OUT_SWIGLU_F16 with a weight not packed gated, or ldy < N/2.
+ */
+int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
+                 const mixq_act_state *state, const mixq_weight *w, int64_t M, void *Y,
+                 int64_t ldy, int32_t out_mode, int32_t *acc_debug, void *ws, size_t ws_bytes,
+                 void *stream);
 
 /* Workspace bytes mixq_gemm_ws needs to split this product on a device with
  * 256 compute units (MI355X): 4096 bytes of tile counters plus two 64 KiB

@@ -64,6 +64,7 @@ struct GemmArgs {
     int32_t ksplit;
     int32_t* sync;  // [tiles] arrival counters, zero between calls
     int32_t* part;  // [tiles][2] int32 partial tiles
+    int32_t out_mode;  // MIXQ_OUT_F32, or MIXQ_OUT_SWIGLU_F16 (Y then holds fp16)
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -900,6 +901,39 @@ void gemm_kernel(GemmArgs a) {
         }
     }
 
+    // ---- SwiGLU output: fp16 silu(gate) * up ------------------------------------------
+    // A gated weight interleaves 32-row blocks of gate and up rows, and every
+    // wave's column range is a multiple of 64, so fragments 2jj and 2jj+1 of a
+    // lane hold gate and up of the same (token, output) pairs.
+    if (a.out_mode == MIXQ_OUT_SWIGLU_F16) {
+        const int ldyh = (int)a.ldy * 2;  // bytes per fp16 row
+        const __amdgpu_buffer_rsrc_t rH =
+            make_rsrc(reinterpret_cast<const uint8_t*>(a.Y) + (int64_t)m0 * ldyh,
+                      (int64_t)rows_a * ldyh);
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::kFN / 2; ++jj) {
+                const int pc = n0 + wn * C::kWTN + jj * 64;  // packed column of the gate block
+                const int oc = pc / 2 + fr;                   // output column
+                const int r0 = wm * C::kWTM + i * 32 + 4 * fh;
+                if (pc + fr < a.N) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int rl = r0 + 8 * (e >> 2) + (e & 3);
+                        const float g = __int_as_float(acc[i][2 * jj][e]);
+                        const float u = __int_as_float(acc[i][2 * jj + 1][e]);
+                        const float y = g / (1.0f + __expf(-g)) * u;
+                        if (rl < rows_a)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                __builtin_bit_cast(unsigned short, (_Float16)y), rH,
+                                rl * ldyh + oc * 2, 0, 0);
+                    }
+                }
+            }
+        return;
+    }
+
     // ---- store Y (fp32) ---------------------------------------------------------------
     // Buffer stores relative to the tile's first row: 32-bit offsets, and rows
     // past M fall outside the buffer as well as failing the explicit check.
@@ -1024,10 +1058,15 @@ namespace {
 
 int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
               const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,
-              int64_t ldy, int32_t* acc_debug, void* ws, size_t ws_bytes, void* stream) {
+              int64_t ldy, int32_t* acc_debug, void* ws, size_t ws_bytes, void* stream,
+              int32_t out_mode = MIXQ_OUT_F32) {
     if (!Xq || !s_x || !state || !w || !Y) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !w->wq || !w->s_w) return MIXQ_ERR_INVALID_ARG;
-    if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < w->N) return MIXQ_ERR_INVALID_ARG;
+    if (out_mode != MIXQ_OUT_F32 && out_mode != MIXQ_OUT_SWIGLU_F16) return MIXQ_ERR_INVALID_ARG;
+    if (out_mode == MIXQ_OUT_SWIGLU_F16 && (w->gated != 1 || w->N % 64 != 0))
+        return MIXQ_ERR_INVALID_ARG;
+    if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < (out_mode == MIXQ_OUT_F32 ? w->N : w->N / 2))
+        return MIXQ_ERR_INVALID_ARG;
     if (w->bits != 8 && w->bits != 4) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap < 0 || state->k_cap > w->K || w->k_cap != state->k_cap)
         return MIXQ_ERR_INVALID_ARG;
@@ -1059,6 +1098,7 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.ksplit = 1;
     a.sync = nullptr;
     a.part = nullptr;
+    a.out_mode = out_mode;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
     const int f = forced_cfg();
@@ -1090,4 +1130,12 @@ extern "C" int mixq_gemm_ws(const int8_t* Xq, const float* s_x, const uint16_t* 
                             float* Y, int64_t ldy, int32_t* acc_debug, void* ws, size_t ws_bytes,
                             void* stream) {
     return mixq::gemm_impl(Xq, s_x, X_out, state, w, M, Y, ldy, acc_debug, ws, ws_bytes, stream);
+}
+
+extern "C" int mixq_gemm_ex(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
+                            const mixq_act_state* state, const mixq_weight* w, int64_t M, void* Y,
+                            int64_t ldy, int32_t out_mode, int32_t* acc_debug, void* ws,
+                            size_t ws_bytes, void* stream) {
+    return mixq::gemm_impl(Xq, s_x, X_out, state, w, M, static_cast<float*>(Y), ldy, acc_debug,
+                           ws, ws_bytes, stream, out_mode);
 }

@@ -20,17 +20,27 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
+// Source row of packed row n: n itself, or for a gated weight ([W_gate;
+// W_up], N = 2I) the 32-row blocks of gate and up rows interleaved, so that
+// the epilogue finds gate j and up j in neighbouring fragments.
+__device__ __forceinline__ int64_t src_row(int64_t n, int64_t N, int gated) {
+    if (!gated) return n;
+    const int64_t blk = n >> 6, within = n & 63;
+    return within < 32 ? blk * 32 + within : N / 2 + blk * 32 + (within - 32);
+}
+
 template <int CPT, int BITS>
 __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_t* __restrict__ W,
                                                                     int64_t N, int32_t K,
                                                                     void* __restrict__ wq,
-                                                                    float* __restrict__ s_w) {
+                                                                    float* __restrict__ s_w,
+                                                                    int gated) {
     __shared__ float red[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nchunks = K / 8;
     constexpr float kQ = BITS == 8 ? 127.0f : 7.0f;
     for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-        const uint16_t* wr = W + n * (int64_t)K;
+        const uint16_t* wr = W + src_row(n, N, gated) * (int64_t)K;
         uint4 v[CPT];
         float am = 0.0f;
 #pragma unroll
@@ -107,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* _
                                                                const int32_t* __restrict__ count_p,
                                                                uint16_t* __restrict__ w_out,
                                                                int32_t ld_out, int32_t* k_out,
-                                                               int force) {
+                                                               int force, int gated) {
     const int count = *count_p;
     if (!force && k_out[blockIdx.x] == count) return;
     const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* _
     for (int64_t t = threadIdx.x; t < total; t += kThreads) {
         const int64_t n = blockIdx.x + (t / kpad) * G;
         const int j = (int)(t % kpad);
-        w_out[n * ld_out + j] = j < count ? W[n * (int64_t)K + idx[j]] : (uint16_t)0;
+        w_out[n * ld_out + j] = j < count ? W[src_row(n, N, gated) * (int64_t)K + idx[j]] : (uint16_t)0;
     }
     __syncthreads();
     if (threadIdx.x == 0) k_out[blockIdx.x] = count;
@@ -129,10 +139,10 @@ int launch_quant(const uint16_t* W, int64_t N, int32_t K, int bits, const mixq_w
     const int grid = (int)(N < 4096 ? N : 4096);
     if (bits == 8)
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 8>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w);
+                           N, K, w->wq, w->s_w, w->gated);
     else
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w);
+                           N, K, w->wq, w->s_w, w->gated);
     return launch_status();
 }
 
@@ -153,7 +163,9 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     if (state->k_cap < 0 || state->k_cap > K) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap > 0 && (!w->w_out || !state->idx)) return MIXQ_ERR_INVALID_ARG;
     if (!state->count) return MIXQ_ERR_INVALID_ARG;
+    if (w->gated != 0 && w->gated != 1) return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (w->gated && N % 64 != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (((uintptr_t)W & 15u) != 0 || ((uintptr_t)w->wq & 15u) != 0)
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (N > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;
@@ -175,6 +187,6 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     const int grid = (int)(N < MIXQ_GATHER_SLOTS ? N : MIXQ_GATHER_SLOTS);
     hipLaunchKernelGGL(gather_cols_kernel, dim3(grid), dim3(kThreads), 0, st, W, N, (int32_t)K,
                        state->idx, state->count, w->w_out, ld_out, w->k_out,
-                       mode == MIXQ_PACK_FULL ? 1 : 0);
+                       mode == MIXQ_PACK_FULL ? 1 : 0, w->gated);
     return launch_status();
 }

@@ -23,6 +23,8 @@ FLAG_FIRED = 1
 FLAG_OVERFLOW = 2
 PACK_FULL = 0
 PACK_OUTLIER_COLS = 1
+OUT_F32 = 0
+OUT_SWIGLU_F16 = 1
 OUTLIER_ALIGN = 32
 K_MULTIPLE = 64
 GATHER_SLOTS = 256
@@ -43,7 +45,7 @@ class ActState(ctypes.Structure):
 class Weight(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
                 ("k_out", ctypes.c_void_p), ("bits", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("k_cap", ctypes.c_int32)]
+                ("k_cap", ctypes.c_int32), ("gated", ctypes.c_int32)]
 
 
 _lib = None
@@ -86,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.mixq_gemm_ws.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
                                    P, I64, P, P, ctypes.c_size_t, P]
         L.mixq_gemm_ws.restype = ctypes.c_int
+        L.mixq_gemm_ex.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
+                                   P, I64, I32, P, P, ctypes.c_size_t, P]
+        L.mixq_gemm_ex.restype = ctypes.c_int
         L.mixq_gemm_workspace_bytes.argtypes = [I64, I64, I64, I32]
         L.mixq_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.mixq_status_string.argtypes = [ctypes.c_int]
@@ -157,9 +162,11 @@ class PackedWeight:
     s_w: torch.Tensor
     w_out: torch.Tensor
     k_out: torch.Tensor
+    gated: int = 0  # 1: W = [W_gate; W_up], packed with 32-row blocks interleaved
 
     @classmethod
-    def create(cls, N: int, K: int, bits: int, k_cap: int, device="cuda") -> "PackedWeight":
+    def create(cls, N: int, K: int, bits: int, k_cap: int, device="cuda",
+               gated: bool = False) -> "PackedWeight":
         nbytes = int(lib().mixq_packed_weight_bytes(N, K, bits))
         if nbytes == 0:
             raise ValueError("invalid weight shape or bits")
@@ -168,11 +175,12 @@ class PackedWeight:
                    wq=torch.empty(nbytes, dtype=torch.uint8, device=device),
                    s_w=torch.empty(N, dtype=torch.float32, device=device),
                    w_out=torch.zeros(max(N * ld, 1), dtype=torch.float16, device=device),
-                   k_out=torch.zeros(GATHER_SLOTS, dtype=torch.int32, device=device))
+                   k_out=torch.zeros(GATHER_SLOTS, dtype=torch.int32, device=device),
+                   gated=int(bool(gated)))
 
     def c(self) -> Weight:
         return Weight(self.wq.data_ptr(), self.s_w.data_ptr(), self.w_out.data_ptr(),
-                      self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap)
+                      self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap, self.gated)
 
     def codes_view(self) -> torch.Tensor:
         """int8 [N, K] (bits 8) or packed uint8 [N, K/2] (bits 4) view of wq."""
@@ -272,6 +280,21 @@ def gemm(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None, state:
                                 ctypes.byref(w), M, _ptr(Y), Y.stride(0), _ptr(acc_debug),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(Y.device))
         _check("mixq_gemm_ws", rc)
+
+
+def gemm_ex(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None,
+            state: OutlierState, pw: PackedWeight, Y: torch.Tensor, out_mode: int,
+            acc_debug: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> None:
+    """mixq_gemm_ex: OUT_F32 (Y fp32 [M, >= N]) or OUT_SWIGLU_F16 (a gated
+    weight; Y fp16 [M, >= N/2] = silu(gate) * up)."""
+    M = Xq.shape[0]
+    st = state.c()
+    w = pw.c()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = lib().mixq_gemm_ex(_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(st), ctypes.byref(w),
+                            M, _ptr(Y), Y.stride(0), int(out_mode), _ptr(acc_debug), _ptr(ws),
+                            nbytes, _stream(Y.device))
+    _check("mixq_gemm_ex", rc)
 
 
 class LayerStep:

@@ -120,16 +120,18 @@ def test_valid_arguments_need_a_device():
     assert mixq.lib().mixq_check_device() == 4
 
 
-def _weight(N=16, K=64, bits=8, k_cap=8, **null):
+def _weight(N=16, K=64, bits=8, k_cap=8, gated=0, **null):
     vals = dict(wq=0x100000, s_w=0x200000, w_out=0x300000, k_out=0x400000)
     vals.update(null)
-    return mixq.Weight(vals["wq"], vals["s_w"], vals["w_out"], vals["k_out"], bits, N, K, k_cap)
+    return mixq.Weight(vals["wq"], vals["s_w"], vals["w_out"], vals["k_out"], bits, N, K, k_cap,
+                       gated)
 
 
 @pytest.mark.parametrize("args,code", [
     (dict(bits=5), 1), (dict(mode=7), 1), (dict(N=0), 1), (dict(w=_weight(N=8)), 1),
     (dict(w=_weight(bits=4)), 1), (dict(w=_weight(k_cap=4)), 1), (dict(w=_weight(wq=0)), 1),
     (dict(w=_weight(k_out=0)), 1), (dict(K=96, w=_weight(K=96)), 2),
+    (dict(w=_weight(gated=2)), 1), (dict(w=_weight(gated=1)), 2),          # gated: N % 64
 ])
 def test_pack_weight_validation(args, code):
     N = args.get("N", 16)
@@ -188,3 +190,35 @@ def test_gemm_ws_validation():
     if not torch.cuda.is_available():
         assert f(*args, ctypes.c_void_p(0x60000), 1 << 20, None) == 4
         assert f(*args, None, 0, None) == 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=5), 1),                                   # unknown output mode
+    (dict(mode=1), 1),                                   # SwiGLU needs a gated weight
+    (dict(mode=1, w=_weight(N=64, gated=1), ldy=31), 1),  # fp16 row shorter than N/2
+    (dict(mode=0, w=_weight(N=64, gated=1), ldy=32), 1),  # fp32 row shorter than N
+])
+def test_gemm_ex_validation(kw, code):
+    w = kw.get("w", _weight())
+    st = _state()
+    rc = mixq.lib().mixq_gemm_ex(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000),
+                                 ctypes.c_void_p(0x40000), ctypes.byref(st), ctypes.byref(w), 4,
+                                 ctypes.c_void_p(0x50000), kw.get("ldy", 16), kw["mode"], None,
+                                 None, 0, None)
+    assert rc == code
+
+
+def test_gemm_ex_valid_arguments_need_a_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = _state()
+    wg = _weight(N=64, gated=1)
+    assert mixq.lib().mixq_pack_weight(ctypes.c_void_p(0x900000), 64, 64, 8, ctypes.byref(st), 0,
+                                       ctypes.byref(wg), None) == 4
+    w = _weight(N=64, gated=1)
+    f = mixq.lib().mixq_gemm_ex
+    for mode, ldy in ((1, 32), (0, 64)):
+        assert f(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+                 ctypes.byref(st), ctypes.byref(w), 4, ctypes.c_void_p(0x50000), ldy, mode, None,
+                 None, 0, None) == 4
