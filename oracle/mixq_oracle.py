@@ -122,6 +122,10 @@ class Oracle:
         """Returns H fp16; see ``residual_add`` below."""
         return residual_add(R, D)
 
+    def progressive_quantize_weight(self, W, group: int = 128):
+        """See ``progressive_quantize_weight`` below."""
+        return progressive_quantize_weight(W, group)
+
     # -- the operation after the layer ---------------------------------------------
     def swiglu(self, Y):
         """Returns silu(gate) * up in float64; see ``swiglu`` below."""
@@ -195,6 +199,72 @@ class Oracle:
         if rc != 0:
             raise OverflowError("integer accumulator exceeds int32")
         return acc, Y
+
+
+GROUP = 128          # progressive INT4: channels per group along K
+Q1_PROGRESSIVE = 119  # protective INT8 range of the first level (derived below)
+
+
+def progressive_quantize_weight(W, group: int = GROUP):
+    """Two-level (progressive) group quantization of a weight so that every
+    product runs on INT8 units -- the QServe page, section on progressive
+    group quantization ("渐进量化"): per output channel an fp16-style scale
+    takes W to 8 bits, then each group of ``group`` consecutive channels of
+    those 8-bit values is quantized to 4 bits with its own scale and zero,
+    and the main loop rebuilds 8-bit values from the 4-bit ones.
+
+    The page gives no constants; the reading taken here, with integer steps
+    so that the result is unique:
+      level 1:  alpha = max_k |W[n,k]|;  s1 = alpha / Q1, rho = Q1 / alpha
+                (binary32 divisions; alpha = 0 gives 1 and 1);
+                q8 = clamp(rne(float(w) * rho), -Q1, Q1)     (binary32 product)
+      level 2, per group: lo = min(0, min q8), hi = max(0, max q8) (zero kept
+                in range, so the zero point is a 4-bit value);
+                s2 = max(1, ceil((hi - lo) / 15));  z = rne(-lo / s2);
+                u = clamp(rne(q8 / s2) + z, 0, 15)   (exact rational rounding)
+      rebuilt:  q8' = (u - z) * s2, the INT8 code the product uses.
+    Q1 = 119 is the largest first-level range for which no rebuilt code leaves
+    INT8 (the page's "no overflow" property): |q8'| <= |rne(q8/s2)| * s2 <=
+    Q1 + s2/2 with s2 <= ceil(2*Q1/15) = 16, so 119 + 8 = 127, while Q1 = 120
+    allows 120 + 8 = 128.
+
+    Returns (q8p int8 [N, K] rebuilt codes, s1 fp32 [N], u uint8 [N, K]
+    4-bit values, s2 uint8 [N, K/group], z uint8 [N, K/group], q8 int8 [N, K]
+    first-level codes).
+    """
+    Wh = W.view(np.float16) if W.dtype == np.uint16 else np.asarray(W, np.float16)
+    N, K = Wh.shape
+    assert K % group == 0
+    Q1 = Q1_PROGRESSIVE
+    Wf = Wh.astype(np.float32)
+    alpha = np.abs(Wf).max(axis=1)
+    s1 = np.ones(N, np.float32)
+    rho = np.ones(N, np.float32)
+    nz = alpha != 0
+    s1[nz] = alpha[nz] / np.float32(Q1)
+    rho[nz] = np.float32(Q1) / alpha[nz]
+    q8 = np.clip(np.rint(Wf * rho[:, None]), -Q1, Q1).astype(np.int64)  # rint: ties to even
+    G = K // group
+    g8 = q8.reshape(N, G, group)
+    lo = np.minimum(g8.min(axis=2), 0)
+    hi = np.maximum(g8.max(axis=2), 0)
+    s2 = np.maximum(1, -((lo - hi) // 15))          # ceil((hi - lo) / 15)
+    z = _rne_div(-lo, s2)
+    u = np.clip(_rne_div(g8, s2[:, :, None]) + z[:, :, None], 0, 15)
+    q8p = (u - z[:, :, None]) * s2[:, :, None]
+    assert np.abs(q8p).max(initial=0) <= 127
+    return (q8p.reshape(N, K).astype(np.int8), s1, u.reshape(N, K).astype(np.uint8),
+            s2.astype(np.uint8), z.astype(np.uint8), q8.astype(np.int8))
+
+
+def _rne_div(a, b):
+    """Round half to even of the exact quotient a / b of integers (b > 0)."""
+    a = np.asarray(a, np.int64)
+    b = np.asarray(b, np.int64)
+    q = a // b                     # floor
+    r2 = 2 * (a - q * b)           # twice the remainder, in [0, 2b)
+    up = (r2 > b) | ((r2 == b) & (q % 2 == 1))
+    return q + up
 
 
 def swiglu(Y):

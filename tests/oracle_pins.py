@@ -661,6 +661,79 @@ def pin_swiglu(o):
     assert not np.allclose(o.swiglu(np.concatenate([u, g], axis=1)), got)
 
 
+def _progressive_rows(seed):
+    """Weight rows for the progressive pins: N(0, 0.02) rows, a row with one
+    large value (most groups then use a few codes), rows of constants (all
+    groups identical, one positive and one negative), and rows built so that
+    groups hit both ends of the first-level range."""
+    r = _rng(seed, 95)
+    K = 256
+    W = r.standard_normal((6, K)) * 0.02
+    W[1, 5] = 0.9
+    W[2, :] = 0.01
+    W[3, :] = -0.013
+    W[4, ::2] = 0.05
+    W[4, 1::2] = -0.05
+    W[5, :128] = np.linspace(-0.07, 0.07, 128)
+    return W.astype(np.float16)
+
+
+def pin_progressive_levels(o):
+    """Progressive INT4.  Level 1: the codes meet the quantization bound
+    |w - q8 * s1| <= s1 (1/2 + slack) with the range 119, which each nonzero
+    row's maximum reaches.  Level 2, by brute force on every group of those
+    codes: s2 is the smallest integer >= 1 whose 15 steps span
+    [min(0, min q8), max(0, max q8)]; z is the zero point in [0, 15] nearest
+    to -min/s2 (ties to even); each u is the 4-bit value whose rebuilt code
+    (u - z) * s2 is nearest to q8, ties to the even (u - z); rebuilt codes stay
+    within INT8."""
+    for seed in range(3):
+        W = _progressive_rows(seed)
+        q8p, s1, u, s2, z, q8 = o.progressive_quantize_weight(W)
+        N, K = W.shape
+        w = W.astype(np.float64)
+        q8 = q8.astype(np.int64)
+        for n in range(N):
+            assert np.abs(q8[n]).max() <= 119
+            if np.abs(w[n]).max() == 0:
+                assert (q8[n] == 0).all() and s1[n] == 1
+                continue
+            err = np.abs(w[n] - q8[n] * float(s1[n]))
+            assert err.max() <= float(s1[n]) * (0.5 + HALF_STEP_SLACK)
+            assert np.abs(q8[n]).max() == 119
+            for gi in range(K // 128):
+                sl = slice(gi * 128, (gi + 1) * 128)
+                S2, Z = int(s2[n, gi]), int(z[n, gi])
+                rec = q8p[n, sl].astype(np.int64)
+                uu = u[n, sl].astype(np.int64)
+                assert 0 <= Z <= 15 and 1 <= S2 <= 16 and (uu >= 0).all() and (uu <= 15).all()
+                assert (rec == (uu - Z) * S2).all() and np.abs(rec).max() <= 127
+                lo = min(0, int(q8[n, sl].min()))
+                hi = max(0, int(q8[n, sl].max()))
+                best_s = next(t for t in range(1, 17) if 15 * t >= hi - lo)
+                assert S2 == best_s, (n, gi, S2, best_s)
+                cands = [(abs(Fraction(-lo, S2) - zz), zz % 2, zz) for zz in range(16)]
+                assert Z == min(cands)[2], (n, gi)
+                for k, qv in zip(range(128), q8[n, sl]):
+                    cu = [(abs((c - Z) * S2 - int(qv)), (c - Z) % 2, c) for c in range(16)]
+                    assert uu[k] == min(cu)[2], (n, gi, k, int(qv))
+
+
+def pin_progressive_no_overflow(o):
+    """Groups at both ends of the first-level range, for every scale the range
+    allows: no rebuilt code leaves [-127, 127], and the maximum reaches 119 +
+    s2/2 rounded to a multiple of s2 at most."""
+    r = _rng(96)
+    worst = 0
+    for trial in range(40):
+        W = (r.standard_normal((2, 128)) * 0.01).astype(np.float64)
+        W[:, 0] = 0.1 * r.choice([-1, 1], 2)
+        W[:, 1] = -W[:, 0] * r.uniform(0, 1, 2)
+        q8p = o.progressive_quantize_weight(W.astype(np.float16))[0]
+        worst = max(worst, int(np.abs(q8p.astype(np.int64)).max()))
+    assert worst <= 127
+
+
 ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode,
             pin_set_bruteforce, pin_quant_error_bound, pin_nearest_code, pin_weight_bound,
             pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
@@ -668,4 +741,4 @@ ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
             pin_decode_sequence, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
             pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals,
-            pin_residual_add, pin_swiglu]
+            pin_residual_add, pin_swiglu, pin_progressive_levels, pin_progressive_no_overflow]

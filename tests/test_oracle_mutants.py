@@ -132,12 +132,24 @@ SWIGLU_MUTANTS = [
 ]
 
 
+PROG_MUTANTS = [
+    ("prog_range_127", "Q1 = Q1_PROGRESSIVE", "Q1 = 127"),
+    ("prog_zero_not_in_range", "lo = np.minimum(g8.min(axis=2), 0)", "lo = g8.min(axis=2)"),
+    ("prog_scale_floor", "s2 = np.maximum(1, -((lo - hi) // 15))",
+     "s2 = np.maximum(1, (hi - lo) // 15)"),
+    ("prog_code_floor", "u = np.clip(_rne_div(g8, s2[:, :, None]) + z[:, :, None], 0, 15)",
+     "u = np.clip(g8 // s2[:, :, None] + z[:, :, None], 0, 15)"),
+    ("prog_zero_sign", "z = _rne_div(-lo, s2)", "z = _rne_div(lo, s2) % 16"),
+]
+
+
 @pytest.mark.parametrize("fn,name,old,new",
                          [("rmsnorm", *m) for m in RMS_MUTANTS] +
                          [("residual_add", *m) for m in RES_MUTANTS] +
-                         [("swiglu", *m) for m in SWIGLU_MUTANTS],
+                         [("swiglu", *m) for m in SWIGLU_MUTANTS] +
+                         [("progressive_quantize_weight", *m) for m in PROG_MUTANTS],
                          ids=[m[0] for m in RMS_MUTANTS] + [m[0] for m in RES_MUTANTS] +
-                         [m[0] for m in SWIGLU_MUTANTS])
+                         [m[0] for m in SWIGLU_MUTANTS] + [m[0] for m in PROG_MUTANTS])
 def test_prologue_mutant_is_caught(fn, name, old, new):
     import inspect
     import textwrap
@@ -148,7 +160,8 @@ def test_prologue_mutant_is_caught(fn, name, old, new):
 
     src = textwrap.dedent(inspect.getsource(getattr(mixq_oracle, fn)))
     assert src.count(old) == 1, f"mutation site not found: {old!r}"
-    ns = {"np": np}
+    ns = {"np": np, "Q1_PROGRESSIVE": mixq_oracle.Q1_PROGRESSIVE, "_rne_div": mixq_oracle._rne_div,
+          "GROUP": mixq_oracle.GROUP}
     exec(compile(src.replace(old, new), f"<{name}>", "exec"), ns)
 
     class Mutant(Oracle):
@@ -158,7 +171,8 @@ def test_prologue_mutant_is_caught(fn, name, old, new):
     o = Mutant()
     failed = []
     for pin in oracle_pins.ALL_PINS:
-        if fn not in pin.__name__ and not (fn == "rmsnorm" and "rmsnorm" in pin.__name__):
+        key = "progressive" if fn == "progressive_quantize_weight" else fn
+        if key not in pin.__name__:
             continue
         try:
             pin(o)
