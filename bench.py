@@ -69,19 +69,21 @@ def algorithmic_bytes(wl, k: int) -> int:
             + 2 * kp * (wl.M + wl.N) + 4 * wl.M * wl.N)
 
 
-def run_gpu(wl, steps: int, warmup: int):
+def run_gpu(wl, steps: int, warmup: int, group: int = 0):
+    """group: 0, or the progressive INT4 group size (INT4 workloads)."""
     import torch
     from mixed_precision_quantized_amax_amd import mixq, workloads
 
     dev = torch.device("cuda", 0)
-    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits}")
+    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits} group={group}")
     W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
     X0 = torch.from_numpy(workloads.make_activation(wl)).to(dev)
     k_cap = 256
     wq_bytes = wl.N * wl.K * wl.bits // 8
     copies = int(min(8, max(2, math.ceil(CACHE_DEFEAT_BYTES / (wq_bytes + 3 * wl.M * wl.K)))))
     state = mixq.OutlierState.create(wl.K, k_cap, dev)
-    packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev) for _ in range(copies)]
+    packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev, group=group)
+             for _ in range(copies)]
     for p in packs:
         mixq.pack_weight(W, state, p, mixq.PACK_FULL)
     # activation copies: the same values in different buffers
@@ -495,6 +497,15 @@ def main():
                             "gemm_us": round(r2["gemm_ms"] * 1e3, 1),
                             "act_quant_us": round(r2["act_ms"] * 1e3, 1),
                             "ms_per_step": round(r2["ms_step"], 4)}
+        w4 = workloads.WORKLOADS["prefill_w4"]
+        r4 = run_gpu(w4, max(10, args.steps // 2), args.warmup, group=128)
+        others["prefill_w4_progressive"] = {
+            "step_tops": round(w4.ops / (r4["ms_step"] / 1e3) / 1e12, 1),
+            "gemm_tops": round(w4.ops / (r4["gemm_ms"] / 1e3) / 1e12, 1),
+            "gemm_us": round(r4["gemm_ms"] * 1e3, 1),
+            "act_quant_us": round(r4["act_ms"] * 1e3, 1),
+            "ms_per_step": round(r4["ms_step"], 4),
+            "weights": "progressive group-wise INT4, groups of 128 (rebuilt to INT8 in the loader)"}
         dwl = workloads.WORKLOADS["decode_seq"]
         d = run_decode_sequence(dwl)
         others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),

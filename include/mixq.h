@@ -76,6 +76,8 @@ enum {
 #define MIXQ_FLAG_OVERFLOW 2         /* gate fired, but |set| would exceed k_cap;
                                         set left unchanged                      */
 
+#define MIXQ_PROGRESSIVE_GROUP 128   /* channels per group of progressive INT4  */
+
 /* output modes of mixq_gemm_ex */
 #define MIXQ_OUT_F32 0               /* Y fp32 [M, N]                            */
 #define MIXQ_OUT_SWIGLU_F16 1        /* gated weight: Y fp16 [M, N/2] =
@@ -132,6 +134,17 @@ typedef struct mixq_weight {
                           I + 32*(p/64) + p%64 - 32); wq, s_w and w_out all
                           follow the packed order.  Needed by
                           MIXQ_OUT_SWIGLU_F16.                                    */
+    int32_t group;     /* 0: INT4 codes are symmetric per channel (as above).
+                          MIXQ_PROGRESSIVE_GROUP (bits 4 only): progressive
+                          group-wise INT4 (QServe page, progressive group
+                          quantization): per channel to INT8 with the range
+                          [-119, 119] (s_w = max|W[n,:]| / 119), then per group
+                          of 128 channels a 4-bit value u in [0, 15], an integer
+                          scale s2 in [1, 16] and zero z in [0, 15]; the product
+                          uses the INT8 code (u - z) * s2.  wq holds u in the
+                          INT4 nibble layout.                                      */
+    uint16_t *gsz;     /* group != 0: [N, K/128], s2 | z << 8 for each row and
+                          group (device memory, written by mixq_pack_weight)    */
 } mixq_weight;
 
 /* ---- size helpers (pure host functions) ---------------------------------- */
@@ -259,7 +272,9 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *          w->gated selects the row order (see mixq_weight) and must be the
  *          same in the FULL call and every OUTLIER_COLS call
  * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for w->gated not 0
- *         or 1, MIXQ_ERR_UNSUPPORTED_SHAPE for a gated N not a multiple of 64.
+ *         or 1, w->group not 0 or MIXQ_PROGRESSIVE_GROUP, a group with bits 8,
+ *         or a null w->gsz with a group; MIXQ_ERR_UNSUPPORTED_SHAPE for a
+ *         gated N not a multiple of 64 or a group not dividing K.
  */
 int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
                      const mixq_act_state *state, int32_t mode, const mixq_weight *w,

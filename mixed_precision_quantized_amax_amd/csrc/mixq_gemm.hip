@@ -65,6 +65,9 @@ struct GemmArgs {
     int32_t* sync;  // [tiles] arrival counters, zero between calls
     int32_t* part;  // [tiles][2] int32 partial tiles
     int32_t out_mode;  // MIXQ_OUT_F32, or MIXQ_OUT_SWIGLU_F16 (Y then holds fp16)
+    // progressive INT4 (null: symmetric per-channel INT4): per row and group
+    // of 128 channels, s2 | z << 8
+    const uint16_t* gsz;
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -74,6 +77,21 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ sw
 __device__ __forceinline__ uint32_t sext_nibbles(uint32_t v) {
     const uint32_t s = v & 0x08080808u;
     return v | ((s << 5) - (s << 1));  // s * 0x1E: 0x08 -> 0xF0 per byte, no carries
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Progressive INT4 (QServe page, progressive group quantization): the
+// rebuilt INT8 code (u - z) * s2 of four 4-bit values u (one per byte),
+// computed as u * s2 + (128 - z * s2) in 16-bit lanes -- no carries between
+// lanes; the result is the code plus 128, in [1, 255] -- and turned back into
+// two's complement by flipping each byte's top bit.
+__device__ __forceinline__ uint32_t prog_decode4(uint32_t u4, u16x2 s2v, u16x2 cv) {
+    const u16x2 e = __builtin_bit_cast(u16x2, u4 & 0x00FF00FFu);
+    const u16x2 o = __builtin_bit_cast(u16x2, (u4 >> 8) & 0x00FF00FFu);
+    const uint32_t re = __builtin_bit_cast(uint32_t, e * s2v + cv);
+    const uint32_t ro = __builtin_bit_cast(uint32_t, o * s2v + cv);
+    return (re | (ro << 8)) ^ 0x80808080u;
 }
 
 // Buffer resource over [base, base + bytes): loads past the end return 0,
@@ -139,11 +157,15 @@ constexpr int waves_per_eu() {
     return (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2;
 }
 
-template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF, bool DEBUG>
+// PROG: progressive group-wise INT4 weights (a compile-time choice: a
+// branch in the loader would split the interleaved main loop).
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF, bool DEBUG,
+          bool PROG = false>
 __global__ __launch_bounds__(WM* WN* kWave)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, WM, WN>(), waves_per_eu<BM, BN, WM, WN>())))
 void gemm_kernel(GemmArgs a) {
     using C = Cfg<BM, BN, WM, WN, BITS>;
+    static_assert(!PROG || BITS == 4, "progressive groups are INT4");
     static_assert(STAGES == 2 || BITS == 8, "INT4 weights use the register-staged loader");
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
     // One array per stage (A tile, then B tile): the compiler then tracks each
@@ -505,6 +527,48 @@ void gemm_kernel(GemmArgs a) {
         struct Regs {
             v4i a[C::kAI];
             v4i b[BITS == 8 ? C::kBI : C::kBI4];
+            uint32_t g[PROG ? C::kBI4 : 1];  // progressive INT4: the rows' s2 | z << 8
+        };
+        // progressive INT4: groups of 128 channels = two K tiles
+        const int ngroups = K / 128;
+        const __amdgpu_buffer_rsrc_t rG =
+            make_rsrc(a.gsz + (int64_t)n0 * ngroups, a.gsz ? (int64_t)rows_b * ngroups * 2 : 0);
+        auto gzload = [&](int kt, Regs& R) {
+            if constexpr (PROG) {
+#pragma unroll
+                for (int i = 0; i < C::kBI4; ++i) {
+                    const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
+                    R.g[i] = __builtin_amdgcn_raw_buffer_load_b16(rG, (row * ngroups + kt / 2) * 2,
+                                                                   0, 0);
+                }
+            }
+        };
+        // INT4 -> INT8 codes of one staged 16-byte load: symmetric codes are
+        // sign-extended nibbles, progressive ones are rebuilt from u, s2, z
+        auto decode4 = [&](const Regs& R, int i, v4i& lo, v4i& hi) {
+            const uint32_t w[4] = {(uint32_t)R.b[i][0], (uint32_t)R.b[i][1], (uint32_t)R.b[i][2],
+                                   (uint32_t)R.b[i][3]};
+            if constexpr (PROG) {
+                const uint32_t g = R.g[i];
+                const unsigned short s2 = g & 0xFFu;
+                const unsigned short c = (unsigned short)(128u - (g >> 8) * s2);
+                const u16x2 s2v = {s2, s2}, cv = {c, c};
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    lo[2 * q] = (int)prog_decode4(w[q] & 0x0F0F0F0Fu, s2v, cv);
+                    lo[2 * q + 1] = (int)prog_decode4((w[q] >> 4) & 0x0F0F0F0Fu, s2v, cv);
+                    hi[2 * q] = (int)prog_decode4(w[2 + q] & 0x0F0F0F0Fu, s2v, cv);
+                    hi[2 * q + 1] = (int)prog_decode4((w[2 + q] >> 4) & 0x0F0F0F0Fu, s2v, cv);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    lo[2 * q] = (int)sext_nibbles(w[q] & 0x0F0F0F0Fu);
+                    lo[2 * q + 1] = (int)sext_nibbles((w[q] >> 4) & 0x0F0F0F0Fu);
+                    hi[2 * q] = (int)sext_nibbles(w[2 + q] & 0x0F0F0F0Fu);
+                    hi[2 * q + 1] = (int)sext_nibbles((w[2 + q] >> 4) & 0x0F0F0F0Fu);
+                }
+            }
         };
         auto gload = [&](int kt, Regs& R) {
 #pragma unroll
@@ -518,6 +582,7 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i)
                     R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+                gzload(kt, R);
             }
         };
         auto lstore = [&](const Regs& R, int buf) {
@@ -536,16 +601,8 @@ void gemm_kernel(GemmArgs a) {
                 for (int i = 0; i < C::kBI4; ++i) {
                     const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
                     const int c2 = lane & 1;
-                    const uint32_t w0 = R.b[i][0], w1 = R.b[i][1], w2 = R.b[i][2], w3 = R.b[i][3];
                     v4i lo, hi;
-                    lo[0] = (int)sext_nibbles(w0 & 0x0F0F0F0Fu);
-                    lo[1] = (int)sext_nibbles((w0 >> 4) & 0x0F0F0F0Fu);
-                    lo[2] = (int)sext_nibbles(w1 & 0x0F0F0F0Fu);
-                    lo[3] = (int)sext_nibbles((w1 >> 4) & 0x0F0F0F0Fu);
-                    hi[0] = (int)sext_nibbles(w2 & 0x0F0F0F0Fu);
-                    hi[1] = (int)sext_nibbles((w2 >> 4) & 0x0F0F0F0Fu);
-                    hi[2] = (int)sext_nibbles(w3 & 0x0F0F0F0Fu);
-                    hi[3] = (int)sext_nibbles((w3 >> 4) & 0x0F0F0F0Fu);
+                    decode4(R, i, lo, hi);
                     *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2)]) = lo;
                     *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2 + 1)]) = hi;
                 }
@@ -561,6 +618,7 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i)
                     R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+                gzload(kt, R);
             }
         };
         if constexpr (PF == 4) {
@@ -698,17 +756,8 @@ void gemm_kernel(GemmArgs a) {
                     for (int i = 0; i < C::kBI4; ++i) {
                         const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
                         const int c2 = lane & 1;
-                        const uint32_t w0 = R.b[i][0], w1 = R.b[i][1], w2 = R.b[i][2],
-                                       w3 = R.b[i][3];
                         v4i lo, hi;
-                        lo[0] = (int)sext_nibbles(w0 & 0x0F0F0F0Fu);
-                        lo[1] = (int)sext_nibbles((w0 >> 4) & 0x0F0F0F0Fu);
-                        lo[2] = (int)sext_nibbles(w1 & 0x0F0F0F0Fu);
-                        lo[3] = (int)sext_nibbles((w1 >> 4) & 0x0F0F0F0Fu);
-                        hi[0] = (int)sext_nibbles(w2 & 0x0F0F0F0Fu);
-                        hi[1] = (int)sext_nibbles((w2 >> 4) & 0x0F0F0F0Fu);
-                        hi[2] = (int)sext_nibbles(w3 & 0x0F0F0F0Fu);
-                        hi[3] = (int)sext_nibbles((w3 >> 4) & 0x0F0F0F0Fu);
+                        decode4(R, i, lo, hi);
                         *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2)]) = lo;
                         *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2 + 1)]) = hi;
                     }
@@ -958,17 +1007,17 @@ void gemm_kernel(GemmArgs a) {
         }
 }
 
-template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1>
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1, bool PROG = false>
 int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit), block(WM * WN * kWave);
     if (debug)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true>), grid, block, 0,
-                           st, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true, PROG>), grid, block,
+                           0, st, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false>), grid, block, 0,
-                           st, a);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false, PROG>), grid,
+                           block, 0, st, a);
     return launch_status();
 }
 
@@ -1036,18 +1085,23 @@ int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
     }
 }
 
-int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
+template <bool PROG>
+int launch_w4_t(const GemmArgs& a, bool debug, hipStream_t st) {
     switch (pick_cfg(a.M, a.N, a.K, 4)) {
-        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2>(a, debug, st);
-        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2>(a, debug, st);
-        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2>(a, debug, st);
-        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2>(a, debug, st);
-        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3>(a, debug, st);
-        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3>(a, debug, st);
-        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4>(a, debug, st);
-        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4>(a, debug, st);
-        default: return launch_cfg<128, 128, 2, 2, 4, 2>(a, debug, st);
+        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG>(a, debug, st);
+        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG>(a, debug, st);
+        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG>(a, debug, st);
+        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2, PROG>(a, debug, st);
+        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3, PROG>(a, debug, st);
+        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG>(a, debug, st);
+        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG>(a, debug, st);
+        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG>(a, debug, st);
+        default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG>(a, debug, st);
     }
+}
+
+int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
+    return a.gsz ? launch_w4_t<true>(a, debug, st) : launch_w4_t<false>(a, debug, st);
 }
 
 }  // namespace
@@ -1065,6 +1119,9 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     if (out_mode != MIXQ_OUT_F32 && out_mode != MIXQ_OUT_SWIGLU_F16) return MIXQ_ERR_INVALID_ARG;
     if (out_mode == MIXQ_OUT_SWIGLU_F16 && (w->gated != 1 || w->N % 64 != 0))
         return MIXQ_ERR_INVALID_ARG;
+    if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || w->bits != 4 || !w->gsz))
+        return MIXQ_ERR_INVALID_ARG;
+    if (w->group != 0 && w->K % MIXQ_PROGRESSIVE_GROUP != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < (out_mode == MIXQ_OUT_F32 ? w->N : w->N / 2))
         return MIXQ_ERR_INVALID_ARG;
     if (w->bits != 8 && w->bits != 4) return MIXQ_ERR_INVALID_ARG;
@@ -1099,6 +1156,7 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.sync = nullptr;
     a.part = nullptr;
     a.out_mode = out_mode;
+    a.gsz = w->group ? w->gsz : nullptr;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
     const int f = forced_cfg();

@@ -29,16 +29,22 @@ __device__ __forceinline__ int64_t src_row(int64_t n, int64_t N, int gated) {
     return within < 32 ? blk * 32 + within : N / 2 + blk * 32 + (within - 32);
 }
 
-template <int CPT, int BITS>
+// PROG: progressive INT4 (QServe page, progressive group quantization):
+// first level to INT8 with the range 119, then per group of 128 channels (16
+// chunks = 16 consecutive lanes) a 4-bit value, an integer scale and a zero;
+// integer steps with IEEE binary32 divisions whose ties are exact.
+template <int CPT, int BITS, bool PROG = false>
 __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_t* __restrict__ W,
                                                                     int64_t N, int32_t K,
                                                                     void* __restrict__ wq,
                                                                     float* __restrict__ s_w,
-                                                                    int gated) {
+                                                                    int gated,
+                                                                    uint16_t* __restrict__ gsz) {
+    static_assert(!PROG || BITS == 4, "progressive groups hold 4-bit values");
     __shared__ float red[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nchunks = K / 8;
-    constexpr float kQ = BITS == 8 ? 127.0f : 7.0f;
+    constexpr float kQ = BITS == 8 ? 127.0f : PROG ? 119.0f : 7.0f;
     for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
         const uint16_t* wr = W + src_row(n, N, gated) * (int64_t)K;
         uint4 v[CPT];
@@ -83,6 +89,32 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
                     half_bits_to_float((uint16_t)(u[e >> 1] >> ((e & 1) * 16))) * rho);
                 y = fminf(fmaxf(y, -kQ), kQ);
                 q[e] = (int)y;
+            }
+            if constexpr (PROG) {
+                // a group of 128 channels is 16 chunks, held by 16 consecutive lanes
+                int mn = 0, mx = 0;  // zero kept in the range: z is a 4-bit value
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    mn = min(mn, q[e]);
+                    mx = max(mx, q[e]);
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    mn = min(mn, __shfl_xor(mn, o, 16));
+                    mx = max(mx, __shfl_xor(mx, o, 16));
+                }
+                const int s2 = max(1, (mx - mn + 14) / 15);  // ceil((mx - mn) / 15)
+                const float fs2 = (float)s2;
+                // |value| <= 238 and s2 <= 16: a quotient that is a tie is exact
+                // in binary32, so rounding the binary32 quotient rounds the
+                // exact one (half to even)
+                const int z = (int)__builtin_rintf((float)(-mn) / fs2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    q[e] = min(max((int)__builtin_rintf((float)q[e] / fs2) + z, 0), 15);
+                if ((tid & 15) == 0)
+                    gsz[n * (int64_t)(K / MIXQ_PROGRESSIVE_GROUP) + c / 16] =
+                        (uint16_t)(s2 | (z << 8));
             }
             if (BITS == 8) {
                 uint32_t p0 = 0, p1 = 0;
@@ -139,10 +171,13 @@ int launch_quant(const uint16_t* W, int64_t N, int32_t K, int bits, const mixq_w
     const int grid = (int)(N < 4096 ? N : 4096);
     if (bits == 8)
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 8>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w, w->gated);
+                           N, K, w->wq, w->s_w, w->gated, nullptr);
+    else if (w->group)
+        hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4, true>), dim3(grid), dim3(kThreads), 0,
+                           st, W, N, K, w->wq, w->s_w, w->gated, w->gsz);
     else
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w, w->gated);
+                           N, K, w->wq, w->s_w, w->gated, nullptr);
     return launch_status();
 }
 
@@ -164,8 +199,11 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     if (state->k_cap > 0 && (!w->w_out || !state->idx)) return MIXQ_ERR_INVALID_ARG;
     if (!state->count) return MIXQ_ERR_INVALID_ARG;
     if (w->gated != 0 && w->gated != 1) return MIXQ_ERR_INVALID_ARG;
+    if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || bits != 4 || !w->gsz))
+        return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (w->gated && N % 64 != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (w->group && K % MIXQ_PROGRESSIVE_GROUP != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (((uintptr_t)W & 15u) != 0 || ((uintptr_t)w->wq & 15u) != 0)
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (N > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;

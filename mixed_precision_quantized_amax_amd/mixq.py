@@ -25,6 +25,7 @@ PACK_FULL = 0
 PACK_OUTLIER_COLS = 1
 OUT_F32 = 0
 OUT_SWIGLU_F16 = 1
+PROGRESSIVE_GROUP = 128
 OUTLIER_ALIGN = 32
 K_MULTIPLE = 64
 GATHER_SLOTS = 256
@@ -45,7 +46,8 @@ class ActState(ctypes.Structure):
 class Weight(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
                 ("k_out", ctypes.c_void_p), ("bits", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("k_cap", ctypes.c_int32), ("gated", ctypes.c_int32)]
+                ("k_cap", ctypes.c_int32), ("gated", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("gsz", ctypes.c_void_p)]
 
 
 _lib = None
@@ -163,10 +165,12 @@ class PackedWeight:
     w_out: torch.Tensor
     k_out: torch.Tensor
     gated: int = 0  # 1: W = [W_gate; W_up], packed with 32-row blocks interleaved
+    group: int = 0  # PROGRESSIVE_GROUP: progressive group-wise INT4
+    gsz: torch.Tensor | None = None  # [N, K/group] uint16: s2 | z << 8
 
     @classmethod
     def create(cls, N: int, K: int, bits: int, k_cap: int, device="cuda",
-               gated: bool = False) -> "PackedWeight":
+               gated: bool = False, group: int = 0) -> "PackedWeight":
         nbytes = int(lib().mixq_packed_weight_bytes(N, K, bits))
         if nbytes == 0:
             raise ValueError("invalid weight shape or bits")
@@ -176,11 +180,14 @@ class PackedWeight:
                    s_w=torch.empty(N, dtype=torch.float32, device=device),
                    w_out=torch.zeros(max(N * ld, 1), dtype=torch.float16, device=device),
                    k_out=torch.zeros(GATHER_SLOTS, dtype=torch.int32, device=device),
-                   gated=int(bool(gated)))
+                   gated=int(bool(gated)), group=int(group),
+                   gsz=(torch.zeros(N * (K // group), dtype=torch.int16, device=device)
+                        if group else None))
 
     def c(self) -> Weight:
         return Weight(self.wq.data_ptr(), self.s_w.data_ptr(), self.w_out.data_ptr(),
-                      self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap, self.gated)
+                      self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap, self.gated,
+                      self.group, None if self.gsz is None else self.gsz.data_ptr())
 
     def codes_view(self) -> torch.Tensor:
         """int8 [N, K] (bits 8) or packed uint8 [N, K/2] (bits 4) view of wq."""

@@ -120,11 +120,11 @@ def test_valid_arguments_need_a_device():
     assert mixq.lib().mixq_check_device() == 4
 
 
-def _weight(N=16, K=64, bits=8, k_cap=8, gated=0, **null):
-    vals = dict(wq=0x100000, s_w=0x200000, w_out=0x300000, k_out=0x400000)
+def _weight(N=16, K=64, bits=8, k_cap=8, gated=0, group=0, **null):
+    vals = dict(wq=0x100000, s_w=0x200000, w_out=0x300000, k_out=0x400000, gsz=0x500000)
     vals.update(null)
     return mixq.Weight(vals["wq"], vals["s_w"], vals["w_out"], vals["k_out"], bits, N, K, k_cap,
-                       gated)
+                       gated, group, vals["gsz"])
 
 
 @pytest.mark.parametrize("args,code", [
@@ -132,6 +132,10 @@ def _weight(N=16, K=64, bits=8, k_cap=8, gated=0, **null):
     (dict(w=_weight(bits=4)), 1), (dict(w=_weight(k_cap=4)), 1), (dict(w=_weight(wq=0)), 1),
     (dict(w=_weight(k_out=0)), 1), (dict(K=96, w=_weight(K=96)), 2),
     (dict(w=_weight(gated=2)), 1), (dict(w=_weight(gated=1)), 2),          # gated: N % 64
+    (dict(w=_weight(group=64, bits=4), bits=4), 1),                        # group size
+    (dict(w=_weight(group=128), bits=8), 1),                               # groups need INT4
+    (dict(w=_weight(group=128, bits=4, gsz=0), bits=4), 1),                # no group table
+    (dict(w=_weight(group=128, bits=4), bits=4), 2),                       # K = 64 < 128
 ])
 def test_pack_weight_validation(args, code):
     N = args.get("N", 16)
@@ -197,6 +201,9 @@ def test_gemm_ws_validation():
     (dict(mode=1), 1),                                   # SwiGLU needs a gated weight
     (dict(mode=1, w=_weight(N=64, gated=1), ldy=31), 1),  # fp16 row shorter than N/2
     (dict(mode=0, w=_weight(N=64, gated=1), ldy=32), 1),  # fp32 row shorter than N
+    (dict(mode=0, w=_weight(group=128, bits=8)), 1),       # groups need INT4
+    (dict(mode=0, w=_weight(group=128, bits=4, gsz=0)), 1),
+    (dict(mode=0, w=_weight(group=128, bits=4)), 2),       # K = 64 < 128
 ])
 def test_gemm_ex_validation(kw, code):
     w = kw.get("w", _weight())

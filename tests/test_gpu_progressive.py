@@ -1,0 +1,117 @@
+"""Progressive group-wise INT4 weights (mixq_weight.group = 128) against the
+oracle: the packed 4-bit values, the group table (s2 | z << 8) and the
+first-level scales bit for bit, the int32 accumulators of the product with
+the rebuilt INT8 codes bit for bit, and Y within 1e-3 * max|Y|."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import check_y, say, to_dev
+from mixed_precision_quantized_amax_amd import mixq, workloads
+from oracle import Oracle, OracleLayer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return Oracle()
+
+
+@pytest.fixture
+def tile(request):
+    old = os.environ.get("MIXQ_GEMM_TILE")
+    os.environ["MIXQ_GEMM_TILE"] = request.param
+    yield request.param
+    if old is None:
+        del os.environ["MIXQ_GEMM_TILE"]
+    else:
+        os.environ["MIXQ_GEMM_TILE"] = old
+
+
+def unpack_u4(packed: np.ndarray, K: int) -> np.ndarray:
+    """Decode the documented nibble layout without sign extension: per 32-bit
+    word (8 consecutive k), byte j holds k+j low and k+j+4 high."""
+    N = packed.shape[0]
+    b = packed.reshape(N, K // 8, 4).astype(np.uint8)
+    out = np.concatenate([b & 0xF, b >> 4], axis=2)
+    return out.reshape(N, K)
+
+
+def run_progressive(X, W, tau, k_cap, acc=True):
+    M, K = X.shape
+    N = W.shape[0]
+    Wd = to_dev(W.view(np.float16))
+    st = mixq.OutlierState.create(K, k_cap)
+    pw = mixq.PackedWeight.create(N, K, 4, k_cap, group=mixq.PROGRESSIVE_GROUP)
+    mixq.pack_weight(Wd, st, pw, mixq.PACK_FULL)
+    ld = mixq.outlier_ld(k_cap)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    Xo = torch.zeros(max(M * ld, 1), dtype=torch.float16, device="cuda") if ld else None
+    mixq.quantize_act(to_dev(X.view(np.float16)), tau, st, Xq, sx, Xo)
+    mixq.pack_weight(Wd, st, pw, mixq.PACK_OUTLIER_COLS)
+    Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    dbg = torch.zeros(M, N, dtype=torch.int32, device="cuda") if acc else None
+    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg)
+    torch.cuda.synchronize()
+    return dict(pw=pw, Y=Y.cpu().numpy(), acc=None if dbg is None else dbg.cpu().numpy(),
+                count=int(st.count.cpu()[0]))
+
+
+def check_codes(orc, g, W):
+    N, K = W.shape
+    q8p, s1, u, s2, z, _ = orc.progressive_quantize_weight(W)
+    pw = g["pw"]
+    got_u = unpack_u4(pw.codes_view().cpu().numpy(), K)
+    bad = np.argwhere(got_u != u)
+    assert bad.shape[0] == 0, f"{bad.shape[0]} 4-bit value mismatches, first {bad[:4].tolist()}"
+    gsz = pw.gsz.view(torch.int16).cpu().numpy().view(np.uint16).reshape(N, K // 128)
+    assert np.array_equal(gsz & 0xFF, s2) and np.array_equal(gsz >> 8, z)
+    assert np.array_equal(pw.s_w.cpu().numpy().view(np.uint32), s1.view(np.uint32))
+    return q8p, s1
+
+
+@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11"], indirect=True)
+@pytest.mark.parametrize("M,K,N,n_out", [(37, 256, 128, 3), (130, 1024, 384, 9),
+                                         (257, 2048, 520, 0), (64, 4096, 256, 40)])
+def test_progressive_random(orc, tile, M, K, N, n_out):
+    X, W, _ = workloads.random_case(seed=M + K + N + 7, M=M, K=K, N=N, n_out=n_out)
+    say(f"[prog] tile{tile} M={M} K={K} N={N}")
+    g = run_progressive(X, W, 6.0, 64)
+    q8p, s1 = check_codes(orc, g, W)
+    o = OracleLayer(W=W, bits=8, tau=6.0, k_cap=64, ldo=mixq.outlier_ld(64), oracle=orc)
+    r = o.step(X, products=False)
+    assert g["count"] == r.count
+    acc = orc.int_gemm(r.Xq, q8p)
+    assert np.array_equal(g["acc"], acc)
+    W_out = orc.gather_weight_cols(W, r.in_set, mixq.outlier_ld(64))
+    Y = orc.output(acc, r.s_x, s1, r.X_out, W_out, r.count)
+    err = check_y(g["Y"], Y)
+    say(f"[prog] ok count={r.count} max|dY|/max|Y|={err:.2e}")
+
+
+def test_progressive_full_size(orc):
+    """The INT4 prefill shape (M = 2048, K = N = 8192) with progressive
+    weights: every code, group entry and scale; acc and Y at sampled
+    positions."""
+    wl = workloads.WORKLOADS["prefill_w4"]
+    X = workloads.make_activation(wl)
+    W = workloads.make_weight(wl)
+    g = run_progressive(X, W, wl.tau, 256, acc=True)
+    q8p, s1 = check_codes(orc, g, W)
+    o = OracleLayer(W=W, bits=8, tau=wl.tau, k_cap=256, ldo=mixq.outlier_ld(256), oracle=orc)
+    r = o.step(X, products=False)
+    assert g["count"] == r.count
+    W_out = orc.gather_weight_cols(W, r.in_set, mixq.outlier_ld(256))
+    rng = np.random.default_rng(9)
+    rows = np.concatenate([rng.integers(0, wl.M, 2000), [0, wl.M - 1, 255, 256]])
+    cols = np.concatenate([rng.integers(0, wl.N, 2000), [0, wl.N - 1, 255, 256]])
+    acc, Y = orc.sampled_output(r.Xq, q8p, r.s_x, s1, r.X_out, W_out, r.count, rows, cols)
+    assert np.array_equal(g["acc"][rows, cols], acc)
+    ref = np.abs(Y).max()
+    err = np.abs(g["Y"][rows, cols].astype(np.float64) - Y).max() / ref
+    say(f"[prog] full: max|dY|/max|Y| = {err:.2e}")
+    assert err <= 1e-3
