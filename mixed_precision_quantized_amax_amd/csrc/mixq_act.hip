@@ -457,13 +457,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         if constexpr (NORM) {
             double hi = 0.0, lo = 0.0;
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                sumsq_chunk(xv[i], hi, lo);
-                // one chunk's squares at a time: left to itself the scheduler
-                // widens all of them to doubles up front, which costs
-                // occupancy
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int i = 0; i < CPT; ++i) sumsq_chunk(xv[i], hi, lo);
             wave_pair_sum(hi, lo);
             if (lane == 0) {
                 rsum[parity][slot][part][0] = hi;
@@ -701,11 +695,8 @@ int launch_act(const ActArgs& a, hipStream_t st) {
     // up to 1024 blocks: at M = 2048 each block takes two tokens, the second
     // one's loads in flight while the first is processed (measured: 1024
     // blocks 13.6 us, 2048 blocks 14.4 us, 512 blocks 16.4 us per call)
-    // with the RMSNorm prologue (159 VGPRs, three blocks per CU) at most as
-    // many blocks as are resident at once (measured at M = 2048: 768 blocks
-    // 25.9 us, 512 blocks 28.7 us, 1024 blocks 26.8 us per call)
-    const int gmax = NORM && !RES ? 768 : 1024;  // the residual variant: 108 VGPRs, four blocks per CU
-    const int grid = (int)(g1 < gmax ? g1 : gmax);
+    // (all variants fit four blocks per CU: at most 127 VGPRs)
+    const int grid = (int)(g1 < 1024 ? g1 : 1024);
     const size_t lds = (size_t)a.words * 8 + (NORM ? (size_t)a.K * 2 : 0);
     hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES>), dim3(grid),
                        dim3(kGateThreads), lds, st, a);
