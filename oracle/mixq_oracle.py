@@ -126,6 +126,10 @@ class Oracle:
         """See ``progressive_quantize_weight`` below."""
         return progressive_quantize_weight(W, group)
 
+    def mixed_feature_quantize_weight(self, W, salient, group: int = 128):
+        """See ``mixed_feature_quantize_weight`` below."""
+        return mixed_feature_quantize_weight(W, salient, group, oracle=self)
+
     # -- the operation after the layer ---------------------------------------------
     def swiglu(self, Y):
         """Returns silu(gate) * up in float64; see ``swiglu`` below."""
@@ -255,6 +259,28 @@ def progressive_quantize_weight(W, group: int = GROUP):
     assert np.abs(q8p).max(initial=0) <= 127
     return (q8p.reshape(N, K).astype(np.int8), s1, u.reshape(N, K).astype(np.uint8),
             s2.astype(np.uint8), z.astype(np.uint8), q8.astype(np.int8))
+
+
+def mixed_feature_quantize_weight(W, salient, group: int = GROUP, oracle=None):
+    """Output-feature mixed precision (the MixLLM page): the output features
+    marked salient keep 8-bit weights, the others get 4 bits, activations stay
+    8-bit and every product runs on INT8 units.  The reading taken here: a
+    salient row is quantized like any INT8 weight row (symmetric, per channel,
+    range 127); every other row is progressive group-wise INT4 (asymmetric
+    4-bit groups of ``group`` channels, ``progressive_quantize_weight``).
+    Each row's codes and scale depend on that row only.
+
+    W: fp16 [N, K]; salient: bool [N].  Returns (codes int8 [N, K], the INT8
+    codes the product uses, scales fp32 [N]).
+    """
+    o = oracle or Oracle()
+    sal = np.asarray(salient, bool)
+    Wh = W.view(np.float16) if W.dtype == np.uint16 else np.asarray(W, np.float16)
+    q8, s8 = o.quantize_weight(Wh, 8)
+    q4p, s4, *_ = progressive_quantize_weight(Wh, group)
+    codes = np.where(sal[:, None], q8, q4p).astype(np.int8)
+    scales = np.where(sal, s8, s4).astype(np.float32)
+    return codes, scales
 
 
 def _rne_div(a, b):

@@ -734,6 +734,33 @@ def pin_progressive_no_overflow(o):
     assert worst <= 127
 
 
+def pin_mixed_feature(o):
+    """Output-feature mixed precision: all rows salient gives the INT8 weight
+    quantizer, no row salient gives progressive INT4, and in between every
+    row carries exactly its own kind (rows are quantized independently, so
+    permuting rows together with the mask permutes codes and scales)."""
+    W = _progressive_rows(4)
+    N = W.shape[0]
+    q8, s8 = o.quantize_weight(W, 8)
+    q4p, s4, *_ = o.progressive_quantize_weight(W)
+    c, sc = o.mixed_feature_quantize_weight(W, np.ones(N, bool))
+    assert (c == q8).all() and (sc.view(np.uint32) == s8.view(np.uint32)).all()
+    c, sc = o.mixed_feature_quantize_weight(W, np.zeros(N, bool))
+    assert (c == q4p).all() and (sc.view(np.uint32) == s4.view(np.uint32)).all()
+    mask = np.array([True, False, True, False, False, True])
+    c, sc = o.mixed_feature_quantize_weight(W, mask)
+    for n in range(N):
+        assert (c[n] == (q8[n] if mask[n] else q4p[n])).all()
+        assert sc[n] == (s8[n] if mask[n] else s4[n])
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    cp, scp = o.mixed_feature_quantize_weight(np.ascontiguousarray(W[perm]), mask[perm])
+    assert (cp == c[perm]).all() and (scp == sc[perm]).all()
+    # the 8-bit rows really are finer than their 4-bit versions
+    err8 = np.abs(q8[mask].astype(np.float64) * s8[mask, None] - W[mask].astype(np.float64)).max()
+    err4 = np.abs(q4p[mask].astype(np.float64) * s4[mask, None] - W[mask].astype(np.float64)).max()
+    assert err8 < err4
+
+
 ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode,
             pin_set_bruteforce, pin_quant_error_bound, pin_nearest_code, pin_weight_bound,
             pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
@@ -741,4 +768,5 @@ ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
             pin_decode_sequence, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
             pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals,
-            pin_residual_add, pin_swiglu, pin_progressive_levels, pin_progressive_no_overflow]
+            pin_residual_add, pin_swiglu, pin_progressive_levels, pin_progressive_no_overflow,
+            pin_mixed_feature]
