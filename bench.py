@@ -69,21 +69,28 @@ def algorithmic_bytes(wl, k: int) -> int:
             + 2 * kp * (wl.M + wl.N) + 4 * wl.M * wl.N)
 
 
-def run_gpu(wl, steps: int, warmup: int, group: int = 0):
-    """group: 0, or the progressive INT4 group size (INT4 workloads)."""
+def run_gpu(wl, steps: int, warmup: int, group: int = 0, salient=None):
+    """group: 0, or the progressive INT4 group size (INT4 workloads).
+    salient: None, or bool [N]: an output-feature mixed-precision weight
+    (those rows at 8 bits as two progressive planes, the rest progressive
+    INT4)."""
     import torch
     from mixed_precision_quantized_amax_amd import mixq, workloads
 
     dev = torch.device("cuda", 0)
-    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits} group={group}")
+    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits} group={group}"
+        f" salient={None if salient is None else int(salient.sum())}")
     W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
     X0 = torch.from_numpy(workloads.make_activation(wl)).to(dev)
     k_cap = 256
     wq_bytes = wl.N * wl.K * wl.bits // 8
     copies = int(min(8, max(2, math.ceil(CACHE_DEFEAT_BYTES / (wq_bytes + 3 * wl.M * wl.K)))))
     state = mixq.OutlierState.create(wl.K, k_cap, dev)
-    packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev, group=group)
-             for _ in range(copies)]
+    if salient is None:
+        packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev, group=group)
+                 for _ in range(copies)]
+    else:
+        packs = [mixq.PackedWeight.create_mixed(salient, wl.K, k_cap, dev) for _ in range(copies)]
     for p in packs:
         mixq.pack_weight(W, state, p, mixq.PACK_FULL)
     # activation copies: the same values in different buffers
@@ -164,7 +171,7 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0):
     act_ms = g0.elapsed_time(g1) / steps
     flag = int(state.flag.cpu()[0])
     return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm_ms=gemm_ms, act_ms=act_ms,
-                count=count, flag=flag, copies=copies)
+                count=count, flag=flag, copies=copies, packed_rows=packs[0].N)
 
 
 def norm_act_bytes(wl, k: int) -> int:
@@ -506,6 +513,17 @@ def main():
             "act_quant_us": round(r4["act_ms"] * 1e3, 1),
             "ms_per_step": round(r4["ms_step"], 4),
             "weights": "progressive group-wise INT4, groups of 128 (rebuilt to INT8 in the loader)"}
+        sal = workloads.make_salient(w4.N)
+        r5 = run_gpu(w4, max(10, args.steps // 2), args.warmup, salient=sal)
+        others["prefill_w4_mixed_features"] = {
+            "step_tops": round(w4.ops / (r5["ms_step"] / 1e3) / 1e12, 1),
+            "gemm_tops": round(w4.ops / (r5["gemm_ms"] / 1e3) / 1e12, 1),
+            "gemm_us": round(r5["gemm_ms"] * 1e3, 1),
+            "act_quant_us": round(r5["act_ms"] * 1e3, 1),
+            "ms_per_step": round(r5["ms_step"], 4),
+            "packed_rows": r5["packed_rows"],
+            "weights": f"{int(sal.sum())} of {w4.N} output features 8-bit (two progressive "
+                       "4-bit planes each), the rest progressive INT4; TOPS count 2*M*N*K"}
         dwl = workloads.WORKLOADS["decode_seq"]
         d = run_decode_sequence(dwl)
         others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),

@@ -77,6 +77,7 @@ enum {
                                         set left unchanged                      */
 
 #define MIXQ_PROGRESSIVE_GROUP 128   /* channels per group of progressive INT4  */
+#define MIXQ_ROW_PAD 0x3FFFFFFF      /* padding row of a mixed-precision map    */
 
 /* output modes of mixq_gemm_ex */
 #define MIXQ_OUT_F32 0               /* Y fp32 [M, N]                            */
@@ -145,6 +146,21 @@ typedef struct mixq_weight {
                           INT4 nibble layout.                                      */
     uint16_t *gsz;     /* group != 0: [N, K/128], s2 | z << 8 for each row and
                           group (device memory, written by mixq_pack_weight)    */
+    const int32_t *rmap; /* NULL, or (progressive INT4 only) output-feature mixed
+                          precision (MixLLM page): [N] device map of packed rows,
+                          from mixq_mixed_rows.  Entry = W row | plane << 30;
+                          plane 0: a 4-bit progressive row; 1 and 2: the high
+                          and low planes of an 8-bit row (code = 16 h + l: h in
+                          [-8, 7] as 4-bit value h + 8 with s2 = 16, z = 8; l in
+                          [0, 15] with s2 = 1, z = 0), in 64-row blocks of 32
+                          high then the same 32 low rows; W row MIXQ_ROW_PAD
+                          marks padding, and so does any W row >= n_out.  Y
+                          column of a packed row = its W row; the product adds
+                          each block's two planes.  Not with gated weights.  */
+    int32_t npair;     /* rmap != NULL: rows [0, npair) hold planes; a multiple
+                          of 256                                                  */
+    int32_t n_out;     /* rmap != NULL: rows of W = output features (columns of
+                          Y); ldy >= n_out                                        */
 } mixq_weight;
 
 /* ---- size helpers (pure host functions) ---------------------------------- */
@@ -259,9 +275,11 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *   code = clamp(round_half_even(W[n,k] * rho), -Q, Q), stored as documented
  *   in mixq_weight;  w_out[n, j] = W[n, idx[j]] for j < count, then zeros.
  *
- *   W      fp16 [N, K] device, row-major (ld = K).  Keep it: the outlier
- *          columns are gathered from it again when the set grows.
- *   N, K   >= 1; K multiple of 64, <= MIXQ_K_MAX
+ *   W      fp16 [N, K] device, row-major (ld = K); [w->n_out, K] when w->rmap
+ *          is set.  Keep it: the outlier columns are gathered from it again
+ *          when the set grows.
+ *   N, K   >= 1; K multiple of 64, <= MIXQ_K_MAX; N = w->N (the packed row
+ *          count, for a mixed-precision weight)
  *   bits   8 or 4
  *   state  the activation state whose set selects the outlier columns
  *   mode   MIXQ_PACK_FULL: everything.  MIXQ_PACK_OUTLIER_COLS: re-gather
@@ -273,7 +291,9 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *          same in the FULL call and every OUTLIER_COLS call
  * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for w->gated not 0
  *         or 1, w->group not 0 or MIXQ_PROGRESSIVE_GROUP, a group with bits 8,
- *         or a null w->gsz with a group; MIXQ_ERR_UNSUPPORTED_SHAPE for a
+ *         or a null w->gsz with a group, and for a w->rmap without a group,
+ *         with a gated weight, with npair not a multiple of 256 or above N,
+ *         or with n_out not in [1, N]; MIXQ_ERR_UNSUPPORTED_SHAPE for a
  *         gated N not a multiple of 64 or a group not dividing K.
  */
 int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
@@ -296,9 +316,13 @@ int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
  *   state           the activation state (count and k_cap are used)
  *   w               packed weight, gathered for the current set
  *   M               tokens, >= 1
- *   Y               fp32 [M, ldy] device, written; ldy >= N
- *   acc_debug       NULL, or int32 [M, N] device: also receives acc
- * Errors: as mixq_quantize_act.
+ *   Y               fp32 [M, ldy] device, written; ldy >= N (>= w->n_out for
+ *                   a mixed-precision weight, whose Y columns are W's rows)
+ *   acc_debug       NULL, or int32 [M, N] device: also receives acc, in
+ *                   packed row order (each plane of a mixed-precision weight
+ *                   on its own)
+ * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for a w->rmap
+ *         that mixq_pack_weight would reject.
  */
 int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
               const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
@@ -347,7 +371,8 @@ int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  *   acc_debug as mixq_gemm, in the packed (interleaved) column order
  * Other arguments: as mixq_gemm_ws (ws may be NULL).
  * Errors: as mixq_gemm; MIXQ_ERR_INVALID_ARG also for an unknown out_mode,
- *         MIXQ_OUT_SWIGLU_F16 with a weight not packed gated, or ldy < N/2.
+ *         MIXQ_OUT_SWIGLU_F16 with a weight not packed gated or with a
+ *         mixed-precision weight, or ldy < N/2.
  */
 int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  const mixq_act_state *state, const mixq_weight *w, int64_t M, void *Y,
@@ -358,6 +383,20 @@ int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  * 256 compute units (MI355X): 4096 bytes of tile counters plus two 64 KiB
  * partial tiles per 128 x 128 output tile; 0 when the product is not split. */
 size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
+
+/*
+ * mixq_mixed_rows -- packed row map of an output-feature mixed-precision
+ * weight (host function).  salient: [N] 0/1 flags (the 8-bit output
+ * features).  The S salient rows, ascending, become planes: 64-row blocks of
+ * 32 high planes then the same rows' 32 low planes, padded to a multiple of
+ * 256 packed rows; the other rows follow, ascending, as 4-bit rows.  Writes
+ * rmap[0 .. returned count) (rmap may be NULL to query the count) and
+ * *npair.  Returns the number of packed rows, or -1 for bad arguments.
+ * Pack a weight with w->N = that count, bits 4, group
+ * MIXQ_PROGRESSIVE_GROUP, w->rmap = a device copy of rmap, w->npair = *npair
+ * and w->n_out = N.
+ */
+int64_t mixq_mixed_rows(const uint8_t *salient, int64_t N, int32_t *rmap, int32_t *npair);
 
 /* Text of a status code (static storage). */
 const char *mixq_status_string(int status);

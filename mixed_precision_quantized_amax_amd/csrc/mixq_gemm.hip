@@ -68,6 +68,11 @@ struct GemmArgs {
     // progressive INT4 (null: symmetric per-channel INT4): per row and group
     // of 128 channels, s2 | z << 8
     const uint16_t* gsz;
+    // output-feature mixed precision (progressive kernels only): packed row ->
+    // W row | plane << 30; packed rows [0, npair) are 64-row blocks of 32 high
+    // and 32 low planes; Y columns are W rows < n_out
+    const int32_t* rmap;
+    int32_t npair, n_out;
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -84,7 +89,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // Progressive INT4 (QServe page, progressive group quantization): the
 // rebuilt INT8 code (u - z) * s2 of four 4-bit values u (one per byte),
 // computed as u * s2 + (128 - z * s2) in 16-bit lanes -- no carries between
-// lanes; the result is the code plus 128, in [1, 255] -- and turned back into
+// lanes; the result is the code plus 128, in [0, 255] -- and turned back into
 // two's complement by flipping each byte's top bit.
 __device__ __forceinline__ uint32_t prog_decode4(uint32_t u4, u16x2 s2v, u16x2 cv) {
     const u16x2 e = __builtin_bit_cast(u16x2, u4 & 0x00FF00FFu);
@@ -160,7 +165,7 @@ constexpr int waves_per_eu() {
 // PROG: progressive group-wise INT4 weights (a compile-time choice: a
 // branch in the loader would split the interleaved main loop).
 template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF, bool DEBUG,
-          bool PROG = false>
+          bool PROG = false, bool MIXED = false>
 __global__ __launch_bounds__(WM* WN* kWave)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, WM, WN>(), waves_per_eu<BM, BN, WM, WN>())))
 void gemm_kernel(GemmArgs a) {
@@ -876,11 +881,11 @@ void gemm_kernel(GemmArgs a) {
     const int count = *a.count;
     const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
 
+    if constexpr (DEBUG) {
 #pragma unroll
-    for (int i = 0; i < C::kFM; ++i) {
+        for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::kFN; ++j) {
-            if constexpr (DEBUG) {
+            for (int j = 0; j < C::kFN; ++j) {
                 const int col = n0 + wn * C::kWTN + j * 32 + fr;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -889,6 +894,27 @@ void gemm_kernel(GemmArgs a) {
                         a.acc_debug[(int64_t)row * a.N + col] = acc[i][j][e];
                 }
             }
+    }
+    if constexpr (MIXED) {
+        // Mixed precision: the tile's packed rows are 64-row blocks of 32 high
+        // then 32 low planes (npair is a multiple of 256, so a tile is all
+        // planes or none, and a wave's columns start on a block), so fragment
+        // 2jj + 1 holds the low plane of fragment 2jj's rows.  The 8-bit
+        // product is their sum, exact in int32; the high fragment carries it.
+        if (n0 < a.npair) {
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < C::kFN / 2; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][2 * jj][e] += acc[i][2 * jj + 1][e];
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < C::kFM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::kFN; ++j) {
             const float swj = sw_t[wn * C::kWTN + j * 32 + fr];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -993,8 +1019,17 @@ void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kFN; ++j) {
-            const int col = n0 + wn * C::kWTN + j * 32 + fr;
+            int col = n0 + wn * C::kWTN + j * 32 + fr;
             const int r0 = wm * C::kWTM + i * 32 + 4 * fh;  // tile-relative row of e = 0
+            if constexpr (MIXED) {
+                // mixed precision: the Y column is the packed row's W row;
+                // low planes (added above) and padding store nothing
+                if (col < a.N) {
+                    const int32_t rm = a.rmap[col];
+                    const int src = rm & MIXQ_ROW_PAD;
+                    col = (((uint32_t)rm >> 30) != 2u && src < a.n_out) ? src : a.N;
+                }
+            }
             if (col < a.N) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
@@ -1007,17 +1042,19 @@ void gemm_kernel(GemmArgs a) {
         }
 }
 
-template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1, bool PROG = false>
+template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1, bool PROG = false,
+          bool MIXED = false>
 int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
+    static_assert(!MIXED || PROG, "mixed-precision weights are progressive INT4");
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit), block(WM * WN * kWave);
     if (debug)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true, PROG>), grid, block,
-                           0, st, a);
-    else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false, PROG>), grid,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true, PROG, MIXED>), grid,
                            block, 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false, PROG, MIXED>),
+                           grid, block, 0, st, a);
     return launch_status();
 }
 
@@ -1085,22 +1122,23 @@ int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
     }
 }
 
-template <bool PROG>
+template <bool PROG, bool MIXED = false>
 int launch_w4_t(const GemmArgs& a, bool debug, hipStream_t st) {
     switch (pick_cfg(a.M, a.N, a.K, 4)) {
-        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG>(a, debug, st);
-        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG>(a, debug, st);
-        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG>(a, debug, st);
-        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2, PROG>(a, debug, st);
-        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3, PROG>(a, debug, st);
-        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG>(a, debug, st);
-        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG>(a, debug, st);
-        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG>(a, debug, st);
-        default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG>(a, debug, st);
+        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
+        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
+        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG, MIXED>(a, debug, st);
+        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2, PROG, MIXED>(a, debug, st);
+        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3, PROG, MIXED>(a, debug, st);
+        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG, MIXED>(a, debug, st);
+        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
+        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
+        default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
     }
 }
 
 int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
+    if (a.rmap) return launch_w4_t<true, true>(a, debug, st);
     return a.gsz ? launch_w4_t<true>(a, debug, st) : launch_w4_t<false>(a, debug, st);
 }
 
@@ -1122,8 +1160,12 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || w->bits != 4 || !w->gsz))
         return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && w->K % MIXQ_PROGRESSIVE_GROUP != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
-    if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < (out_mode == MIXQ_OUT_F32 ? w->N : w->N / 2))
+    if (w->rmap && (w->group == 0 || w->gated || out_mode != MIXQ_OUT_F32 || w->npair < 0 ||
+                    w->npair % 256 != 0 || w->npair > w->N || w->n_out <= 0 || w->n_out > w->N))
         return MIXQ_ERR_INVALID_ARG;
+    // Y columns: N, N / 2 for SwiGLU, n_out for a mixed-precision weight
+    const int64_t ny = w->rmap ? w->n_out : out_mode == MIXQ_OUT_F32 ? w->N : w->N / 2;
+    if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < ny) return MIXQ_ERR_INVALID_ARG;
     if (w->bits != 8 && w->bits != 4) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap < 0 || state->k_cap > w->K || w->k_cap != state->k_cap)
         return MIXQ_ERR_INVALID_ARG;
@@ -1157,6 +1199,9 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.part = nullptr;
     a.out_mode = out_mode;
     a.gsz = w->group ? w->gsz : nullptr;
+    a.rmap = w->group ? w->rmap : nullptr;
+    a.npair = w->rmap ? w->npair : 0;
+    a.n_out = w->rmap ? w->n_out : 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
     const int f = forced_cfg();

@@ -39,14 +39,36 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
                                                                     void* __restrict__ wq,
                                                                     float* __restrict__ s_w,
                                                                     int gated,
-                                                                    uint16_t* __restrict__ gsz) {
+                                                                    uint16_t* __restrict__ gsz,
+                                                                    const int32_t* __restrict__ rmap,
+                                                                    int64_t n_out) {
     static_assert(!PROG || BITS == 4, "progressive groups hold 4-bit values");
     __shared__ float red[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nchunks = K / 8;
     constexpr float kQ = BITS == 8 ? 127.0f : PROG ? 119.0f : 7.0f;
+    const int ngroups = K / MIXQ_PROGRESSIVE_GROUP;
     for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-        const uint16_t* wr = W + src_row(n, N, gated) * (int64_t)K;
+        // mixed precision: the packed row's W row and plane (0: 4-bit row;
+        // 1, 2: high and low plane of an 8-bit row), the same for the whole block
+        int64_t srow = src_row(n, N, gated);
+        int plane = 0;
+        if (PROG && rmap) {
+            const int32_t rm = rmap[n];
+            srow = rm & MIXQ_ROW_PAD;
+            plane = (int)((uint32_t)rm >> 30);
+            if (srow >= n_out) {  // padding: all codes 0
+                uint8_t* dst = static_cast<uint8_t*>(wq) + n * (int64_t)(K / 2);
+                const uint32_t fill = plane == 1 ? 0x88888888u : 0u;  // high plane: 8 is 0
+                for (int c = tid; c < nchunks; c += kThreads)
+                    *reinterpret_cast<uint32_t*>(dst + (int64_t)c * 4) = fill;
+                for (int g = tid; g < ngroups; g += kThreads)
+                    gsz[n * (int64_t)ngroups + g] = plane == 1 ? (uint16_t)(16 | (8 << 8)) : (uint16_t)1;
+                if (tid == 0) s_w[n] = 1.0f;
+                continue;
+            }
+        }
+        const uint16_t* wr = W + srow * (int64_t)K;
         uint4 v[CPT];
         float am = 0.0f;
 #pragma unroll
@@ -67,13 +89,15 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
         for (int w = 1; w < kWaves; ++w) g = fmaxf(g, red[w]);
         __syncthreads();
 
+        // an 8-bit row of a mixed-precision weight uses the INT8 range
+        const float qr = plane ? 127.0f : kQ;
         float s, rho;
         if (g == 0.0f) {
             s = 1.0f;
             rho = 1.0f;
         } else {
-            s = g / kQ;
-            rho = kQ / g;
+            s = g / qr;
+            rho = qr / g;
         }
         if (tid == 0) s_w[n] = s;
 
@@ -87,10 +111,19 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
             for (int e = 0; e < 8; ++e) {
                 float y = __builtin_rintf(
                     half_bits_to_float((uint16_t)(u[e >> 1] >> ((e & 1) * 16))) * rho);
-                y = fminf(fmaxf(y, -kQ), kQ);
+                y = fminf(fmaxf(y, -qr), qr);
                 q[e] = (int)y;
             }
-            if constexpr (PROG) {
+            if (PROG && plane) {
+                // code = 16 h + l with h in [-8, 7], l in [0, 15]: the high
+                // plane holds h + 8 with s2 16, z 8, the low plane l with s2 1, z 0
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    q[e] = plane == 1 ? (q[e] + 128) >> 4 : (q[e] + 128) & 15;
+                if ((tid & 15) == 0)
+                    gsz[n * (int64_t)ngroups + c / 16] =
+                        plane == 1 ? (uint16_t)(16 | (8 << 8)) : (uint16_t)1;
+            } else if constexpr (PROG) {
                 // a group of 128 channels is 16 chunks, held by 16 consecutive lanes
                 int mn = 0, mx = 0;  // zero kept in the range: z is a 4-bit value
 #pragma unroll
@@ -113,8 +146,7 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
                 for (int e = 0; e < 8; ++e)
                     q[e] = min(max((int)__builtin_rintf((float)q[e] / fs2) + z, 0), 15);
                 if ((tid & 15) == 0)
-                    gsz[n * (int64_t)(K / MIXQ_PROGRESSIVE_GROUP) + c / 16] =
-                        (uint16_t)(s2 | (z << 8));
+                    gsz[n * (int64_t)ngroups + c / 16] = (uint16_t)(s2 | (z << 8));
             }
             if (BITS == 8) {
                 uint32_t p0 = 0, p1 = 0;
@@ -149,7 +181,9 @@ __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* _
                                                                const int32_t* __restrict__ count_p,
                                                                uint16_t* __restrict__ w_out,
                                                                int32_t ld_out, int32_t* k_out,
-                                                               int force, int gated) {
+                                                               int force, int gated,
+                                                               const int32_t* __restrict__ rmap,
+                                                               int64_t n_out) {
     const int count = *count_p;
     if (!force && k_out[blockIdx.x] == count) return;
     const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
@@ -159,7 +193,16 @@ __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* _
     for (int64_t t = threadIdx.x; t < total; t += kThreads) {
         const int64_t n = blockIdx.x + (t / kpad) * G;
         const int j = (int)(t % kpad);
-        w_out[n * ld_out + j] = j < count ? W[src_row(n, N, gated) * (int64_t)K + idx[j]] : (uint16_t)0;
+        // mixed precision: the outlier columns ride on the high plane (or the
+        // 4-bit row); low planes and padding get zeros
+        int64_t srow = src_row(n, N, gated);
+        bool live = true;
+        if (rmap) {
+            const int32_t rm = rmap[n];
+            srow = rm & MIXQ_ROW_PAD;
+            live = srow < n_out && ((uint32_t)rm >> 30) != 2u;
+        }
+        w_out[n * ld_out + j] = (live && j < count) ? W[srow * (int64_t)K + idx[j]] : (uint16_t)0;
     }
     __syncthreads();
     if (threadIdx.x == 0) k_out[blockIdx.x] = count;
@@ -171,13 +214,14 @@ int launch_quant(const uint16_t* W, int64_t N, int32_t K, int bits, const mixq_w
     const int grid = (int)(N < 4096 ? N : 4096);
     if (bits == 8)
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 8>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w, w->gated, nullptr);
+                           N, K, w->wq, w->s_w, w->gated, nullptr, nullptr, (int64_t)0);
     else if (w->group)
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4, true>), dim3(grid), dim3(kThreads), 0,
-                           st, W, N, K, w->wq, w->s_w, w->gated, w->gsz);
+                           st, W, N, K, w->wq, w->s_w, w->gated, w->gsz, w->rmap,
+                           (int64_t)w->n_out);
     else
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w, w->gated, nullptr);
+                           N, K, w->wq, w->s_w, w->gated, nullptr, nullptr, (int64_t)0);
     return launch_status();
 }
 
@@ -200,6 +244,9 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     if (!state->count) return MIXQ_ERR_INVALID_ARG;
     if (w->gated != 0 && w->gated != 1) return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || bits != 4 || !w->gsz))
+        return MIXQ_ERR_INVALID_ARG;
+    if (w->rmap && (w->group == 0 || w->gated || w->npair < 0 || w->npair % 256 != 0 ||
+                    w->npair > N || w->n_out <= 0 || w->n_out > N))
         return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (w->gated && N % 64 != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
@@ -225,6 +272,7 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     const int grid = (int)(N < MIXQ_GATHER_SLOTS ? N : MIXQ_GATHER_SLOTS);
     hipLaunchKernelGGL(gather_cols_kernel, dim3(grid), dim3(kThreads), 0, st, W, N, (int32_t)K,
                        state->idx, state->count, w->w_out, ld_out, w->k_out,
-                       mode == MIXQ_PACK_FULL ? 1 : 0, w->gated);
+                       mode == MIXQ_PACK_FULL ? 1 : 0, w->gated, w->rmap,
+                       (int64_t)w->n_out);
     return launch_status();
 }

@@ -11,6 +11,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +27,7 @@ PACK_OUTLIER_COLS = 1
 OUT_F32 = 0
 OUT_SWIGLU_F16 = 1
 PROGRESSIVE_GROUP = 128
+ROW_PAD = 0x3FFFFFFF  # padding row of a mixed-precision row map
 OUTLIER_ALIGN = 32
 K_MULTIPLE = 64
 GATHER_SLOTS = 256
@@ -47,7 +49,8 @@ class Weight(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
                 ("k_out", ctypes.c_void_p), ("bits", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("k_cap", ctypes.c_int32), ("gated", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("gsz", ctypes.c_void_p)]
+                ("gsz", ctypes.c_void_p), ("rmap", ctypes.c_void_p), ("npair", ctypes.c_int32),
+                ("n_out", ctypes.c_int32)]
 
 
 _lib = None
@@ -93,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.mixq_gemm_ex.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
                                    P, I64, I32, P, P, ctypes.c_size_t, P]
         L.mixq_gemm_ex.restype = ctypes.c_int
+        L.mixq_mixed_rows.argtypes = [P, I64, P, P]
+        L.mixq_mixed_rows.restype = I64
         L.mixq_gemm_workspace_bytes.argtypes = [I64, I64, I64, I32]
         L.mixq_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.mixq_status_string.argtypes = [ctypes.c_int]
@@ -167,6 +172,10 @@ class PackedWeight:
     gated: int = 0  # 1: W = [W_gate; W_up], packed with 32-row blocks interleaved
     group: int = 0  # PROGRESSIVE_GROUP: progressive group-wise INT4
     gsz: torch.Tensor | None = None  # [N, K/group] uint16: s2 | z << 8
+    # output-feature mixed precision: packed row -> W row | plane << 30
+    rmap: torch.Tensor | None = None
+    npair: int = 0  # packed rows [0, npair) are high / low planes of 8-bit rows
+    n_out: int = 0  # rows of W (columns of Y) when rmap is set
 
     @classmethod
     def create(cls, N: int, K: int, bits: int, k_cap: int, device="cuda",
@@ -184,10 +193,31 @@ class PackedWeight:
                    gsz=(torch.zeros(N * (K // group), dtype=torch.int16, device=device)
                         if group else None))
 
+    @classmethod
+    def create_mixed(cls, salient, K: int, k_cap: int, device="cuda") -> "PackedWeight":
+        """An output-feature mixed-precision weight: the rows flagged in
+        ``salient`` (bool [N_out]) keep 8-bit codes, as a high and a low
+        progressive 4-bit plane; the other rows are progressive INT4."""
+        sal = np.ascontiguousarray(np.asarray(salient, dtype=np.uint8))
+        n_out = int(sal.shape[0])
+        npair = ctypes.c_int32(0)
+        total = int(lib().mixq_mixed_rows(sal.ctypes.data, n_out, None, ctypes.byref(npair)))
+        if total <= 0:
+            raise ValueError("invalid salient flags")
+        rm = np.zeros(total, np.int32)
+        lib().mixq_mixed_rows(sal.ctypes.data, n_out, rm.ctypes.data, ctypes.byref(npair))
+        pw = cls.create(total, K, 4, k_cap, device=device, group=PROGRESSIVE_GROUP)
+        pw.rmap = torch.from_numpy(rm).to(device)
+        pw.npair = int(npair.value)
+        pw.n_out = n_out
+        return pw
+
     def c(self) -> Weight:
         return Weight(self.wq.data_ptr(), self.s_w.data_ptr(), self.w_out.data_ptr(),
                       self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap, self.gated,
-                      self.group, None if self.gsz is None else self.gsz.data_ptr())
+                      self.group, None if self.gsz is None else self.gsz.data_ptr(),
+                      None if self.rmap is None else self.rmap.data_ptr(), self.npair,
+                      self.n_out)
 
     def codes_view(self) -> torch.Tensor:
         """int8 [N, K] (bits 8) or packed uint8 [N, K/2] (bits 4) view of wq."""
@@ -250,11 +280,14 @@ def add_rmsnorm_quantize_act(R: torch.Tensor, D: torch.Tensor, H: torch.Tensor,
 
 def pack_weight(W: torch.Tensor, state: OutlierState, pw: PackedWeight,
                 mode: int = PACK_FULL) -> None:
+    """mixq_pack_weight.  W: fp16 [N, K], or [n_out, K] for a mixed-precision
+    weight (whose packed row count N is larger)."""
     assert W.dtype == torch.float16 and W.is_contiguous()
-    N, K = W.shape
+    assert W.shape[0] == (pw.n_out if pw.rmap is not None else pw.N)
+    K = W.shape[1]
     st = state.c()
     w = pw.c()
-    rc = lib().mixq_pack_weight(_ptr(W), N, K, pw.bits, ctypes.byref(st), mode, ctypes.byref(w),
+    rc = lib().mixq_pack_weight(_ptr(W), pw.N, K, pw.bits, ctypes.byref(st), mode, ctypes.byref(w),
                                 _stream(W.device))
     _check("mixq_pack_weight", rc)
 

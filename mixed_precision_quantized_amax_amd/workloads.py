@@ -15,6 +15,8 @@ Recipe (NumPy PCG64, ``default_rng``):
      the normal draw multiplied by a factor;
   4. W: normal float32 [N, K] with standard deviation ``w_std``;
   5. both cast to float16 (round to nearest even) at the end.
+For an output-feature mixed-precision weight, the 8-bit rows are a seeded
+choice of 10% of the output features (``make_salient``).
 For the decode sequence, a separate stream per step is derived from
 ``SeedSequence([seed, 1 + step])``.  For the RMSNorm fused in front of the
 layer, X serves as the hidden state and the norm's weight is drawn from its
@@ -123,6 +125,17 @@ def make_activation(wl: Workload, seed: int | None = None, M: int | None = None)
     X = rng.standard_normal((m, wl.K), dtype=np.float32)
     _plant(rng, X, ch, wl)
     return _fp16(X)
+
+
+def make_salient(N: int, fraction: float = 0.1, seed: int = 0) -> np.ndarray:
+    """Salient output features for an output-feature mixed-precision weight:
+    round(fraction * N) rows drawn without replacement (the MixLLM page keeps
+    10% of them at 8 bits; its global ranking by estimated loss needs a
+    trained model, so a seeded choice stands in for it).  bool [N]."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, N, 0x5A]))
+    sal = np.zeros(N, bool)
+    sal[rng.choice(N, int(round(fraction * N)), replace=False)] = True
+    return sal
 
 
 def make_norm_gamma(wl: Workload, seed: int | None = None) -> np.ndarray:
