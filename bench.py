@@ -101,7 +101,9 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0, salient=None):
     Xo = [torch.zeros(wl.M * ld, dtype=torch.float16, device=dev) for _ in range(copies)]
     Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    ws = mixq.gemm_workspace(wl.M, wl.N, wl.K, wl.bits, dev)  # split K (thin shapes only)
+    # split-K workspace (thin shapes, and the tail of a product a little over
+    # one round of 256 x 256 tiles); N = the packed row count
+    ws = mixq.gemm_workspace(wl.M, packs[0].N, wl.K, wl.bits, dev)
     steps_c = [mixq.LayerStep(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws)
                for c in range(copies)]
 

@@ -339,14 +339,23 @@ int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  * split in two blocks.  Both store their exact int32 partial tile in ws; the
  * second to finish adds the other's and runs the epilogue.  No block waits
  * for another.  Integer partial sums make acc and Y bit-identical to the
- * unsplit product.  Otherwise, or when ws is NULL or smaller than required,
- * the call is mixq_gemm.
+ * unsplit product.
+ *
+ * A large product whose 256 x 256 tiles need one round of the device plus a
+ * short second one runs the columns that fill one round on 256 x 256 tiles
+ * and the remaining columns as a second launch of 128 x 128 tiles (with or
+ * without ws); with ws, that launch also splits K two or four ways in the
+ * same way, so that its blocks fill the device.
+ *
+ * Otherwise, or when ws is NULL or smaller than required, the call is
+ * mixq_gemm.
  *
  *   ws        device memory of ws_bytes, 16-byte aligned; its first 4096 bytes
  *             (tile counters) must be zero-filled once by the caller, after
  *             which every completed call leaves them zero.  Calls sharing a
  *             ws must not overlap (one stream, or serialized).
  *   ws_bytes  at least mixq_gemm_workspace_bytes(M, N, K, bits) for the split
+ *             (N = w->N, the packed row count of a mixed-precision weight)
  * Other arguments and errors: as mixq_gemm.
  */
 int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
@@ -380,8 +389,10 @@ int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  void *stream);
 
 /* Workspace bytes mixq_gemm_ws needs to split this product on a device with
- * 256 compute units (MI355X): 4096 bytes of tile counters plus two 64 KiB
- * partial tiles per 128 x 128 output tile; 0 when the product is not split. */
+ * 256 compute units (MI355X): 4096 bytes of tile counters plus, per split
+ * 128 x 128 output tile, one 64 KiB partial tile per part (two for a thin
+ * product, two or four for the tail of a large one); 0 when nothing is
+ * split. */
 size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
 
 /*

@@ -73,8 +73,11 @@ extern "C" {
 size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
     using namespace mixq;
     const int S = split_plan(M, N, K, bits, 256);
-    if (S <= 1) return 0;
-    return (size_t)split_workspace_bytes(M, N, S);
+    if (S > 1) return (size_t)split_workspace_bytes(M, N, S);
+    int St = 1;
+    const int n_split = tail_plan(M, N, K, 256, &St);
+    if (n_split > 0 && St > 1) return (size_t)tail_workspace_bytes(M, N, n_split, St);
+    return 0;
 }
 
 

@@ -60,6 +60,9 @@ struct GemmArgs {
     int64_t ldy;
     int32_t* acc_debug;
     int32_t tiles_m, tiles_n;
+    // this launch's output columns: tiles start at n_begin and cover
+    // [n_begin, n_end) (a launch may take only part of N, see gemm_impl)
+    int32_t n_begin, n_end;
     // split K (K-pair kernels): ksplit blocks per output tile, 1 or 2
     int32_t ksplit;
     int32_t* sync;  // [tiles] arrival counters, zero between calls
@@ -73,6 +76,7 @@ struct GemmArgs {
     // and 32 low planes; Y columns are W rows < n_out
     const int32_t* rmap;
     int32_t npair, n_out;
+    int32_t wbits;  // 8 or 4 (host side: which launcher)
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -207,7 +211,7 @@ void gemm_kernel(GemmArgs a) {
     const int within = tbid - group * gm * a.tiles_n;
     const int tm = first_m + within % gsize;
     const int tn = within / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM, n0 = a.n_begin + tn * BN;
 
     const int K = a.K;
     const int KT = K / kBK;
@@ -464,68 +468,6 @@ void gemm_kernel(GemmArgs a) {
             if (p + 3 < KP) gload(rA, p + 3, SA);
         }
         __syncthreads();
-        if (BM == kSplitTile && a.ksplit > 1) {
-            // Split K in two: both blocks of the tile store their exact int32
-            // partial tile, then arrive on the tile counter; the second to
-            // arrive adds the other's partial and finishes the tile, the
-            // first leaves.  Nobody waits for anybody.  The partials are
-            // stored and loaded with device-scope coherent accesses (the sc1
-            // bit: what relaxed agent-scope atomics compile to), 16 bytes per
-            // lane -- dword-wide coherent loads took 15 us for a 64 KiB
-            // partial, these 1.3 us -- and each wave's stores are
-            // acknowledged before its block arrives, so the second block
-            // reads complete data.  Integer sums: the result does not depend
-            // on the arrival order.
-            constexpr int kF = C::kFM * C::kFN;
-            constexpr int64_t kSlot = (int64_t)C::kNW * kF * 16 * kWave;  // int32 per partial
-            constexpr int kCoherent = 16;  // buffer cache-policy bit sc1 (device scope)
-            const int S = a.ksplit;
-            // slot layout, 16-byte units: [wave][fragment][e / 4][lane]
-            const __amdgpu_buffer_rsrc_t rP =
-                make_rsrc(reinterpret_cast<const uint8_t*>(a.part + (int64_t)tbid * S * kSlot),
-                          (int64_t)S * kSlot * 4);
-            auto unit = [&](int t, int f, int q) {
-                return (int)((t * kSlot / 4 + (int64_t)((wave * kF + f) * 4 + q) * kWave + lane) * 16);
-            };
-#pragma unroll
-            for (int i = 0; i < C::kFM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::kFN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                       acc[i][j][4 * q + 3]};
-                        __builtin_amdgcn_raw_buffer_store_b128(v, rP, unit(split, i * C::kFN + j, q), 0,
-                                                               kCoherent);
-                    }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            __shared__ int second;
-            if (tid == 0) {
-                const int old = __hip_atomic_fetch_add(a.sync + tbid, 1, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-                second = old == S - 1;
-                // every block has arrived: clear the counter for the next call
-                if (old == S - 1)
-                    __hip_atomic_store(a.sync + tbid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
-            if (!second) return;
-            for (int t = 0; t < S; ++t) {
-                if (t == split) continue;
-#pragma unroll
-                for (int i = 0; i < C::kFM; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::kFN; ++j)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
-                                rP, unit(t, i * C::kFN + j, q), 0, kCoherent);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
-                        }
-            }
-        }
     } else if constexpr (STAGES == 2) {
         // ---- register-staged, double-buffered LDS ------------------------------------
         // Global loads run PF tiles ahead of the multiply, in PF register sets.
@@ -660,19 +602,25 @@ void gemm_kernel(GemmArgs a) {
             AFr fa0, fa1;
             BFr fb0, fb1;
             Regs S0, S1;
-            gload(0, S0);
-            gload(1, S1);
+            // this block's K tiles kb .. kb + KTs - 1 (a split K range on
+            // 128 x 128 tiles; the host keeps each range a whole number of
+            // 128-channel groups)
+            const int KTs = BM == kSplitTile ? KT / a.ksplit : KT;
+            const int kb = BM == kSplitTile ? split * KTs : 0;
+            gload(kb, S0);
+            gload(kb + 1, S1);
             lstore(S0, 0);
             lstore(S1, 1);
             // Same issue order as the loop (S0's tile before S1's), and no
             // condition: every path into the loop then has S1's loads newest,
             // so the waits derived at the loop head leave them in flight.  For
-            // KT < 4 the extra loads read past the row's K range, which stays
-            // inside the buffer (or reads zeros past its end) and is unused.
+            // KTs < 4 the extra loads read past the block's K range (the next
+            // range, or the next row), which stays inside the buffer (or reads
+            // zeros past its end) and is unused.
             __builtin_amdgcn_sched_barrier(0);
-            gload(2, S0);
+            gload(kb + 2, S0);
             __builtin_amdgcn_sched_barrier(0);
-            gload(3, S1);
+            gload(kb + 3, S1);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             lread(sA0, sB0, fa0, fb0);
@@ -680,11 +628,11 @@ void gemm_kernel(GemmArgs a) {
             int k = 0;
             // steady state: every read, write and load of the pair exists, so
             // the body is one basic block and the interleave pattern applies
-            for (; k + 6 <= KT; k += 2) {
+            for (; k + 6 <= KTs; k += 2) {
                 lread(sA1, sB1, fa1, fb1);
                 mfmas(fa0, fb0);
                 lstore(S0, 0);
-                gload(k + 4, S0);
+                gload(kb + k + 4, S0);
                 sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN),
                                  C::kAI + (BITS == 8 ? C::kBI : 2 * C::kBI4),
                                  C::kAI + (BITS == 8 ? C::kBI : C::kBI4)>();
@@ -692,23 +640,23 @@ void gemm_kernel(GemmArgs a) {
                 lread(sA0, sB0, fa0, fb0);
                 mfmas(fa1, fb1);
                 lstore(S1, 1);
-                gload(k + 5, S1);
+                gload(kb + k + 5, S1);
                 sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN),
                                  C::kAI + (BITS == 8 ? C::kBI : 2 * C::kBI4),
                                  C::kAI + (BITS == 8 ? C::kBI : C::kBI4)>();
                 __syncthreads();
             }
-            // last pairs (KT even)
-            for (; k < KT; k += 2) {
+            // last pairs (KTs even)
+            for (; k < KTs; k += 2) {
                 lread(sA1, sB1, fa1, fb1);
                 mfmas(fa0, fb0);
-                if (k + 2 < KT) lstore(S0, 0);
-                if (k + 4 < KT) gload(k + 4, S0);
+                if (k + 2 < KTs) lstore(S0, 0);
+                if (k + 4 < KTs) gload(kb + k + 4, S0);
                 __syncthreads();
-                if (k + 2 < KT) lread(sA0, sB0, fa0, fb0);
+                if (k + 2 < KTs) lread(sA0, sB0, fa0, fb0);
                 mfmas(fa1, fb1);
-                if (k + 3 < KT) lstore(S1, 1);
-                if (k + 5 < KT) gload(k + 5, S1);
+                if (k + 3 < KTs) lstore(S1, 1);
+                if (k + 5 < KTs) gload(kb + k + 5, S1);
                 __syncthreads();
             }
         } else if constexpr (PF == 3) {
@@ -788,15 +736,20 @@ void gemm_kernel(GemmArgs a) {
                 __syncthreads();
             }
         } else if constexpr (PF == 1) {
+            // this block's K tiles kb .. kb + KTs - 1 (a split K range on
+            // 128 x 128 tiles; the host keeps each range a whole number of
+            // 128-channel groups)
+            const int KTs = BM == kSplitTile ? KT / a.ksplit : KT;
+            const int kb = BM == kSplitTile ? split * KTs : 0;
             Regs R;
-            gload(0, R);
+            gload(kb, R);
             lstore(R, 0);
             __syncthreads();
-            for (int kt = 0; kt < KT; ++kt) {
+            for (int kt = 0; kt < KTs; ++kt) {
                 const int cur = kt & 1;
-                if (kt + 1 < KT) gload(kt + 1, R);
+                if (kt + 1 < KTs) gload(kb + kt + 1, R);
                 mma_tile(cur ? sA1 : sA0, cur ? sB1 : sB0);
-                if (kt + 1 < KT) lstore(R, cur ^ 1);
+                if (kt + 1 < KTs) lstore(R, cur ^ 1);
                 __syncthreads();
             }
         } else {
@@ -867,6 +820,70 @@ void gemm_kernel(GemmArgs a) {
             }
         }
         __syncthreads();
+    }
+
+    if (BM == kSplitTile && a.ksplit > 1) {
+        // Split K: every block of the tile stores its exact int32 partial
+        // tile, then arrives on the tile counter; the last to arrive adds
+        // the others' partials and finishes the tile, the others leave.
+        // Nobody waits for anybody.  The partials are
+        // stored and loaded with device-scope coherent accesses (the sc1
+        // bit: what relaxed agent-scope atomics compile to), 16 bytes per
+        // lane -- dword-wide coherent loads took 15 us for a 64 KiB
+        // partial, these 1.3 us -- and each wave's stores are
+        // acknowledged before its block arrives, so the second block
+        // reads complete data.  Integer sums: the result does not depend
+        // on the arrival order.  (The K-pair kernels arrive here after the
+        // barrier that ends their loop, the others after their last one.)
+        constexpr int kF = C::kFM * C::kFN;
+        constexpr int64_t kSlot = (int64_t)C::kNW * kF * 16 * kWave;  // int32 per partial
+        constexpr int kCoherent = 16;  // buffer cache-policy bit sc1 (device scope)
+        const int S = a.ksplit;
+        // slot layout, 16-byte units: [wave][fragment][e / 4][lane]
+        const __amdgpu_buffer_rsrc_t rP =
+            make_rsrc(reinterpret_cast<const uint8_t*>(a.part + (int64_t)tbid * S * kSlot),
+                      (int64_t)S * kSlot * 4);
+        auto unit = [&](int t, int f, int q) {
+            return (int)((t * kSlot / 4 + (int64_t)((wave * kF + f) * 4 + q) * kWave + lane) * 16);
+        };
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                   acc[i][j][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rP, unit(split, i * C::kFN + j, q), 0,
+                                                           kCoherent);
+                }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        __shared__ int second;
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(a.sync + tbid, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            second = old == S - 1;
+            // every block has arrived: clear the counter for the next call
+            if (old == S - 1)
+                __hip_atomic_store(a.sync + tbid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!second) return;
+        for (int t = 0; t < S; ++t) {
+            if (t == split) continue;
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+                            rP, unit(t, i * C::kFN + j, q), 0, kCoherent);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+                    }
+        }
     }
 
     // ---- epilogue: dequantize and scale in registers, in place ---------------------
@@ -1047,7 +1064,7 @@ template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1, bool
 int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
     static_assert(!MIXED || PROG, "mixed-precision weights are progressive INT4");
     a.tiles_m = (a.M + BM - 1) / BM;
-    a.tiles_n = (a.N + BN - 1) / BN;
+    a.tiles_n = (a.n_end - a.n_begin + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit), block(WM * WN * kWave);
     if (debug)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true, PROG, MIXED>), grid,
@@ -1075,6 +1092,7 @@ enum {
     kCfg256x256KP = 12,  // 4 waves of 128x128, 128-byte K pairs (whole-line loads)
     kCfg256x256KS = 13,  // as 12, issue order pinned slot by slot
     kCfg128x128KP = 14,  // 4 waves of 64x64, 128-byte K pairs
+    kCfg128x128SP = 15,  // 4 waves of 64x64, cross-tile software pipeline (INT4 weights)
 };
 
 int forced_cfg() {
@@ -1086,12 +1104,13 @@ int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     const int f = forced_cfg();
     if ((f == kCfg256x256P2 || f == kCfg256x128P2 || f == kCfg256x256AD || f == kCfg256x128AD ||
          f == kCfg256x256SP || f == kCfg256x128SP || f == kCfg256x256KP ||
-         f == kCfg256x256KS || f == kCfg128x128KP) &&
+         f == kCfg256x256KS || f == kCfg128x128KP || f == kCfg128x128SP) &&
         K % 128 != 0)
         return kCfg128x128;
+    if (f == kCfg128x128SP && bits == 8) return kCfg128x128KP;
     if ((f == kCfg256x256KP || f == kCfg256x256KS) && bits == 4) return kCfg256x256SP;
     if (f == kCfg128x128KP && bits == 4) return kCfg128x128;
-    if (f >= 1 && f <= 14 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
+    if (f >= 1 && f <= 15 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
     // Large 256x256 tiles (software-pipelined when K allows) once they give
     // about one tile per CU; 128x128 tiles (K pairs for INT8 weights) for
     // thinner products.
@@ -1103,8 +1122,8 @@ int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     return bits == 8 && K % 128 == 0 ? kCfg128x128KP : kCfg128x128;
 }
 
-int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
-    switch (pick_cfg(a.M, a.N, a.K, 8)) {
+int launch_w8(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
+    switch (cfg) {
         case kCfg256x256: return launch_cfg<256, 256, 2, 2, 8, 2>(a, debug, st);
         case kCfg256x128: return launch_cfg<256, 128, 2, 2, 8, 2>(a, debug, st);
         case kCfg256x256D: return launch_cfg<256, 256, 2, 2, 8, 3>(a, debug, st);
@@ -1123,8 +1142,8 @@ int launch_w8(const GemmArgs& a, bool debug, hipStream_t st) {
 }
 
 template <bool PROG, bool MIXED = false>
-int launch_w4_t(const GemmArgs& a, bool debug, hipStream_t st) {
-    switch (pick_cfg(a.M, a.N, a.K, 4)) {
+int launch_w4_t(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
+    switch (cfg) {
         case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
         case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
         case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG, MIXED>(a, debug, st);
@@ -1133,13 +1152,18 @@ int launch_w4_t(const GemmArgs& a, bool debug, hipStream_t st) {
         case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG, MIXED>(a, debug, st);
         case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
         case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
+        case kCfg128x128SP: return launch_cfg<128, 128, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
         default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
     }
 }
 
-int launch_w4(const GemmArgs& a, bool debug, hipStream_t st) {
-    if (a.rmap) return launch_w4_t<true, true>(a, debug, st);
-    return a.gsz ? launch_w4_t<true>(a, debug, st) : launch_w4_t<false>(a, debug, st);
+int launch_w4(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
+    if (a.rmap) return launch_w4_t<true, true>(a, cfg, debug, st);
+    return a.gsz ? launch_w4_t<true>(a, cfg, debug, st) : launch_w4_t<false>(a, cfg, debug, st);
+}
+
+int launch_bits(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
+    return a.wbits == 8 ? launch_w8(a, cfg, debug, st) : launch_w4(a, cfg, debug, st);
 }
 
 }  // namespace
@@ -1194,6 +1218,9 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.ldy = ldy;
     a.acc_debug = acc_debug;
     a.tiles_m = a.tiles_n = 0;
+    a.n_begin = 0;
+    a.n_end = a.N;
+    a.wbits = w->bits;
     a.ksplit = 1;
     a.sync = nullptr;
     a.part = nullptr;
@@ -1215,8 +1242,34 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
         a.part = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + kSplitSyncBytes);
         return launch_cfg<128, 128, 2, 2, 8, 4, 5>(a, acc_debug != nullptr, st);
     }
-    return w->bits == 8 ? launch_w8(a, acc_debug != nullptr, st)
-                        : launch_w4(a, acc_debug != nullptr, st);
+    const bool dbg = acc_debug != nullptr;
+    // Tail split: when the 256 x 256 tiles come to one round of the device
+    // plus a short second round (N a little above a multiple of the columns
+    // one round holds), the second round would cost a whole tile time for a
+    // few tiles.  Instead the 256 x 256 launch takes the tile columns that
+    // fill one round, and a second launch covers the remaining columns with
+    // 128 x 128 tiles, four times as many blocks, each a quarter of the work.
+    // With a workspace the tail's K is split as well, so that its blocks
+    // fill the device (tail_plan).
+    int St = 1;
+    const int n_split = f == kCfgAuto && (pc == kCfg256x256KS || pc == kCfg256x256SP)
+                            ? tail_plan(M, w->N, w->K, device_cu_count(), &St)
+                            : 0;
+    if (n_split > 0) {
+        const int tail_cfg = w->bits == 8 ? kCfg128x128KP : kCfg128x128SP;
+        GemmArgs a2 = a;
+        a.n_end = n_split;
+        a2.n_begin = n_split;
+        if (St > 1 && ws && (int64_t)ws_bytes >= tail_workspace_bytes(M, w->N, n_split, St)) {
+            a2.ksplit = St;
+            a2.sync = static_cast<int32_t*>(ws);
+            a2.part = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + kSplitSyncBytes);
+        }
+        rc = launch_bits(a, pc, dbg, st);
+        if (rc != MIXQ_OK) return rc;
+        return launch_bits(a2, tail_cfg, dbg, st);
+    }
+    return launch_bits(a, pc, dbg, st);
 }
 
 }  // namespace

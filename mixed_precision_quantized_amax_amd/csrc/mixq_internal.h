@@ -36,6 +36,27 @@ inline int split_plan(int64_t M, int64_t N, int64_t K, int bits, int cus) {
 inline int64_t split_workspace_bytes(int64_t M, int64_t N, int S) {
     return kSplitSyncBytes + split_tiles(M, N) * S * kSplitSlotBytes;
 }
+// Tail split of a product on 256 x 256 tiles (K a multiple of 128) that
+// needs one round of the device plus a short second one: the columns
+// [0, n_split) keep 256 x 256 tiles, the rest run as 128 x 128 tiles with K
+// split *S ways (S in 1, 2, 4) so that the tail fills about two blocks per
+// compute unit.  Returns n_split, or 0 for no tail split.
+inline int tail_plan(int64_t M, int64_t N, int64_t K, int cus, int* S) {
+    *S = 1;
+    if (M <= 0 || N <= 0 || K % 128 != 0 || cus <= 0) return 0;
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    if (tm * tn < 192) return 0;  // not the 256x256 path
+    const int64_t fit = cus / tm;  // whole tile columns in one round
+    if (fit <= 0 || tn <= fit || 2 * (tn - fit) * tm > cus) return 0;
+    const int64_t n_split = fit * 256;
+    const int64_t tail = split_tiles(M, N - n_split);
+    if (tail <= kSplitSyncBytes / 4)
+        while (*S < 4 && tail * *S * 2 <= 2 * (int64_t)cus && K % (128 * 2 * *S) == 0) *S *= 2;
+    return (int)n_split;
+}
+inline int64_t tail_workspace_bytes(int64_t M, int64_t N, int64_t n_split, int S) {
+    return kSplitSyncBytes + split_tiles(M, N - n_split) * S * kSplitSlotBytes;
+}
 
 inline bool valid_k(int64_t K) { return K > 0 && K % MIXQ_K_MULTIPLE == 0 && K <= MIXQ_K_MAX; }
 

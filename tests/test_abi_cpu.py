@@ -191,6 +191,12 @@ def test_gemm_workspace_bytes():
     assert L.mixq_gemm_workspace_bytes(256, 8192, 8192, 4) == 0       # INT4: no split
     assert L.mixq_gemm_workspace_bytes(256, 8192, 8192 - 128, 8) == 0  # K % 256 != 0
     assert L.mixq_gemm_workspace_bytes(0, 8192, 8192, 8) == 0
+    # a 256 x 256 product one round plus a short tail: columns [8192, N) as
+    # 128 x 128 tiles with K split four ways (16 x 8 tail tiles)
+    assert L.mixq_gemm_workspace_bytes(2048, 9165, 8192, 4) == 4096 + 16 * 8 * 4 * slot
+    assert L.mixq_gemm_workspace_bytes(2048, 8448, 1024, 8) == 4096 + 16 * 2 * 4 * slot
+    assert L.mixq_gemm_workspace_bytes(2048, 8448, 128, 8) == 0       # K too short to split
+    assert L.mixq_gemm_workspace_bytes(2048, 16384, 8192, 8) == 0     # two full rounds
 
 
 def test_gemm_ws_validation():

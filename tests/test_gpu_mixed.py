@@ -51,7 +51,7 @@ def salient_set(N, S, seed):
     return sal
 
 
-def run_mixed(X, W, sal, tau, k_cap, acc=True):
+def run_mixed(X, W, sal, tau, k_cap, acc=True, ws=False):
     M, K = X.shape
     Wd = to_dev(W.view(np.float16))
     st = mixq.OutlierState.create(K, k_cap)
@@ -65,10 +65,11 @@ def run_mixed(X, W, sal, tau, k_cap, acc=True):
     mixq.pack_weight(Wd, st, pw, mixq.PACK_OUTLIER_COLS)
     Y = torch.full((M, W.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
     dbg = torch.zeros(M, pw.N, dtype=torch.int32, device="cuda") if acc else None
-    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg)
+    wsb = mixq.gemm_workspace(M, pw.N, K, 4) if ws else None
+    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg, wsb)
     torch.cuda.synchronize()
     return dict(pw=pw, Y=Y.cpu().numpy(), acc=None if dbg is None else dbg.cpu().numpy(),
-                count=int(st.count.cpu()[0]))
+                count=int(st.count.cpu()[0]), ws=wsb)
 
 
 def packed_values(pw):
@@ -118,7 +119,7 @@ def check_pack(orc, g, W, sal, W_out):
     return codes, scales, hi, lo, p4, src
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11"], indirect=True)
+@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11", "15"], indirect=True)
 @pytest.mark.parametrize("M,K,N,S,n_act", [(37, 256, 128, 5, 3), (130, 1024, 384, 100, 9),
                                            (257, 2048, 520, 129, 0), (64, 1024, 256, 0, 40),
                                            (100, 512, 300, 300, 4)])
@@ -156,7 +157,7 @@ def test_mixed_full_size(orc):
     X = workloads.make_activation(wl)
     W = workloads.make_weight(wl)
     sal = workloads.make_salient(wl.N)
-    g = run_mixed(X, W, sal, wl.tau, 256)
+    g = run_mixed(X, W, sal, wl.tau, 256, ws=True)
     o = OracleLayer(W=W, bits=8, tau=wl.tau, k_cap=256, ldo=mixq.outlier_ld(256), oracle=orc)
     r = o.step(X, products=False)
     assert g["count"] == r.count

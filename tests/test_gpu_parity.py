@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 TILES = {"auto": "0", "256x256": "1", "128x128": "2", "256x256_lds3": "3", "256x128": "4",
          "256x256_lds4": "5", "256x256_pf2": "6", "256x128_pf2": "7", "256x256_adirect": "8",
          "256x128_adirect": "9", "256x256_swp": "10", "256x128_swp": "11",
-         "256x256_kpair": "12", "256x256_kpin": "13", "128x128_kpair": "14"}
+         "256x256_kpair": "12", "256x256_kpin": "13", "128x128_kpair": "14",
+         "128x128_swp": "15"}
 
 
 @pytest.fixture(scope="module")

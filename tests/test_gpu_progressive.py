@@ -40,7 +40,7 @@ def unpack_u4(packed: np.ndarray, K: int) -> np.ndarray:
     return out.reshape(N, K)
 
 
-def run_progressive(X, W, tau, k_cap, acc=True):
+def run_progressive(X, W, tau, k_cap, acc=True, ws=False):
     M, K = X.shape
     N = W.shape[0]
     Wd = to_dev(W.view(np.float16))
@@ -55,10 +55,11 @@ def run_progressive(X, W, tau, k_cap, acc=True):
     mixq.pack_weight(Wd, st, pw, mixq.PACK_OUTLIER_COLS)
     Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     dbg = torch.zeros(M, N, dtype=torch.int32, device="cuda") if acc else None
-    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg)
+    wsb = mixq.gemm_workspace(M, pw.N, K, 4) if ws else None
+    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg, wsb)
     torch.cuda.synchronize()
     return dict(pw=pw, Y=Y.cpu().numpy(), acc=None if dbg is None else dbg.cpu().numpy(),
-                count=int(st.count.cpu()[0]))
+                count=int(st.count.cpu()[0]), ws=wsb)
 
 
 def check_codes(orc, g, W):
@@ -74,7 +75,7 @@ def check_codes(orc, g, W):
     return q8p, s1
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11"], indirect=True)
+@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11", "15"], indirect=True)
 @pytest.mark.parametrize("M,K,N,n_out", [(37, 256, 128, 3), (130, 1024, 384, 9),
                                          (257, 2048, 520, 0), (64, 4096, 256, 40)])
 def test_progressive_random(orc, tile, M, K, N, n_out):
