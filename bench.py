@@ -69,28 +69,21 @@ def algorithmic_bytes(wl, k: int) -> int:
             + 2 * kp * (wl.M + wl.N) + 4 * wl.M * wl.N)
 
 
-def run_gpu(wl, steps: int, warmup: int, group: int = 0, salient=None):
-    """group: 0, or the progressive INT4 group size (INT4 workloads).
-    salient: None, or bool [N]: an output-feature mixed-precision weight
-    (those rows at 8 bits as two progressive planes, the rest progressive
-    INT4)."""
+def run_gpu(wl, steps: int, warmup: int, group: int = 0):
+    """group: 0, or the progressive INT4 group size (INT4 workloads)."""
     import torch
     from mixed_precision_quantized_amax_amd import mixq, workloads
 
     dev = torch.device("cuda", 0)
-    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits} group={group}"
-        f" salient={None if salient is None else int(salient.sum())}")
+    log(f"[bench] workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} bits={wl.bits} group={group}")
     W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
     X0 = torch.from_numpy(workloads.make_activation(wl)).to(dev)
     k_cap = 256
     wq_bytes = wl.N * wl.K * wl.bits // 8
     copies = int(min(8, max(2, math.ceil(CACHE_DEFEAT_BYTES / (wq_bytes + 3 * wl.M * wl.K)))))
     state = mixq.OutlierState.create(wl.K, k_cap, dev)
-    if salient is None:
-        packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev, group=group)
-                 for _ in range(copies)]
-    else:
-        packs = [mixq.PackedWeight.create_mixed(salient, wl.K, k_cap, dev) for _ in range(copies)]
+    packs = [mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev, group=group)
+             for _ in range(copies)]
     for p in packs:
         mixq.pack_weight(W, state, p, mixq.PACK_FULL)
     # activation copies: the same values in different buffers
@@ -173,7 +166,62 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0, salient=None):
     act_ms = g0.elapsed_time(g1) / steps
     flag = int(state.flag.cpu()[0])
     return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm_ms=gemm_ms, act_ms=act_ms,
-                count=count, flag=flag, copies=copies, packed_rows=packs[0].N)
+                count=count, flag=flag, copies=copies)
+
+
+def run_mixed(wl, steps: int, warmup: int, salient):
+    """Output-feature mixed precision on the workload's shape: the salient
+    rows as an INT8 row subset, the others as progressive INT4, one
+    activation pass, then both outlier-column gathers and both products into
+    one Y."""
+    import torch
+    from mixed_precision_quantized_amax_amd import mixq, workloads
+
+    dev = torch.device("cuda", 0)
+    log(f"[bench] mixed features on {wl.name}: {int(salient.sum())} of {wl.N} rows at 8 bits")
+    W = torch.from_numpy(workloads.make_weight(wl)).to(dev)
+    X0 = torch.from_numpy(workloads.make_activation(wl)).to(dev)
+    k_cap = 256
+    copies = 4
+    state = mixq.OutlierState.create(wl.K, k_cap, dev)
+    mws = [mixq.MixedWeight.create(salient, wl.K, k_cap, dev) for _ in range(copies)]
+    for m in mws:
+        m.pack(W, state, mixq.PACK_FULL)
+    Xs = [X0.clone() for _ in range(copies)]
+    ld = mixq.outlier_ld(k_cap)
+    Xq = [torch.empty(wl.M, wl.K, dtype=torch.int8, device=dev) for _ in range(copies)]
+    sx = [torch.empty(wl.M, dtype=torch.float32, device=dev) for _ in range(copies)]
+    Xo = [torch.zeros(wl.M * ld, dtype=torch.float16, device=dev) for _ in range(copies)]
+    Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
+    ws = mws[0].workspaces(wl.M, dev)
+
+    def act(i):
+        c = i % copies
+        mixq.quantize_act(Xs[c], wl.tau, state, Xq[c], sx[c], Xo[c])
+        mws[c].pack(W, state, mixq.PACK_OUTLIER_COLS)
+
+    def gemm(i):
+        c = i % copies
+        mws[c].gemm(Xq[c], sx[c], Xo[c], state, Y, ws=ws)
+
+    for i in range(warmup):
+        act(i)
+        gemm(i)
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fns in (("ms_step", (act, gemm)), ("gemm_ms", (gemm,)), ("act_ms", (act,))):
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            for f in fns:
+                f(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) / steps
+    res["rows"] = (mws[0].w8.N if mws[0].w8 is not None else 0,
+                   mws[0].w4.N if mws[0].w4 is not None else 0)
+    return res
 
 
 def norm_act_bytes(wl, k: int) -> int:
@@ -516,16 +564,16 @@ def main():
             "ms_per_step": round(r4["ms_step"], 4),
             "weights": "progressive group-wise INT4, groups of 128 (rebuilt to INT8 in the loader)"}
         sal = workloads.make_salient(w4.N)
-        r5 = run_gpu(w4, max(10, args.steps // 2), args.warmup, salient=sal)
+        r5 = run_mixed(w4, max(10, args.steps // 2), args.warmup, sal)
         others["prefill_w4_mixed_features"] = {
             "step_tops": round(w4.ops / (r5["ms_step"] / 1e3) / 1e12, 1),
             "gemm_tops": round(w4.ops / (r5["gemm_ms"] / 1e3) / 1e12, 1),
             "gemm_us": round(r5["gemm_ms"] * 1e3, 1),
             "act_quant_us": round(r5["act_ms"] * 1e3, 1),
             "ms_per_step": round(r5["ms_step"], 4),
-            "packed_rows": r5["packed_rows"],
-            "weights": f"{int(sal.sum())} of {w4.N} output features 8-bit (two progressive "
-                       "4-bit planes each), the rest progressive INT4; TOPS count 2*M*N*K"}
+            "weights": f"{r5['rows'][0]} of {w4.N} output features 8-bit (an INT8 row subset), "
+                       f"{r5['rows'][1]} progressive INT4; two products into one Y; "
+                       "TOPS count 2*M*N*K"}
         dwl = workloads.WORKLOADS["decode_seq"]
         d = run_decode_sequence(dwl)
         others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),

@@ -77,7 +77,6 @@ enum {
                                         set left unchanged                      */
 
 #define MIXQ_PROGRESSIVE_GROUP 128   /* channels per group of progressive INT4  */
-#define MIXQ_ROW_PAD 0x3FFFFFFF      /* padding row of a mixed-precision map    */
 
 /* output modes of mixq_gemm_ex */
 #define MIXQ_OUT_F32 0               /* Y fp32 [M, N]                            */
@@ -146,19 +145,15 @@ typedef struct mixq_weight {
                           INT4 nibble layout.                                      */
     uint16_t *gsz;     /* group != 0: [N, K/128], s2 | z << 8 for each row and
                           group (device memory, written by mixq_pack_weight)    */
-    const int32_t *rmap; /* NULL, or (progressive INT4 only) output-feature mixed
-                          precision (MixLLM page): [N] device map of packed rows,
-                          from mixq_mixed_rows.  Entry = W row | plane << 30;
-                          plane 0: a 4-bit progressive row; 1 and 2: the high
-                          and low planes of an 8-bit row (code = 16 h + l: h in
-                          [-8, 7] as 4-bit value h + 8 with s2 = 16, z = 8; l in
-                          [0, 15] with s2 = 1, z = 0), in 64-row blocks of 32
-                          high then the same 32 low rows; W row MIXQ_ROW_PAD
-                          marks padding, and so does any W row >= n_out.  Y
-                          column of a packed row = its W row; the product adds
-                          each block's two planes.  Not with gated weights.  */
-    int32_t npair;     /* rmap != NULL: rows [0, npair) hold planes; a multiple
-                          of 256                                                  */
+    const int32_t *rmap; /* NULL, or a row subset: [N] device array, the W row
+                          each packed row quantizes, which is also the Y column
+                          the product writes for it.  Output-feature mixed
+                          precision (MixLLM page) is two such weights over one
+                          W: the salient rows at bits 8 and the others at bits
+                          4, each multiplied by its own mixq_gemm call into the
+                          same Y.  An entry outside [0, n_out) packs zeros and
+                          writes nothing.  Bits 8, or bits 4 with a group; not
+                          with gated weights or the SwiGLU output.             */
     int32_t n_out;     /* rmap != NULL: rows of W = output features (columns of
                           Y); ldy >= n_out                                        */
 } mixq_weight;
@@ -276,10 +271,10 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *   in mixq_weight;  w_out[n, j] = W[n, idx[j]] for j < count, then zeros.
  *
  *   W      fp16 [N, K] device, row-major (ld = K); [w->n_out, K] when w->rmap
- *          is set.  Keep it: the outlier columns are gathered from it again
- *          when the set grows.
+ *          is set (packed row n then quantizes W row rmap[n]).  Keep it: the
+ *          outlier columns are gathered from it again when the set grows.
  *   N, K   >= 1; K multiple of 64, <= MIXQ_K_MAX; N = w->N (the packed row
- *          count, for a mixed-precision weight)
+ *          count: the length of rmap when it is set)
  *   bits   8 or 4
  *   state  the activation state whose set selects the outlier columns
  *   mode   MIXQ_PACK_FULL: everything.  MIXQ_PACK_OUTLIER_COLS: re-gather
@@ -291,10 +286,10 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *          same in the FULL call and every OUTLIER_COLS call
  * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for w->gated not 0
  *         or 1, w->group not 0 or MIXQ_PROGRESSIVE_GROUP, a group with bits 8,
- *         or a null w->gsz with a group, and for a w->rmap without a group,
- *         with a gated weight, with npair not a multiple of 256 or above N,
- *         or with n_out not in [1, N]; MIXQ_ERR_UNSUPPORTED_SHAPE for a
- *         gated N not a multiple of 64 or a group not dividing K.
+ *         or a null w->gsz with a group, and for a w->rmap with a gated
+ *         weight, with symmetric INT4 or with n_out < 1;
+ *         MIXQ_ERR_UNSUPPORTED_SHAPE for a gated N
+ *         not a multiple of 64 or a group not dividing K.
  */
 int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
                      const mixq_act_state *state, int32_t mode, const mixq_weight *w,
@@ -316,11 +311,10 @@ int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
  *   state           the activation state (count and k_cap are used)
  *   w               packed weight, gathered for the current set
  *   M               tokens, >= 1
- *   Y               fp32 [M, ldy] device, written; ldy >= N (>= w->n_out for
- *                   a mixed-precision weight, whose Y columns are W's rows)
+ *   Y               fp32 [M, ldy] device; ldy >= N.  With w->rmap: ldy >=
+ *                   w->n_out, and only the columns rmap names are written
  *   acc_debug       NULL, or int32 [M, N] device: also receives acc, in
- *                   packed row order (each plane of a mixed-precision weight
- *                   on its own)
+ *                   packed row order
  * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for a w->rmap
  *         that mixq_pack_weight would reject.
  */
@@ -355,7 +349,7 @@ int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  *             which every completed call leaves them zero.  Calls sharing a
  *             ws must not overlap (one stream, or serialized).
  *   ws_bytes  at least mixq_gemm_workspace_bytes(M, N, K, bits) for the split
- *             (N = w->N, the packed row count of a mixed-precision weight)
+ *             (N = w->N)
  * Other arguments and errors: as mixq_gemm.
  */
 int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
@@ -380,8 +374,8 @@ int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  *   acc_debug as mixq_gemm, in the packed (interleaved) column order
  * Other arguments: as mixq_gemm_ws (ws may be NULL).
  * Errors: as mixq_gemm; MIXQ_ERR_INVALID_ARG also for an unknown out_mode,
- *         MIXQ_OUT_SWIGLU_F16 with a weight not packed gated or with a
- *         mixed-precision weight, or ldy < N/2.
+ *         MIXQ_OUT_SWIGLU_F16 with a weight not packed gated or with a row
+ *         subset, or ldy < N/2.
  */
 int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  const mixq_act_state *state, const mixq_weight *w, int64_t M, void *Y,
@@ -394,20 +388,6 @@ int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  * product, two or four for the tail of a large one); 0 when nothing is
  * split. */
 size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
-
-/*
- * mixq_mixed_rows -- packed row map of an output-feature mixed-precision
- * weight (host function).  salient: [N] 0/1 flags (the 8-bit output
- * features).  The S salient rows, ascending, become planes: 64-row blocks of
- * 32 high planes then the same rows' 32 low planes, padded to a multiple of
- * 256 packed rows; the other rows follow, ascending, as 4-bit rows.  Writes
- * rmap[0 .. returned count) (rmap may be NULL to query the count) and
- * *npair.  Returns the number of packed rows, or -1 for bad arguments.
- * Pack a weight with w->N = that count, bits 4, group
- * MIXQ_PROGRESSIVE_GROUP, w->rmap = a device copy of rmap, w->npair = *npair
- * and w->n_out = N.
- */
-int64_t mixq_mixed_rows(const uint8_t *salient, int64_t N, int32_t *rmap, int32_t *npair);
 
 /* Text of a status code (static storage). */
 const char *mixq_status_string(int status);

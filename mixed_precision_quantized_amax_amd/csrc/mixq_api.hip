@@ -81,32 +81,6 @@ size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) 
 }
 
 
-int64_t mixq_mixed_rows(const uint8_t* salient, int64_t N, int32_t* rmap, int32_t* npair) {
-    if (!salient || !npair || N <= 0 || N >= MIXQ_ROW_PAD) return -1;
-    int64_t S = 0;
-    for (int64_t n = 0; n < N; ++n) S += salient[n] ? 1 : 0;
-    const int64_t blocks = (S + 127) / 128 * 4;  // 32-row blocks, padded to 256 planes
-    const int64_t np = blocks * 64;
-    const int64_t total = np + (N - S);
-    if (np > 0x7FFFFFFF || total > 0x7FFFFFFF) return -1;
-    *npair = (int32_t)np;
-    if (!rmap) return total;
-    int64_t n = 0;  // next salient row candidate
-    for (int64_t b = 0; b < blocks; ++b) {
-        int32_t src[32];
-        for (int t = 0; t < 32; ++t) {
-            while (n < N && !salient[n]) ++n;
-            src[t] = (n < N) ? (int32_t)n++ : MIXQ_ROW_PAD;
-        }
-        for (int t = 0; t < 32; ++t) rmap[b * 64 + t] = src[t] | (1 << 30);
-        for (int t = 0; t < 32; ++t) rmap[b * 64 + 32 + t] = src[t] | (2 << 30);
-    }
-    int64_t p = np;
-    for (n = 0; n < N; ++n)
-        if (!salient[n]) rmap[p++] = (int32_t)n;
-    return total;
-}
-
 int64_t mixq_outlier_ld(int32_t k_cap) { return k_cap <= 0 ? 0 : mixq::outlier_ld(k_cap); }
 
 int64_t mixq_bitmap_words(int64_t K) { return K <= 0 ? 0 : mixq::bitmap_words(K); }

@@ -71,11 +71,11 @@ struct GemmArgs {
     // progressive INT4 (null: symmetric per-channel INT4): per row and group
     // of 128 channels, s2 | z << 8
     const uint16_t* gsz;
-    // output-feature mixed precision (progressive kernels only): packed row ->
-    // W row | plane << 30; packed rows [0, npair) are 64-row blocks of 32 high
-    // and 32 low planes; Y columns are W rows < n_out
+    // row subset (ROWS kernels): packed row -> W row = Y column, for W rows
+    // in [0, n_out) (output-feature mixed precision: the 8-bit rows and the
+    // 4-bit rows of one W are two such weights)
     const int32_t* rmap;
-    int32_t npair, n_out;
+    int32_t n_out;
     int32_t wbits;  // 8 or 4 (host side: which launcher)
 };
 
@@ -169,7 +169,7 @@ constexpr int waves_per_eu() {
 // PROG: progressive group-wise INT4 weights (a compile-time choice: a
 // branch in the loader would split the interleaved main loop).
 template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF, bool DEBUG,
-          bool PROG = false, bool MIXED = false>
+          bool PROG = false, bool ROWS = false>
 __global__ __launch_bounds__(WM* WN* kWave)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, WM, WN>(), waves_per_eu<BM, BN, WM, WN>())))
 void gemm_kernel(GemmArgs a) {
@@ -912,22 +912,6 @@ void gemm_kernel(GemmArgs a) {
                 }
             }
     }
-    if constexpr (MIXED) {
-        // Mixed precision: the tile's packed rows are 64-row blocks of 32 high
-        // then 32 low planes (npair is a multiple of 256, so a tile is all
-        // planes or none, and a wave's columns start on a block), so fragment
-        // 2jj + 1 holds the low plane of fragment 2jj's rows.  The 8-bit
-        // product is their sum, exact in int32; the high fragment carries it.
-        if (n0 < a.npair) {
-#pragma unroll
-            for (int i = 0; i < C::kFM; ++i)
-#pragma unroll
-                for (int jj = 0; jj < C::kFN / 2; ++jj)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[i][2 * jj][e] += acc[i][2 * jj + 1][e];
-        }
-    }
-
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i) {
 #pragma unroll
@@ -1036,23 +1020,21 @@ void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kFN; ++j) {
-            int col = n0 + wn * C::kWTN + j * 32 + fr;
+            const int col = n0 + wn * C::kWTN + j * 32 + fr;
             const int r0 = wm * C::kWTM + i * 32 + 4 * fh;  // tile-relative row of e = 0
-            if constexpr (MIXED) {
-                // mixed precision: the Y column is the packed row's W row;
-                // low planes (added above) and padding store nothing
+            int ycol = col;  // Y column: the packed row, or its W row for a row subset
+            if constexpr (ROWS) {
                 if (col < a.N) {
-                    const int32_t rm = a.rmap[col];
-                    const int src = rm & MIXQ_ROW_PAD;
-                    col = (((uint32_t)rm >> 30) != 2u && src < a.n_out) ? src : a.N;
+                    const int32_t src = a.rmap[col];
+                    ycol = (src >= 0 && src < a.n_out) ? src : -1;
                 }
             }
-            if (col < a.N) {
+            if (col < a.N && (!ROWS || ycol >= 0)) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int rl = r0 + 8 * (e >> 2) + (e & 3);
                     if (rl < rows_a)
-                        __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][e], rY, rl * ldy4 + col * 4,
+                        __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][e], rY, rl * ldy4 + ycol * 4,
                                                               0, 0);
                 }
             }
@@ -1060,17 +1042,16 @@ void gemm_kernel(GemmArgs a) {
 }
 
 template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1, bool PROG = false,
-          bool MIXED = false>
+          bool ROWS = false>
 int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
-    static_assert(!MIXED || PROG, "mixed-precision weights are progressive INT4");
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.n_end - a.n_begin + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit), block(WM * WN * kWave);
     if (debug)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true, PROG, MIXED>), grid,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, true, PROG, ROWS>), grid,
                            block, 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false, PROG, MIXED>),
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BITS, STAGES, PF, false, PROG, ROWS>),
                            grid, block, 0, st, a);
     return launch_status();
 }
@@ -1122,7 +1103,16 @@ int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     return bits == 8 && K % 128 == 0 ? kCfg128x128KP : kCfg128x128;
 }
 
+template <bool ROWS = false>
 int launch_w8(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
+    if constexpr (ROWS) {
+        // row subsets: the configurations their shapes are given
+        switch (cfg) {
+            case kCfg256x256KS: return launch_cfg<256, 256, 2, 2, 8, 4, 6, false, true>(a, debug, st);
+            case kCfg128x128KP: return launch_cfg<128, 128, 2, 2, 8, 4, 5, false, true>(a, debug, st);
+            default: return launch_cfg<128, 128, 2, 2, 8, 2, 1, false, true>(a, debug, st);
+        }
+    }
     switch (cfg) {
         case kCfg256x256: return launch_cfg<256, 256, 2, 2, 8, 2>(a, debug, st);
         case kCfg256x128: return launch_cfg<256, 128, 2, 2, 8, 2>(a, debug, st);
@@ -1141,29 +1131,31 @@ int launch_w8(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
     }
 }
 
-template <bool PROG, bool MIXED = false>
+template <bool PROG, bool ROWS = false>
 int launch_w4_t(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
     switch (cfg) {
-        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
-        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
-        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG, MIXED>(a, debug, st);
-        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2, PROG, MIXED>(a, debug, st);
-        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3, PROG, MIXED>(a, debug, st);
-        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG, MIXED>(a, debug, st);
-        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
-        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
-        case kCfg128x128SP: return launch_cfg<128, 128, 2, 2, 4, 2, 4, PROG, MIXED>(a, debug, st);
-        default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG, MIXED>(a, debug, st);
+        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG, ROWS>(a, debug, st);
+        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG, ROWS>(a, debug, st);
+        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG, ROWS>(a, debug, st);
+        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2, PROG, ROWS>(a, debug, st);
+        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3, PROG, ROWS>(a, debug, st);
+        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG, ROWS>(a, debug, st);
+        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG, ROWS>(a, debug, st);
+        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG, ROWS>(a, debug, st);
+        case kCfg128x128SP: return launch_cfg<128, 128, 2, 2, 4, 2, 4, PROG, ROWS>(a, debug, st);
+        default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG, ROWS>(a, debug, st);
     }
 }
 
 int launch_w4(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
-    if (a.rmap) return launch_w4_t<true, true>(a, cfg, debug, st);
+    if (a.rmap) return launch_w4_t<true, true>(a, cfg, debug, st);  // progressive rows only
     return a.gsz ? launch_w4_t<true>(a, cfg, debug, st) : launch_w4_t<false>(a, cfg, debug, st);
 }
 
 int launch_bits(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
-    return a.wbits == 8 ? launch_w8(a, cfg, debug, st) : launch_w4(a, cfg, debug, st);
+    if (a.wbits == 8)
+        return a.rmap ? launch_w8<true>(a, cfg, debug, st) : launch_w8(a, cfg, debug, st);
+    return launch_w4(a, cfg, debug, st);
 }
 
 }  // namespace
@@ -1184,10 +1176,11 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || w->bits != 4 || !w->gsz))
         return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && w->K % MIXQ_PROGRESSIVE_GROUP != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
-    if (w->rmap && (w->group == 0 || w->gated || out_mode != MIXQ_OUT_F32 || w->npair < 0 ||
-                    w->npair % 256 != 0 || w->npair > w->N || w->n_out <= 0 || w->n_out > w->N))
+    // row subsets: INT8 or progressive INT4 rows, fp32 output
+    if (w->rmap && (w->gated || out_mode != MIXQ_OUT_F32 || w->n_out < 1 ||
+                    (w->bits == 4 && w->group == 0)))
         return MIXQ_ERR_INVALID_ARG;
-    // Y columns: N, N / 2 for SwiGLU, n_out for a mixed-precision weight
+    // Y columns: N, N / 2 for SwiGLU, n_out for a row subset
     const int64_t ny = w->rmap ? w->n_out : out_mode == MIXQ_OUT_F32 ? w->N : w->N / 2;
     if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < ny) return MIXQ_ERR_INVALID_ARG;
     if (w->bits != 8 && w->bits != 4) return MIXQ_ERR_INVALID_ARG;
@@ -1226,8 +1219,7 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.part = nullptr;
     a.out_mode = out_mode;
     a.gsz = w->group ? w->gsz : nullptr;
-    a.rmap = w->group ? w->rmap : nullptr;
-    a.npair = w->rmap ? w->npair : 0;
+    a.rmap = w->rmap;
     a.n_out = w->rmap ? w->n_out : 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
@@ -1240,7 +1232,8 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
         a.ksplit = S;
         a.sync = static_cast<int32_t*>(ws);
         a.part = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + kSplitSyncBytes);
-        return launch_cfg<128, 128, 2, 2, 8, 4, 5>(a, acc_debug != nullptr, st);
+        return a.rmap ? launch_cfg<128, 128, 2, 2, 8, 4, 5, false, true>(a, acc_debug != nullptr, st)
+                      : launch_cfg<128, 128, 2, 2, 8, 4, 5>(a, acc_debug != nullptr, st);
     }
     const bool dbg = acc_debug != nullptr;
     // Tail split: when the 256 x 256 tiles come to one round of the device

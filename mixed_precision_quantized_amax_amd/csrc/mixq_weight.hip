@@ -49,21 +49,18 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
     constexpr float kQ = BITS == 8 ? 127.0f : PROG ? 119.0f : 7.0f;
     const int ngroups = K / MIXQ_PROGRESSIVE_GROUP;
     for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
-        // mixed precision: the packed row's W row and plane (0: 4-bit row;
-        // 1, 2: high and low plane of an 8-bit row), the same for the whole block
+        // the packed row's W row (a row subset: rmap[n]), the same for the
+        // whole block; an entry outside W packs zeros
         int64_t srow = src_row(n, N, gated);
-        int plane = 0;
-        if (PROG && rmap) {
-            const int32_t rm = rmap[n];
-            srow = rm & MIXQ_ROW_PAD;
-            plane = (int)((uint32_t)rm >> 30);
-            if (srow >= n_out) {  // padding: all codes 0
-                uint8_t* dst = static_cast<uint8_t*>(wq) + n * (int64_t)(K / 2);
-                const uint32_t fill = plane == 1 ? 0x88888888u : 0u;  // high plane: 8 is 0
-                for (int c = tid; c < nchunks; c += kThreads)
-                    *reinterpret_cast<uint32_t*>(dst + (int64_t)c * 4) = fill;
-                for (int g = tid; g < ngroups; g += kThreads)
-                    gsz[n * (int64_t)ngroups + g] = plane == 1 ? (uint16_t)(16 | (8 << 8)) : (uint16_t)1;
+        if (rmap) {
+            srow = rmap[n];
+            if (srow < 0 || srow >= n_out) {
+                uint8_t* dst = static_cast<uint8_t*>(wq) + n * (int64_t)(BITS == 8 ? K : K / 2);
+                for (int c = tid; c < nchunks * (BITS == 8 ? 2 : 1); c += kThreads)
+                    *reinterpret_cast<uint32_t*>(dst + (int64_t)c * 4) = 0u;
+                if constexpr (PROG)
+                    for (int g = tid; g < ngroups; g += kThreads)
+                        gsz[n * (int64_t)ngroups + g] = (uint16_t)1;  // s2 1, z 0
                 if (tid == 0) s_w[n] = 1.0f;
                 continue;
             }
@@ -89,15 +86,13 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
         for (int w = 1; w < kWaves; ++w) g = fmaxf(g, red[w]);
         __syncthreads();
 
-        // an 8-bit row of a mixed-precision weight uses the INT8 range
-        const float qr = plane ? 127.0f : kQ;
         float s, rho;
         if (g == 0.0f) {
             s = 1.0f;
             rho = 1.0f;
         } else {
-            s = g / qr;
-            rho = qr / g;
+            s = g / kQ;
+            rho = kQ / g;
         }
         if (tid == 0) s_w[n] = s;
 
@@ -111,19 +106,10 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
             for (int e = 0; e < 8; ++e) {
                 float y = __builtin_rintf(
                     half_bits_to_float((uint16_t)(u[e >> 1] >> ((e & 1) * 16))) * rho);
-                y = fminf(fmaxf(y, -qr), qr);
+                y = fminf(fmaxf(y, -kQ), kQ);
                 q[e] = (int)y;
             }
-            if (PROG && plane) {
-                // code = 16 h + l with h in [-8, 7], l in [0, 15]: the high
-                // plane holds h + 8 with s2 16, z 8, the low plane l with s2 1, z 0
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    q[e] = plane == 1 ? (q[e] + 128) >> 4 : (q[e] + 128) & 15;
-                if ((tid & 15) == 0)
-                    gsz[n * (int64_t)ngroups + c / 16] =
-                        plane == 1 ? (uint16_t)(16 | (8 << 8)) : (uint16_t)1;
-            } else if constexpr (PROG) {
+            if constexpr (PROG) {
                 // a group of 128 channels is 16 chunks, held by 16 consecutive lanes
                 int mn = 0, mx = 0;  // zero kept in the range: z is a 4-bit value
 #pragma unroll
@@ -193,15 +179,9 @@ __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* _
     for (int64_t t = threadIdx.x; t < total; t += kThreads) {
         const int64_t n = blockIdx.x + (t / kpad) * G;
         const int j = (int)(t % kpad);
-        // mixed precision: the outlier columns ride on the high plane (or the
-        // 4-bit row); low planes and padding get zeros
-        int64_t srow = src_row(n, N, gated);
-        bool live = true;
-        if (rmap) {
-            const int32_t rm = rmap[n];
-            srow = rm & MIXQ_ROW_PAD;
-            live = srow < n_out && ((uint32_t)rm >> 30) != 2u;
-        }
+        // a row subset takes W row rmap[n]; an entry outside W gets zeros
+        const int64_t srow = rmap ? (int64_t)rmap[n] : src_row(n, N, gated);
+        const bool live = !rmap || (srow >= 0 && srow < n_out);
         w_out[n * ld_out + j] = (live && j < count) ? W[srow * (int64_t)K + idx[j]] : (uint16_t)0;
     }
     __syncthreads();
@@ -214,14 +194,16 @@ int launch_quant(const uint16_t* W, int64_t N, int32_t K, int bits, const mixq_w
     const int grid = (int)(N < 4096 ? N : 4096);
     if (bits == 8)
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 8>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w, w->gated, nullptr, nullptr, (int64_t)0);
+                           N, K, w->wq, w->s_w, w->gated, nullptr, w->rmap,
+                           (int64_t)w->n_out);
     else if (w->group)
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4, true>), dim3(grid), dim3(kThreads), 0,
                            st, W, N, K, w->wq, w->s_w, w->gated, w->gsz, w->rmap,
                            (int64_t)w->n_out);
     else
         hipLaunchKernelGGL((quantize_weight_kernel<CPT, 4>), dim3(grid), dim3(kThreads), 0, st, W,
-                           N, K, w->wq, w->s_w, w->gated, nullptr, nullptr, (int64_t)0);
+                           N, K, w->wq, w->s_w, w->gated, nullptr, w->rmap,
+                           (int64_t)w->n_out);
     return launch_status();
 }
 
@@ -245,8 +227,8 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     if (w->gated != 0 && w->gated != 1) return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || bits != 4 || !w->gsz))
         return MIXQ_ERR_INVALID_ARG;
-    if (w->rmap && (w->group == 0 || w->gated || w->npair < 0 || w->npair % 256 != 0 ||
-                    w->npair > N || w->n_out <= 0 || w->n_out > N))
+    // row subsets: INT8 or progressive INT4 rows
+    if (w->rmap && (w->gated || w->n_out < 1 || (bits == 4 && w->group == 0)))
         return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (w->gated && N % 64 != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;

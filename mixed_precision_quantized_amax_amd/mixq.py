@@ -27,7 +27,6 @@ PACK_OUTLIER_COLS = 1
 OUT_F32 = 0
 OUT_SWIGLU_F16 = 1
 PROGRESSIVE_GROUP = 128
-ROW_PAD = 0x3FFFFFFF  # padding row of a mixed-precision row map
 OUTLIER_ALIGN = 32
 K_MULTIPLE = 64
 GATHER_SLOTS = 256
@@ -49,8 +48,7 @@ class Weight(ctypes.Structure):
     _fields_ = [("wq", ctypes.c_void_p), ("s_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
                 ("k_out", ctypes.c_void_p), ("bits", ctypes.c_int32), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("k_cap", ctypes.c_int32), ("gated", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("gsz", ctypes.c_void_p), ("rmap", ctypes.c_void_p), ("npair", ctypes.c_int32),
-                ("n_out", ctypes.c_int32)]
+                ("gsz", ctypes.c_void_p), ("rmap", ctypes.c_void_p), ("n_out", ctypes.c_int32)]
 
 
 _lib = None
@@ -96,8 +94,6 @@ def lib() -> ctypes.CDLL:
         L.mixq_gemm_ex.argtypes = [P, P, P, ctypes.POINTER(ActState), ctypes.POINTER(Weight), I64,
                                    P, I64, I32, P, P, ctypes.c_size_t, P]
         L.mixq_gemm_ex.restype = ctypes.c_int
-        L.mixq_mixed_rows.argtypes = [P, I64, P, P]
-        L.mixq_mixed_rows.restype = I64
         L.mixq_gemm_workspace_bytes.argtypes = [I64, I64, I64, I32]
         L.mixq_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.mixq_status_string.argtypes = [ctypes.c_int]
@@ -172,9 +168,8 @@ class PackedWeight:
     gated: int = 0  # 1: W = [W_gate; W_up], packed with 32-row blocks interleaved
     group: int = 0  # PROGRESSIVE_GROUP: progressive group-wise INT4
     gsz: torch.Tensor | None = None  # [N, K/group] uint16: s2 | z << 8
-    # output-feature mixed precision: packed row -> W row | plane << 30
+    # row subset: packed row -> W row (= Y column); int32 [N] on the device
     rmap: torch.Tensor | None = None
-    npair: int = 0  # packed rows [0, npair) are high / low planes of 8-bit rows
     n_out: int = 0  # rows of W (columns of Y) when rmap is set
 
     @classmethod
@@ -194,30 +189,21 @@ class PackedWeight:
                         if group else None))
 
     @classmethod
-    def create_mixed(cls, salient, K: int, k_cap: int, device="cuda") -> "PackedWeight":
-        """An output-feature mixed-precision weight: the rows flagged in
-        ``salient`` (bool [N_out]) keep 8-bit codes, as a high and a low
-        progressive 4-bit plane; the other rows are progressive INT4."""
-        sal = np.ascontiguousarray(np.asarray(salient, dtype=np.uint8))
-        n_out = int(sal.shape[0])
-        npair = ctypes.c_int32(0)
-        total = int(lib().mixq_mixed_rows(sal.ctypes.data, n_out, None, ctypes.byref(npair)))
-        if total <= 0:
-            raise ValueError("invalid salient flags")
-        rm = np.zeros(total, np.int32)
-        lib().mixq_mixed_rows(sal.ctypes.data, n_out, rm.ctypes.data, ctypes.byref(npair))
-        pw = cls.create(total, K, 4, k_cap, device=device, group=PROGRESSIVE_GROUP)
-        pw.rmap = torch.from_numpy(rm).to(device)
-        pw.npair = int(npair.value)
-        pw.n_out = n_out
+    def create_rows(cls, rows, n_out: int, K: int, bits: int, k_cap: int, device="cuda",
+                    group: int = 0) -> "PackedWeight":
+        """A weight over a subset of W's rows: packed row n quantizes W row
+        rows[n] and the product writes Y column rows[n]."""
+        rm = torch.as_tensor(np.asarray(rows, dtype=np.int32))
+        pw = cls.create(int(rm.shape[0]), K, bits, k_cap, device=device, group=group)
+        pw.rmap = rm.to(device)
+        pw.n_out = int(n_out)
         return pw
 
     def c(self) -> Weight:
         return Weight(self.wq.data_ptr(), self.s_w.data_ptr(), self.w_out.data_ptr(),
                       self.k_out.data_ptr(), self.bits, self.N, self.K, self.k_cap, self.gated,
                       self.group, None if self.gsz is None else self.gsz.data_ptr(),
-                      None if self.rmap is None else self.rmap.data_ptr(), self.npair,
-                      self.n_out)
+                      None if self.rmap is None else self.rmap.data_ptr(), self.n_out)
 
     def codes_view(self) -> torch.Tensor:
         """int8 [N, K] (bits 8) or packed uint8 [N, K/2] (bits 4) view of wq."""
@@ -280,8 +266,7 @@ def add_rmsnorm_quantize_act(R: torch.Tensor, D: torch.Tensor, H: torch.Tensor,
 
 def pack_weight(W: torch.Tensor, state: OutlierState, pw: PackedWeight,
                 mode: int = PACK_FULL) -> None:
-    """mixq_pack_weight.  W: fp16 [N, K], or [n_out, K] for a mixed-precision
-    weight (whose packed row count N is larger)."""
+    """mixq_pack_weight.  W: fp16 [N, K], or [n_out, K] for a row subset."""
     assert W.dtype == torch.float16 and W.is_contiguous()
     assert W.shape[0] == (pw.n_out if pw.rmap is not None else pw.N)
     K = W.shape[1]
@@ -449,3 +434,40 @@ class MixQLinear:
         return Y
 
     __call__ = forward
+
+
+@dataclass
+class MixedWeight:
+    """Output-feature mixed precision (MixLLM page): the salient output
+    features of W keep 8-bit weights and the others get progressive 4-bit
+    ones, as two row-subset weights whose products write disjoint columns of
+    one Y."""
+    w8: PackedWeight | None  # None when no feature is salient
+    w4: PackedWeight | None  # None when every feature is
+
+    @classmethod
+    def create(cls, salient, K: int, k_cap: int, device="cuda") -> "MixedWeight":
+        sal = np.asarray(salient, dtype=bool)
+        n = int(sal.shape[0])
+        r8, r4 = np.flatnonzero(sal), np.flatnonzero(~sal)
+        return cls(w8=PackedWeight.create_rows(r8, n, K, 8, k_cap, device) if r8.size else None,
+                   w4=PackedWeight.create_rows(r4, n, K, 4, k_cap, device,
+                                               group=PROGRESSIVE_GROUP) if r4.size else None)
+
+    def parts(self):
+        return [p for p in (self.w4, self.w8) if p is not None]
+
+    def pack(self, W: torch.Tensor, state: OutlierState, mode: int = PACK_FULL) -> None:
+        for p in self.parts():
+            pack_weight(W, state, p, mode)
+
+    def workspaces(self, M: int, device=None):
+        """Split-K workspaces, (4-bit, 8-bit)."""
+        return tuple(None if p is None else gemm_workspace(M, p.N, p.K, p.bits, device)
+                     for p in (self.w4, self.w8))
+
+    def gemm(self, Xq, s_x, X_out, state, Y, acc_debug=(None, None), ws=(None, None)) -> None:
+        """Both products into Y; acc_debug and ws are (4-bit, 8-bit) pairs."""
+        for p, dbg, w in zip((self.w4, self.w8), acc_debug, ws):
+            if p is not None:
+                gemm(Xq, s_x, X_out, state, p, Y, dbg, w)

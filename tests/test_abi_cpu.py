@@ -5,7 +5,6 @@ import ctypes
 import os
 import re
 
-import numpy as np
 import pytest
 
 from mixed_precision_quantized_amax_amd import mixq
@@ -121,17 +120,17 @@ def test_valid_arguments_need_a_device():
     assert mixq.lib().mixq_check_device() == 4
 
 
-def _weight(N=16, K=64, bits=8, k_cap=8, gated=0, group=0, npair=0, n_out=0, **null):
+def _weight(N=16, K=64, bits=8, k_cap=8, gated=0, group=0, n_out=0, **null):
     vals = dict(wq=0x100000, s_w=0x200000, w_out=0x300000, k_out=0x400000, gsz=0x500000, rmap=0)
     vals.update(null)
     return mixq.Weight(vals["wq"], vals["s_w"], vals["w_out"], vals["k_out"], bits, N, K, k_cap,
-                       gated, group, vals["gsz"], vals["rmap"] or None, npair, n_out)
+                       gated, group, vals["gsz"], vals["rmap"] or None, n_out)
 
 
-def _mixed(N=512, n_out=300, npair=256, group=128, **kw):
-    """A mixed-precision weight descriptor (K = 128: one progressive group)."""
+def _rows(N=512, n_out=3000, bits=4, group=128, **kw):
+    """A row-subset descriptor (K = 128: one progressive group)."""
     kw.setdefault("rmap", 0x600000)
-    return _weight(N=N, K=128, bits=4, group=group, npair=npair, n_out=n_out, **kw)
+    return _weight(N=N, K=128, bits=bits, group=group if bits == 4 else 0, n_out=n_out, **kw)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -143,12 +142,10 @@ def _mixed(N=512, n_out=300, npair=256, group=128, **kw):
     (dict(w=_weight(group=128), bits=8), 1),                               # groups need INT4
     (dict(w=_weight(group=128, bits=4, gsz=0), bits=4), 1),                # no group table
     (dict(w=_weight(group=128, bits=4), bits=4), 2),                       # K = 64 < 128
-    (dict(w=_mixed(group=0), N=512, K=128, bits=4), 1),                    # map needs groups
-    (dict(w=_mixed(npair=128), N=512, K=128, bits=4), 1),                  # npair % 256
-    (dict(w=_mixed(npair=768), N=512, K=128, bits=4), 1),                  # npair > N
-    (dict(w=_mixed(n_out=0), N=512, K=128, bits=4), 1),                    # no output rows
-    (dict(w=_mixed(n_out=513), N=512, K=128, bits=4), 1),                  # n_out > N
-    (dict(w=_mixed(gated=1), N=512, K=128, bits=4), 1),                    # not with gated
+    (dict(w=_rows(group=0), N=512, K=128, bits=4), 1),                     # INT4 rows: groups
+    (dict(w=_rows(n_out=0), N=512, K=128, bits=4), 1),                     # no output rows
+    (dict(w=_rows(gated=1), N=512, K=128, bits=4), 1),                     # not with gated
+    (dict(w=_rows(bits=8, n_out=0), N=512, K=128, bits=8), 1),
 ])
 def test_pack_weight_validation(args, code):
     N = args.get("N", 16)
@@ -223,11 +220,11 @@ def test_gemm_ws_validation():
     (dict(mode=0, w=_weight(group=128, bits=8)), 1),       # groups need INT4
     (dict(mode=0, w=_weight(group=128, bits=4, gsz=0)), 1),
     (dict(mode=0, w=_weight(group=128, bits=4)), 2),       # K = 64 < 128
-    (dict(mode=0, w=_mixed(), ldy=299), 1),                # Y row shorter than n_out
-    (dict(mode=1, w=_mixed(), ldy=512), 1),                # no SwiGLU output
-    (dict(mode=0, w=_mixed(npair=100), ldy=512), 1),
-    (dict(mode=0, w=_mixed(group=0), ldy=512), 1),
-    (dict(mode=0, w=_mixed(n_out=600), ldy=600), 1),
+    (dict(mode=0, w=_rows(), ldy=2999), 1),                # Y row shorter than n_out
+    (dict(mode=1, w=_rows(), ldy=3000), 1),                # no SwiGLU output
+    (dict(mode=0, w=_rows(group=0), ldy=3000), 1),         # INT4 rows: groups
+    (dict(mode=0, w=_rows(n_out=0), ldy=3000), 1),
+    (dict(mode=0, w=_rows(bits=8, n_out=0), ldy=3000), 1),
 ])
 def test_gemm_ex_validation(kw, code):
     w = kw.get("w", _weight())
@@ -253,59 +250,10 @@ def test_gemm_ex_valid_arguments_need_a_device():
         assert f(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
                  ctypes.byref(st), ctypes.byref(w), 4, ctypes.c_void_p(0x50000), ldy, mode, None,
                  None, 0, None) == 4
-    # a mixed-precision weight: W has n_out rows, Y n_out columns
-    wm = _mixed()
-    assert mixq.lib().mixq_pack_weight(ctypes.c_void_p(0x900000), 512, 128, 4, ctypes.byref(st),
-                                       0, ctypes.byref(wm), None) == 4
-    assert f(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
-             ctypes.byref(st), ctypes.byref(wm), 4, ctypes.c_void_p(0x50000), 300, 0, None, None, 0,
-             None) == 4
-
-
-def _rows(salient):
-    sal = np.ascontiguousarray(np.asarray(salient, np.uint8))
-    npair = ctypes.c_int32(-1)
-    L = mixq.lib()
-    total = L.mixq_mixed_rows(sal.ctypes.data, sal.shape[0], None, ctypes.byref(npair))
-    rm = np.full(max(total, 1), -7, np.int32)
-    assert L.mixq_mixed_rows(sal.ctypes.data, sal.shape[0], rm.ctypes.data,
-                             ctypes.byref(npair)) == total
-    return total, npair.value, rm[:total]
-
-
-@pytest.mark.parametrize("N,S,seed", [(1, 0, 0), (1, 1, 0), (300, 0, 1), (300, 7, 2),
-                                      (300, 128, 3), (300, 129, 4), (1000, 300, 5),
-                                      (4096, 41, 6), (64, 64, 7)])
-def test_mixed_rows_map(N, S, seed):
-    """Output-feature mixed precision (MixLLM page): the packed row map.  The
-    salient rows, ascending, fill 64-row blocks of 32 high planes then the
-    same rows' 32 low planes, padded to a multiple of 256; the other rows
-    follow in order."""
-    rng = np.random.default_rng(seed)
-    sal = np.zeros(N, bool)
-    sal[rng.choice(N, S, replace=False)] = True
-    total, npair, rm = _rows(sal)
-    blocks = -(-S // 128) * 4
-    assert npair == blocks * 64 and npair % 256 == 0
-    assert total == npair + N - S
-    src, plane = rm & 0x3FFFFFFF, rm.astype(np.uint32) >> 30
-    pad = src == mixq.ROW_PAD
-    assert set(np.unique(plane[:npair])) <= {1, 2} and (plane[npair:] == 0).all()
-    for b in range(blocks):
-        hi, lo = rm[64 * b: 64 * b + 32], rm[64 * b + 32: 64 * b + 64]
-        assert ((hi.astype(np.uint32) >> 30) == 1).all() and ((lo.astype(np.uint32) >> 30) == 2).all()
-        assert ((hi & 0x3FFFFFFF) == (lo & 0x3FFFFFFF)).all()
-    live = src[:npair][(plane[:npair] == 1) & ~pad[:npair]]
-    assert live.tolist() == np.flatnonzero(sal).tolist()          # ascending, each once
-    assert pad[:npair].sum() == 2 * (npair // 2 - S)               # padding at the end
-    assert not pad[npair:].any()
-    assert src[npair:].tolist() == np.flatnonzero(~sal).tolist()
-
-
-def test_mixed_rows_bad_arguments():
-    L = mixq.lib()
-    npair = ctypes.c_int32(0)
-    sal = np.ones(4, np.uint8)
-    assert L.mixq_mixed_rows(None, 4, None, ctypes.byref(npair)) == -1
-    assert L.mixq_mixed_rows(sal.ctypes.data, 0, None, ctypes.byref(npair)) == -1
-    assert L.mixq_mixed_rows(sal.ctypes.data, 4, None, None) == -1
+    # row subsets (INT4 progressive and INT8): W has n_out rows, Y n_out columns
+    for wm, bits in ((_rows(), 4), (_rows(bits=8), 8)):
+        assert mixq.lib().mixq_pack_weight(ctypes.c_void_p(0x900000), 512, 128, bits,
+                                           ctypes.byref(st), 0, ctypes.byref(wm), None) == 4
+        assert f(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+                 ctypes.byref(st), ctypes.byref(wm), 4, ctypes.c_void_p(0x50000), 3000, 0, None,
+                 None, 0, None) == 4

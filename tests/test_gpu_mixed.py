@@ -1,10 +1,10 @@
 """Output-feature mixed precision (MixLLM page: the salient output features
 keep 8-bit weights, the rest 4-bit, all products on INT8 units) against the
-oracle.  A salient row's INT8 code is split into a high and a low
-progressive 4-bit plane; the product adds the two planes' accumulators.
-Checked: every plane's 4-bit values, group entries and scales bit for bit
-against the oracle's codes, the outlier columns, the int32 accumulators per
-plane and of each output feature, and Y within 1e-3 * max|Y|."""
+oracle.  The salient rows form an INT8 row-subset weight and the others a
+progressive INT4 one; each product writes its own columns of Y.  Checked:
+every row's codes, group entries and scales bit for bit against the oracle's
+mixed codes, the outlier columns, both products' int32 accumulators bit for
+bit, every Y column written, Y within 1e-3 * max|Y|."""
 import os
 
 import numpy as np
@@ -16,8 +16,6 @@ from mixed_precision_quantized_amax_amd import mixq, workloads
 from oracle import Oracle, OracleLayer
 
 pytestmark = pytest.mark.gpu
-
-MASK = 0x3FFFFFFF
 
 
 @pytest.fixture(scope="module")
@@ -55,25 +53,29 @@ def run_mixed(X, W, sal, tau, k_cap, acc=True, ws=False):
     M, K = X.shape
     Wd = to_dev(W.view(np.float16))
     st = mixq.OutlierState.create(K, k_cap)
-    pw = mixq.PackedWeight.create_mixed(sal, K, k_cap)
-    mixq.pack_weight(Wd, st, pw, mixq.PACK_FULL)
+    mw = mixq.MixedWeight.create(sal, K, k_cap)
+    mw.pack(Wd, st, mixq.PACK_FULL)
     ld = mixq.outlier_ld(k_cap)
     Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
     sx = torch.empty(M, dtype=torch.float32, device="cuda")
     Xo = torch.zeros(max(M * ld, 1), dtype=torch.float16, device="cuda") if ld else None
     mixq.quantize_act(to_dev(X.view(np.float16)), tau, st, Xq, sx, Xo)
-    mixq.pack_weight(Wd, st, pw, mixq.PACK_OUTLIER_COLS)
+    mw.pack(Wd, st, mixq.PACK_OUTLIER_COLS)
     Y = torch.full((M, W.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
-    dbg = torch.zeros(M, pw.N, dtype=torch.int32, device="cuda") if acc else None
-    wsb = mixq.gemm_workspace(M, pw.N, K, 4) if ws else None
-    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg, wsb)
+    dbg = tuple(torch.zeros(M, p.N, dtype=torch.int32, device="cuda")
+                if (acc and p is not None) else None for p in (mw.w4, mw.w8))
+    wsb = mw.workspaces(M) if ws else (None, None)
+    mw.gemm(Xq, sx, Xo, st, Y, dbg, wsb)
     torch.cuda.synchronize()
-    return dict(pw=pw, Y=Y.cpu().numpy(), acc=None if dbg is None else dbg.cpu().numpy(),
-                count=int(st.count.cpu()[0]), ws=wsb)
+    return dict(mw=mw, Y=Y.cpu().numpy(), count=int(st.count.cpu()[0]), ws=wsb,
+                acc=tuple(None if d is None else d.cpu().numpy() for d in dbg))
 
 
 def packed_values(pw):
-    """The INT8 value (u - z) * s2 of every packed row and channel."""
+    """The INT8 code of every packed row and channel: bits 8 directly, bits 4
+    rebuilt as (u - z) * s2."""
+    if pw.bits == 8:
+        return pw.codes_view().cpu().numpy().astype(np.int32), None
     K = pw.K
     u = unpack_u4(pw.codes_view().cpu().numpy(), K).astype(np.int32)
     gsz = pw.gsz.view(torch.int16).cpu().numpy().view(np.uint16).reshape(pw.N, K // 128)
@@ -82,44 +84,30 @@ def packed_values(pw):
     return (u - z) * s2, gsz
 
 
-def layout(pw):
-    rm = pw.rmap.cpu().numpy()
-    src = rm & MASK
-    plane = rm.astype(np.uint32) >> 30
-    live = src < pw.n_out
-    return src, plane, live
-
-
 def check_pack(orc, g, W, sal, W_out):
-    """The packed planes against the oracle's codes and scales."""
-    pw = g["pw"]
+    """Both parts against the oracle's mixed codes and scales."""
     codes, scales = orc.mixed_feature_quantize_weight(W, sal)
-    v, gsz = packed_values(pw)
-    src, plane, live = layout(pw)
-    s_w = pw.s_w.cpu().numpy()
-    hi = np.flatnonzero((plane == 1) & live)
-    lo = hi + 32
-    assert np.array_equal(src[lo], src[hi]) and (plane[lo] == 2).all()
-    # an 8-bit row: high plane 16 h (h in [-8, 7]), low plane l in [0, 15]
-    assert np.array_equal(v[hi] + v[lo], codes[src[hi]].astype(np.int32))
-    assert ((v[hi] % 16) == 0).all() and (v[lo] >= 0).all() and (v[lo] <= 15).all()
-    assert ((gsz[hi] == (16 | 8 << 8)).all()) and (gsz[lo] == 1).all()
-    p4 = np.flatnonzero(plane == 0)
-    assert np.array_equal(v[p4], codes[src[p4]].astype(np.int32))
-    for rows in (hi, lo, p4):
-        assert np.array_equal(s_w[rows].view(np.uint32), scales[src[rows]].view(np.uint32))
-    pad = np.flatnonzero(~live)
-    assert (v[pad] == 0).all() and (s_w[pad] == 1.0).all()
-    # outlier columns ride on the high plane and the 4-bit rows only
-    wo = pw.w_out_view().cpu().numpy().view(np.uint16)
-    carry = np.concatenate([hi, p4])
-    assert np.array_equal(wo[carry], W_out[src[carry]])
-    zero = np.concatenate([lo, pad])
-    assert (wo[zero] == 0).all()
-    return codes, scales, hi, lo, p4, src
+    _, _, u, s2, z, _ = orc.progressive_quantize_weight(W)
+    mw = g["mw"]
+    for p, rows in ((mw.w8, np.flatnonzero(sal)), (mw.w4, np.flatnonzero(~sal))):
+        if p is None:
+            assert rows.size == 0
+            continue
+        assert np.array_equal(p.rmap.cpu().numpy(), rows)
+        v, gsz = packed_values(p)
+        assert np.array_equal(v, codes[rows].astype(np.int32))
+        if gsz is not None:  # the stored 4-bit values and group entries themselves
+            got_u = unpack_u4(p.codes_view().cpu().numpy(), p.K)
+            assert np.array_equal(got_u, u[rows])
+            assert np.array_equal(gsz & 0xFF, s2[rows]) and np.array_equal(gsz >> 8, z[rows])
+        assert np.array_equal(p.s_w.cpu().numpy().view(np.uint32), scales[rows].view(np.uint32))
+        wo = p.w_out_view().cpu().numpy().view(np.uint16)
+        assert np.array_equal(wo, W_out[rows])
+    return codes, scales
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11", "15"], indirect=True)
+@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11", "13", "14", "15"],
+                         indirect=True)
 @pytest.mark.parametrize("M,K,N,S,n_act", [(37, 256, 128, 5, 3), (130, 1024, 384, 100, 9),
                                            (257, 2048, 520, 129, 0), (64, 1024, 256, 0, 40),
                                            (100, 512, 300, 300, 4)])
@@ -132,17 +120,13 @@ def test_mixed_random(orc, tile, M, K, N, S, n_act):
     r = o.step(X, products=False)
     assert g["count"] == r.count
     W_out = orc.gather_weight_cols(W, r.in_set, mixq.outlier_ld(64))
-    codes, scales, hi, lo, p4, src = check_pack(orc, g, W, sal, W_out)
+    codes, scales = check_pack(orc, g, W, sal, W_out)
     acc = orc.int_gemm(r.Xq, codes)
-    got = g["acc"]
-    # per plane, then per output feature
-    hi_codes = ((codes.astype(np.int32) + 128) >> 4) * 16 - 128
-    lo_codes = (codes.astype(np.int32) + 128) & 15
-    if hi.size:
-        assert np.array_equal(got[:, hi], orc.int_gemm(r.Xq, hi_codes[src[hi]].astype(np.int8)))
-        assert np.array_equal(got[:, lo], orc.int_gemm(r.Xq, lo_codes[src[lo]].astype(np.int8)))
-        assert np.array_equal(got[:, hi] + got[:, lo], acc[:, src[hi]])
-    assert np.array_equal(got[:, p4], acc[:, src[p4]])
+    a4, a8 = g["acc"]
+    if a4 is not None:
+        assert np.array_equal(a4, acc[:, ~sal])
+    if a8 is not None:
+        assert np.array_equal(a8, acc[:, sal])
     Y = orc.output(acc, r.s_x, scales, r.X_out, W_out, r.count)
     assert not np.isnan(g["Y"]).any(), "an output feature was not written"
     err = check_y(g["Y"], Y)
@@ -151,8 +135,8 @@ def test_mixed_random(orc, tile, M, K, N, S, n_act):
 
 def test_mixed_full_size(orc):
     """The INT4 prefill shape (M = 2048, K = N = 8192) with 10% of the output
-    features at 8 bits: every plane's values, group entries and scales; the
-    accumulators and Y at sampled positions."""
+    features at 8 bits (split-K workspaces given): every code, group entry
+    and scale; the accumulators and Y at sampled positions."""
     wl = workloads.WORKLOADS["prefill_w4"]
     X = workloads.make_activation(wl)
     W = workloads.make_weight(wl)
@@ -162,19 +146,18 @@ def test_mixed_full_size(orc):
     r = o.step(X, products=False)
     assert g["count"] == r.count
     W_out = orc.gather_weight_cols(W, r.in_set, mixq.outlier_ld(256))
-    codes, scales, hi, lo, p4, src = check_pack(orc, g, W, sal, W_out)
+    codes, scales = check_pack(orc, g, W, sal, W_out)
     rng = np.random.default_rng(11)
-    rows = np.concatenate([rng.integers(0, wl.M, 2000), [0, wl.M - 1]])
     cols = np.concatenate([rng.integers(0, wl.N, 2000), np.flatnonzero(sal)[:8],
                            np.flatnonzero(~sal)[-8:]])
-    rows = np.resize(rows, cols.shape[0])
+    rows = np.resize(np.concatenate([rng.integers(0, wl.M, 2000), [0, wl.M - 1]]), cols.shape[0])
     acc, Y = orc.sampled_output(r.Xq, codes, r.s_x, scales, r.X_out, W_out, r.count, rows, cols)
-    # the accumulator of an output feature: its 4-bit row, or its two planes
-    where = np.empty(wl.N, np.int64)
-    where[src[p4]] = p4
-    where[src[hi]] = hi
-    lo_of = np.where(sal[cols], where[cols] + 32, where[cols])
-    got = g["acc"][rows, where[cols]] + np.where(sal[cols], g["acc"][rows, lo_of], 0)
+    # the accumulator of an output feature sits in its part's packed column
+    pos = np.empty(wl.N, np.int64)
+    pos[sal] = np.arange(sal.sum())
+    pos[~sal] = np.arange((~sal).sum())
+    a4, a8 = g["acc"]
+    got = np.where(sal[cols], a8[rows, pos[cols] * sal[cols]], a4[rows, pos[cols] * ~sal[cols]])
     assert np.array_equal(got, acc)
     assert not np.isnan(g["Y"]).any(), "an output feature was not written"
     ref = np.abs(Y).max()
