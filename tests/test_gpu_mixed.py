@@ -164,3 +164,50 @@ def test_mixed_full_size(orc):
     err = np.abs(g["Y"][rows, cols].astype(np.float64) - Y).max() / ref
     say(f"[mixed] full: max|dY|/max|Y| = {err:.2e}")
     assert err <= 1e-3
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_row_subset_entries_outside_w(orc, bits):
+    """Row-map entries outside [0, n_out) pack zero codes with scale 1 and
+    zero outlier columns, and write no Y column; the other rows are exact
+    and every unnamed Y column keeps its old contents."""
+    M, K, n_out = 70, 256, 300
+    X, W, _ = workloads.random_case(seed=bits, M=M, K=K, N=n_out, n_out=3)
+    rows = np.array([5, -1, 299, n_out, 17, 2**31 - 1], np.int32)
+    Wd = to_dev(W.view(np.float16))
+    st = mixq.OutlierState.create(K, 64)
+    pw = mixq.PackedWeight.create_rows(rows, n_out, K, bits, 64,
+                                       group=mixq.PROGRESSIVE_GROUP if bits == 4 else 0)
+    mixq.pack_weight(Wd, st, pw, mixq.PACK_FULL)
+    ld = mixq.outlier_ld(64)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    Xo = torch.zeros(M * ld, dtype=torch.float16, device="cuda")
+    mixq.quantize_act(to_dev(X.view(np.float16)), 6.0, st, Xq, sx, Xo)
+    mixq.pack_weight(Wd, st, pw, mixq.PACK_OUTLIER_COLS)
+    Y = torch.full((M, n_out), float("nan"), dtype=torch.float32, device="cuda")
+    dbg = torch.zeros(M, pw.N, dtype=torch.int32, device="cuda")
+    mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg)
+    torch.cuda.synchronize()
+    live = (rows >= 0) & (rows < n_out)
+    v, _ = packed_values(pw)
+    s_w = pw.s_w.cpu().numpy()
+    wo = pw.w_out_view().cpu().numpy().view(np.uint16)
+    assert (v[~live] == 0).all() and (s_w[~live] == 1.0).all() and (wo[~live] == 0).all()
+    assert (dbg.cpu().numpy()[:, ~live] == 0).all()
+    o = OracleLayer(W=W, bits=8, tau=6.0, k_cap=64, ldo=ld, oracle=orc)
+    r = o.step(X, products=False)
+    W_out = orc.gather_weight_cols(W, r.in_set, ld)
+    if bits == 8:
+        codes, scales = orc.quantize_weight(W, 8)
+    else:
+        codes, scales, *_ = orc.progressive_quantize_weight(W)
+    sel = rows[live]
+    assert np.array_equal(v[live], codes[sel].astype(np.int32))
+    acc = orc.int_gemm(r.Xq, codes[sel])
+    assert np.array_equal(dbg.cpu().numpy()[:, live], acc)
+    Yref = orc.output(acc, r.s_x, scales[sel], r.X_out, W_out[sel], r.count)
+    y = Y.cpu().numpy()
+    check_y(y[:, sel], Yref)
+    others = np.setdiff1d(np.arange(n_out), sel)
+    assert np.isnan(y[:, others]).all(), "a column no row names was written"
