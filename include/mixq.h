@@ -143,8 +143,9 @@ typedef struct mixq_weight {
                           scale s2 in [1, 16] and zero z in [0, 15]; the product
                           uses the INT8 code (u - z) * s2.  wq holds u in the
                           INT4 nibble layout.                                      */
-    uint16_t *gsz;     /* group != 0: [N, K/128], s2 | z << 8 for each row and
-                          group (device memory, written by mixq_pack_weight)    */
+    uint16_t *gsz;     /* group != 0: [K/128, N] (group-major), s2 | z << 8 for
+                          each group and row (device memory, written by
+                          mixq_pack_weight); N * K/128 * 2 bytes < 2^31        */
     const int32_t *rmap; /* NULL, or a row subset: [N] device array, the W row
                           each packed row quantizes, which is also the Y column
                           the product writes for it.  Output-feature mixed

@@ -476,16 +476,19 @@ void gemm_kernel(GemmArgs a) {
             v4i b[BITS == 8 ? C::kBI : C::kBI4];
             uint32_t g[PROG ? C::kBI4 : 1];  // progressive INT4: the rows' s2 | z << 8
         };
-        // progressive INT4: groups of 128 channels = two K tiles
+        // progressive INT4: groups of 128 channels = two K tiles; the table is
+        // group-major ([K/128][N]), so one group's entries of a wave's 32 rows
+        // are one contiguous 64-byte run
         const int ngroups = K / 128;
         const __amdgpu_buffer_rsrc_t rG =
-            make_rsrc(a.gsz + (int64_t)n0 * ngroups, a.gsz ? (int64_t)rows_b * ngroups * 2 : 0);
+            make_rsrc(a.gsz + n0,
+                      a.gsz ? ((int64_t)(ngroups - 1) * a.N + rows_b) * 2 : 0);
         auto gzload = [&](int kt, Regs& R) {
             if constexpr (PROG) {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i) {
                     const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
-                    R.g[i] = __builtin_amdgcn_raw_buffer_load_b16(rG, (row * ngroups + kt / 2) * 2,
+                    R.g[i] = __builtin_amdgcn_raw_buffer_load_b16(rG, ((kt / 2) * a.N + row) * 2,
                                                                    0, 0);
                 }
             }
@@ -1176,6 +1179,9 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || w->bits != 4 || !w->gsz))
         return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && w->K % MIXQ_PROGRESSIVE_GROUP != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    // the group table's byte offsets are 32-bit
+    if (w->group != 0 && w->N * (w->K / MIXQ_PROGRESSIVE_GROUP) * 2 > 0x7FFFFFFF)
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
     // row subsets: INT8 or progressive INT4 rows, fp32 output
     if (w->rmap && (w->gated || out_mode != MIXQ_OUT_F32 || w->n_out < 1 ||
                     (w->bits == 4 && w->group == 0)))

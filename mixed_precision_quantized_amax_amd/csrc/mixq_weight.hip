@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
                     *reinterpret_cast<uint32_t*>(dst + (int64_t)c * 4) = 0u;
                 if constexpr (PROG)
                     for (int g = tid; g < ngroups; g += kThreads)
-                        gsz[n * (int64_t)ngroups + g] = (uint16_t)1;  // s2 1, z 0
+                        gsz[g * N + n] = (uint16_t)1;  // s2 1, z 0
                 if (tid == 0) s_w[n] = 1.0f;
                 continue;
             }
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
                 for (int e = 0; e < 8; ++e)
                     q[e] = min(max((int)__builtin_rintf((float)q[e] / fs2) + z, 0), 15);
                 if ((tid & 15) == 0)
-                    gsz[n * (int64_t)ngroups + c / 16] = (uint16_t)(s2 | (z << 8));
+                    gsz[(c / 16) * N + n] = (uint16_t)(s2 | (z << 8));
             }
             if (BITS == 8) {
                 uint32_t p0 = 0, p1 = 0;

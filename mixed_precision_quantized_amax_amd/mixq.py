@@ -167,7 +167,7 @@ class PackedWeight:
     k_out: torch.Tensor
     gated: int = 0  # 1: W = [W_gate; W_up], packed with 32-row blocks interleaved
     group: int = 0  # PROGRESSIVE_GROUP: progressive group-wise INT4
-    gsz: torch.Tensor | None = None  # [N, K/group] uint16: s2 | z << 8
+    gsz: torch.Tensor | None = None  # [K/group, N] uint16: s2 | z << 8
     # row subset: packed row -> W row (= Y column); int32 [N] on the device
     rmap: torch.Tensor | None = None
     n_out: int = 0  # rows of W (columns of Y) when rmap is set

@@ -78,7 +78,7 @@ def packed_values(pw):
         return pw.codes_view().cpu().numpy().astype(np.int32), None
     K = pw.K
     u = unpack_u4(pw.codes_view().cpu().numpy(), K).astype(np.int32)
-    gsz = pw.gsz.view(torch.int16).cpu().numpy().view(np.uint16).reshape(pw.N, K // 128)
+    gsz = pw.gsz.view(torch.int16).cpu().numpy().view(np.uint16).reshape(K // 128, pw.N).T
     s2 = np.repeat((gsz & 0xFF).astype(np.int32), 128, axis=1)
     z = np.repeat((gsz >> 8).astype(np.int32), 128, axis=1)
     return (u - z) * s2, gsz

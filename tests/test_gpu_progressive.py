@@ -69,7 +69,7 @@ def check_codes(orc, g, W):
     got_u = unpack_u4(pw.codes_view().cpu().numpy(), K)
     bad = np.argwhere(got_u != u)
     assert bad.shape[0] == 0, f"{bad.shape[0]} 4-bit value mismatches, first {bad[:4].tolist()}"
-    gsz = pw.gsz.view(torch.int16).cpu().numpy().view(np.uint16).reshape(N, K // 128)
+    gsz = pw.gsz.view(torch.int16).cpu().numpy().view(np.uint16).reshape(K // 128, N).T
     assert np.array_equal(gsz & 0xFF, s2) and np.array_equal(gsz >> 8, z)
     assert np.array_equal(pw.s_w.cpu().numpy().view(np.uint32), s1.view(np.uint32))
     return q8p, s1
