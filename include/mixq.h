@@ -116,9 +116,12 @@ typedef struct mixq_act_state {
  */
 typedef struct mixq_weight {
     void *wq;          /* bits 8: int8 [N, K] row-major codes in [-127, 127];
-                          bits 4: uint8 [N, K/2]; each 32-bit word holds 8
-                          consecutive k: byte j = (q[k+j] & 15) | (q[k+j+4] & 15) << 4,
-                          codes in [-7, 7]                                        */
+                          bits 4: K-tile-major inside 32-row blocks, uint8
+                          [ceil(N/32)][K/64][32 rows][32 bytes]: row n's 64 k of
+                          tile k/64 are the 32 bytes at block n/32, row n%32, as
+                          8 words in k order; each word holds 8 consecutive k:
+                          byte j = (q[k+j] & 15) | (q[k+j+4] & 15) << 4, codes
+                          in [-7, 7]; rows of the last block past N unused    */
     float *s_w;        /* [N] per-output-channel scale                            */
     uint16_t *w_out;   /* fp16 [N, mixq_outlier_ld(k_cap)]: W at the outlier
                           channels in set order, then zeros                       */
@@ -166,7 +169,8 @@ int64_t mixq_outlier_ld(int32_t k_cap);
 int64_t mixq_bitmap_words(int64_t K);
 /* Number of 32-bit words of a state's work area: 2 * ceil(K / 32) + 4. */
 int64_t mixq_state_work_words(int64_t K);
-/* Bytes of mixq_weight.wq: N*K for 8 bits, N*K/2 for 4 bits; 0 if invalid. */
+/* Bytes of mixq_weight.wq: N*K for 8 bits, ceil(N/32)*32*K/2 for 4 bits
+ * (whole 32-row blocks); 0 if invalid. */
 size_t mixq_packed_weight_bytes(int64_t N, int64_t K, int32_t bits);
 
 /*

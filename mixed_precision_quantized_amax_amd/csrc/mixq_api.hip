@@ -90,7 +90,7 @@ int64_t mixq_state_work_words(int64_t K) { return K <= 0 ? 0 : 2 * mixq::bitmap_
 size_t mixq_packed_weight_bytes(int64_t N, int64_t K, int32_t bits) {
     if (N <= 0 || K <= 0 || K % 2) return 0;
     if (bits == 8) return (size_t)N * (size_t)K;
-    if (bits == 4) return (size_t)N * (size_t)(K / 2);
+    if (bits == 4) return (size_t)((N + 31) / 32 * 32) * (size_t)(K / 2);  // whole 32-row blocks
     return 0;
 }
 

@@ -220,9 +220,10 @@ void gemm_kernel(GemmArgs a) {
     const int wrow_bytes = BITS == 8 ? K : K / 2;
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.Xq + (int64_t)m0 * K, (int64_t)rows_a * K);
+    // INT4 rows are stored in whole 32-row blocks (the tile's rows start on one)
     const __amdgpu_buffer_rsrc_t rB =
         make_rsrc(static_cast<const uint8_t*>(a.wq) + (int64_t)n0 * wrow_bytes,
-                  (int64_t)rows_b * wrow_bytes);
+                  (int64_t)(BITS == 8 ? rows_b : (rows_b + 31) / 32 * 32) * wrow_bytes);
 
     // ---- per-lane load slots ------------------------------------------------------
     // Wave instruction i fills rows R0..R0+15 (R0 = (i*NW + wave)*16); lane l
@@ -239,13 +240,12 @@ void gemm_kernel(GemmArgs a) {
         const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
         voffB[i] = row * K + (((lane & 3) ^ swz(row)) << 4);
     }
-    // INT4: wave instruction i covers packed rows R0..R0+31, lane -> row R0 + l/2, half l%2
+    // INT4: wave instruction i covers packed rows R0..R0+31 (R0 = 32 (i NW +
+    // wave), one 32-row block of the K-tile-major layout), lane -> row R0 +
+    // l/2, half l%2: the instruction reads the block's 1 KiB for one K tile
     int voffB4[C::kBI4];
 #pragma unroll
-    for (int i = 0; i < C::kBI4; ++i) {
-        const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
-        voffB4[i] = row * (K / 2) + ((lane & 1) << 4);
-    }
+    for (int i = 0; i < C::kBI4; ++i) voffB4[i] = (i * C::kNW + wave) * KT * 1024 + lane * 16;
 
     // ---- per-lane fragment read offsets (bytes within a stage) ------------------------
     const int fr = lane & 31;
@@ -531,7 +531,7 @@ void gemm_kernel(GemmArgs a) {
             } else {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i)
-                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * 1024, 0);
                 gzload(kt, R);
             }
         };
@@ -567,7 +567,7 @@ void gemm_kernel(GemmArgs a) {
             } else {
 #pragma unroll
                 for (int i = 0; i < C::kBI4; ++i)
-                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * (kBK / 2), 0);
+                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * 1024, 0);
                 gzload(kt, R);
             }
         };

@@ -33,6 +33,12 @@ __device__ __forceinline__ int64_t src_row(int64_t n, int64_t N, int gated) {
 // first level to INT8 with the range 119, then per group of 128 channels (16
 // chunks = 16 consecutive lanes) a 4-bit value, an integer scale and a zero;
 // integer steps with IEEE binary32 divisions whose ties are exact.
+// Byte offset of 4-bit chunk c (8 consecutive k, 4 bytes) of packed row n:
+// K-tile-major inside 32-row blocks, [N/32][K/64][32 rows][32 bytes].
+__device__ __forceinline__ int64_t int4_offset(int64_t n, int c, int K) {
+    return ((n / 32) * (K / 64) + c / 8) * 1024 + (n % 32) * 32 + (c % 8) * 4;
+}
+
 template <int CPT, int BITS, bool PROG = false>
 __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_t* __restrict__ W,
                                                                     int64_t N, int32_t K,
@@ -55,9 +61,14 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
         if (rmap) {
             srow = rmap[n];
             if (srow < 0 || srow >= n_out) {
-                uint8_t* dst = static_cast<uint8_t*>(wq) + n * (int64_t)(BITS == 8 ? K : K / 2);
-                for (int c = tid; c < nchunks * (BITS == 8 ? 2 : 1); c += kThreads)
-                    *reinterpret_cast<uint32_t*>(dst + (int64_t)c * 4) = 0u;
+                uint8_t* const w8 = static_cast<uint8_t*>(wq);
+                for (int c = tid; c < nchunks; c += kThreads) {
+                    if (BITS == 8)
+                        *reinterpret_cast<uint2*>(w8 + n * (int64_t)K + (int64_t)c * 8) =
+                            make_uint2(0u, 0u);
+                    else
+                        *reinterpret_cast<uint32_t*>(w8 + int4_offset(n, c, K)) = 0u;
+                }
                 if constexpr (PROG)
                     for (int g = tid; g < ngroups; g += kThreads)
                         gsz[g * N + n] = (uint16_t)1;  // s2 1, z 0
@@ -149,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     word |= (((uint32_t)q[j] & 0xFu) | (((uint32_t)q[j + 4] & 0xFu) << 4)) << (8 * j);
-                uint8_t* dst = static_cast<uint8_t*>(wq) + n * (int64_t)(K / 2) + (int64_t)c * 4;
-                *reinterpret_cast<uint32_t*>(dst) = word;
+                *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(wq) + int4_offset(n, c, K)) =
+                    word;
             }
         }
     }

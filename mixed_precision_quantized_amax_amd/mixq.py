@@ -209,7 +209,10 @@ class PackedWeight:
         """int8 [N, K] (bits 8) or packed uint8 [N, K/2] (bits 4) view of wq."""
         if self.bits == 8:
             return self.wq.view(torch.int8).view(self.N, self.K)
-        return self.wq.view(self.N, self.K // 2)
+        # K-tile-major inside 32-row blocks: [N/32][K/64][32 rows][32 bytes]
+        nb = (self.N + 31) // 32
+        t = self.wq.view(nb, self.K // 64, 32, 32).permute(0, 2, 1, 3)
+        return t.reshape(nb * 32, self.K // 2)[: self.N]
 
     def w_out_view(self) -> torch.Tensor:
         return self.w_out[: self.N * outlier_ld(self.k_cap)].view(self.N, outlier_ld(self.k_cap))

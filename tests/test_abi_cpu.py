@@ -38,6 +38,7 @@ def test_size_helpers():
     assert L.mixq_state_work_words(8192) == 2 * 256 + 4
     assert L.mixq_packed_weight_bytes(8192, 8192, 8) == 8192 * 8192
     assert L.mixq_packed_weight_bytes(8192, 8192, 4) == 8192 * 4096
+    assert L.mixq_packed_weight_bytes(40, 128, 4) == 64 * 64          # whole 32-row blocks
     assert L.mixq_packed_weight_bytes(8, 64, 5) == 0
     assert L.mixq_version() >= 100
     for c in range(6):
