@@ -288,3 +288,17 @@ def test_split_k(orc, M, K, N, n_out):
     torch.cuda.synchronize()
     assert np.array_equal(g.Y.cpu().numpy().view(np.uint32), yh)
     assert int(g.ws[:1024].abs().sum().cpu()) == 0, "tile counters not cleared"
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_few_tokens_full_weight(orc, M, bits):
+    """Decoding a handful of tokens through the full 8192 x 8192 weight: a
+    single partial row tile over 64 column tiles.  Every output against the
+    oracle, with the split-K workspace when the shape takes one and without;
+    both give the same Y bit for bit."""
+    X, W, _ = workloads.random_case(seed=40 + M, M=M, K=8192, N=8192, n_out=6)
+    g, _ = full_compare(orc, X, W, bits, 6.0, 64, tag=f"few M={M}")
+    h = GpuLayer(W, bits, 6.0, 64, M, split=False)
+    h.step(X)
+    assert np.array_equal(g.Y.cpu().numpy().view(np.uint32), h.Y.cpu().numpy().view(np.uint32))
