@@ -142,14 +142,28 @@ PROG_MUTANTS = [
     ("prog_zero_sign", "z = _rne_div(-lo, s2)", "z = _rne_div(lo, s2) % 16"),
 ]
 
+MIXED_MUTANTS = [
+    ("mixed_mask_inverted", "codes = np.where(sal[:, None], q8, q4p)",
+     "codes = np.where(~sal[:, None], q8, q4p)"),
+    ("mixed_scales_swapped", "scales = np.where(sal, s8, s4)", "scales = np.where(sal, s4, s8)"),
+    ("mixed_int4_rows_symmetric", "q4p, s4, *_ = progressive_quantize_weight(Wh, group)",
+     "q4p, s4 = o.quantize_weight(Wh, 4)"),
+    ("mixed_int4_values_not_rebuilt", "q4p, s4, *_ = progressive_quantize_weight(Wh, group)",
+     "_, s4, q4p, *_ = progressive_quantize_weight(Wh, group)"),
+]
+PIN_KEY = {"progressive_quantize_weight": "progressive",
+           "mixed_feature_quantize_weight": "mixed_feature"}
+
 
 @pytest.mark.parametrize("fn,name,old,new",
                          [("rmsnorm", *m) for m in RMS_MUTANTS] +
                          [("residual_add", *m) for m in RES_MUTANTS] +
                          [("swiglu", *m) for m in SWIGLU_MUTANTS] +
-                         [("progressive_quantize_weight", *m) for m in PROG_MUTANTS],
+                         [("progressive_quantize_weight", *m) for m in PROG_MUTANTS] +
+                         [("mixed_feature_quantize_weight", *m) for m in MIXED_MUTANTS],
                          ids=[m[0] for m in RMS_MUTANTS] + [m[0] for m in RES_MUTANTS] +
-                         [m[0] for m in SWIGLU_MUTANTS] + [m[0] for m in PROG_MUTANTS])
+                         [m[0] for m in SWIGLU_MUTANTS] + [m[0] for m in PROG_MUTANTS] +
+                         [m[0] for m in MIXED_MUTANTS])
 def test_prologue_mutant_is_caught(fn, name, old, new):
     import inspect
     import textwrap
@@ -161,7 +175,8 @@ def test_prologue_mutant_is_caught(fn, name, old, new):
     src = textwrap.dedent(inspect.getsource(getattr(mixq_oracle, fn)))
     assert src.count(old) == 1, f"mutation site not found: {old!r}"
     ns = {"np": np, "Q1_PROGRESSIVE": mixq_oracle.Q1_PROGRESSIVE, "_rne_div": mixq_oracle._rne_div,
-          "GROUP": mixq_oracle.GROUP}
+          "GROUP": mixq_oracle.GROUP, "Oracle": Oracle,
+          "progressive_quantize_weight": mixq_oracle.progressive_quantize_weight}
     exec(compile(src.replace(old, new), f"<{name}>", "exec"), ns)
 
     class Mutant(Oracle):
@@ -171,7 +186,7 @@ def test_prologue_mutant_is_caught(fn, name, old, new):
     o = Mutant()
     failed = []
     for pin in oracle_pins.ALL_PINS:
-        key = "progressive" if fn == "progressive_quantize_weight" else fn
+        key = PIN_KEY.get(fn, fn)
         if key not in pin.__name__:
             continue
         try:
