@@ -692,17 +692,16 @@ template <int CPT_G, int CPT_R, bool NORM, bool RES>
 int launch_act(const ActArgs& a, hipStream_t st) {
     constexpr int kRowsPerBlock = kGateThreads / kWave / kGateWaves;
     int64_t g1 = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
-    // up to 1024 blocks: at M = 2048 each block takes two tokens, the second
-    // one's loads in flight while the first is processed (measured: 1024
-    // blocks 13.6 us, 2048 blocks 14.4 us, 512 blocks 16.4 us per call)
-    // (all variants fit four blocks per CU: at most 127 VGPRs).
-    // The RMSNorm pass has more arithmetic per byte: with one token per
-    // block (2048 blocks at M = 2048) the second round's loads overlap the
-    // first round's arithmetic (measured: 25.0-25.7 us against 27.0-27.5 us
-    // with 1024 blocks, 30.2-30.4 us with 512).  With the residual add the
-    // second round's extra stream of D and H costs more than that (31.7-32.0
-    // us against 28.9-29.4 us), so it keeps 1024.
-    const int64_t cap = NORM && !RES ? 2048 : 1024;
+    // Up to 2048 blocks (all variants fit four blocks per CU: at most 127
+    // VGPRs).  At M = 2048 that is one token per block and two rounds of the
+    // device: the second round's loads overlap the first round's arithmetic.
+    // Measured with alternating builds on one box, per call at M = 2048,
+    // K = 8192: the plain pass 18.8-19.1 us against 20.0-20.7 us with 1024
+    // blocks of two tokens each; the RMSNorm pass 25.0-25.7 us against
+    // 27.0-27.5 us (30.2-30.4 us with 512).  With the residual add the
+    // second round's extra streams of D and H cost more than the overlap
+    // gains (31.7-32.0 us against 28.9-29.4 us), so it keeps 1024.
+    const int64_t cap = RES ? 1024 : 2048;
     const int grid = (int)(g1 < cap ? g1 : cap);
     const size_t lds = (size_t)a.words * 8 + (NORM ? (size_t)a.K * 2 : 0);
     hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES>), dim3(grid),
