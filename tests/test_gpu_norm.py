@@ -96,6 +96,7 @@ def layer_pair(orc, W, gamma, eps, tau, k_cap, M, ldh=None):
     (1, 64, 32, 0, 1e-5, False), (37, 512, 96, 3, 1e-5, False), (130, 4096, 256, 20, 1e-6, False),
     (64, 8192, 128, 82, 1e-5, False), (5, 32768, 64, 10, 1e-5, False),
     (300, 1024, 200, 0, 0.0, False), (40, 2048, 64, 4, 1e-5, True), (3, 32768, 32, 0, 0.0, True),
+    (4097, 1024, 64, 6, 1e-5, False),  # several tokens per block, an odd count for some
 ])
 def test_norm_random(orc, M, K, N, n_out, eps, wide):
     H, gamma = make_case(M * 7 + K + n_out, M, K, n_out, wide)
@@ -243,6 +244,7 @@ def split_case(H, seed):
 @pytest.mark.parametrize("M,K,N,n_out,lds", [
     (1, 64, 32, 0, None), (37, 512, 96, 3, None), (130, 4096, 256, 20, (4104, 4096, 4112)),
     (64, 8192, 128, 82, None), (5, 32768, 64, 10, None),
+    (2049, 1024, 64, 6, None),  # two and three tokens per block
 ])
 def test_res_random(orc, M, K, N, n_out, lds):
     Hs, gamma = make_case(M * 5 + K + n_out, M, K, n_out)
