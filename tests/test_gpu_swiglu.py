@@ -151,3 +151,19 @@ def test_swiglu_full_size(orc):
     say(f"[swiglu] full: max|dY|/max|Y| = {err:.2e} over {rows.size} samples")
     assert err <= TOL, err
     assert np.isfinite(g["Yh"]).all()
+
+
+def _random_cases(n=10, seed=77):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 500)), 64 * int(rng.integers(1, 25)), 64 * int(rng.integers(1, 11)),
+             int(rng.integers(0, 20)), int(rng.choice([8, 4])), bool(rng.integers(0, 2)))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("i,M,K,N,n_out,bits,ws", _random_cases())
+def test_swiglu_random_shapes(orc, i, M, K, N, n_out, bits, ws):
+    """Seeded random shapes through the automatic launch choice (N a
+    multiple of 64, as a gated weight requires), INT8 and INT4, with and
+    without a split-K workspace."""
+    X, W, _ = workloads.random_case(seed=500 + i, M=M, K=K, N=N, n_out=n_out)
+    check_swiglu(orc, X, W, bits=bits, ws=ws, tag=f"rand{i}")
