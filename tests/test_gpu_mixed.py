@@ -114,8 +114,16 @@ def check_pack(orc, g, W, sal, W_out):
 def test_mixed_random(orc, tile, M, K, N, S, n_act):
     X, W, _ = workloads.random_case(seed=M + K + N + S, M=M, K=K, N=N, n_out=n_act)
     sal = salient_set(N, S, M + S)
-    say(f"[mixed] tile{tile} M={M} K={K} N={N} S={S}")
-    g = run_mixed(X, W, sal, 6.0, 64)
+    check_mixed(orc, X, W, sal, tag=f"tile{tile}")
+
+
+def check_mixed(orc, X, W, sal, ws=False, tag=""):
+    """Both parts' codes, scales and outlier columns, both products' int32
+    accumulators bit for bit, every Y column written, Y within tolerance."""
+    M, K = X.shape
+    N = W.shape[0]
+    say(f"[mixed] {tag} M={M} K={K} N={N} S={int(sal.sum())} ws={ws}")
+    g = run_mixed(X, W, sal, 6.0, 64, ws=ws)
     o = OracleLayer(W=W, bits=8, tau=6.0, k_cap=64, ldo=mixq.outlier_ld(64), oracle=orc)
     r = o.step(X, products=False)
     assert g["count"] == r.count
@@ -131,6 +139,24 @@ def test_mixed_random(orc, tile, M, K, N, S, n_act):
     assert not np.isnan(g["Y"]).any(), "an output feature was not written"
     err = check_y(g["Y"], Y)
     say(f"[mixed] ok count={r.count} max|dY|/max|Y|={err:.2e}")
+
+
+def _random_cases(n=10, seed=91):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 600))
+        out.append((i, int(rng.integers(1, 600)), 128 * int(rng.integers(1, 17)), N,
+                    int(rng.integers(0, N + 1)), int(rng.integers(0, 30)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("i,M,K,N,S,n_act,ws", _random_cases())
+def test_mixed_random_shapes(orc, i, M, K, N, S, n_act, ws):
+    """Seeded random shapes and salient counts (none to all output features)
+    through the automatic launch choice, with and without workspaces."""
+    X, W, _ = workloads.random_case(seed=700 + i, M=M, K=K, N=N, n_out=n_act)
+    check_mixed(orc, X, W, salient_set(N, S, 800 + i), ws=ws, tag=f"rand{i}")
 
 
 def test_mixed_full_size(orc):
