@@ -397,8 +397,13 @@ class OracleLayer:
         self.Wq, self.s_w = self.oracle.quantize_weight(self.W, self.bits)
 
     def step(self, X: np.ndarray, products: bool = True) -> LayerResult:
+        """One call: gate and union against the set carried from the previous
+        call, quantize with the updated set, gather the weight's outlier
+        columns for that same set, then the two products and the output with
+        the updated set size."""
         o = self.oracle
-        new_set, count, flag = o.update_outlier_set(X, self.tau, self.in_set, self.k_cap)
+        before = self.in_set
+        new_set, count, flag = o.update_outlier_set(X, self.tau, before, self.k_cap)
         self.in_set = new_set
         Xq, s_x, X_out = o.quantize_act(X, self.in_set, self.ldo)
         res = LayerResult(in_set=self.in_set.copy(), idx=o.outlier_list(self.in_set),

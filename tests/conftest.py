@@ -1,3 +1,4 @@
+import pytest
 import os
 import sys
 
@@ -11,3 +12,13 @@ if HERE not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture
+def tile(request):
+    """Force one GEMM kernel variant (a name of mixq.GEMM_VARIANTS) for the
+    test, then restore the automatic choice."""
+    from mixed_precision_quantized_amax_amd import mixq
+    mixq.set_gemm_variant(request.param)
+    yield request.param
+    mixq.set_gemm_variant("auto")

@@ -415,6 +415,72 @@ def pin_decode_sequence(o):
         cur = cur_new
 
 
+def pin_layer_driver(o, layer_cls=None):
+    """The decode driver every GPU comparison runs as its checker
+    (OracleLayer.step, and run_layer for a single call): over a planted
+    multi-step run -- persistent outlier channels, transient ones on some
+    steps, a step where nothing exceeds tau -- after every step the set is
+    the union of every channel seen above tau so far (brute-force column
+    scan, carried across steps here), the flag is the brute-force gate on the
+    channels not yet cached, the ids are that set ascending, and Xq, s_x,
+    X_out, acc and Y equal the single oracle calls (each pinned above)
+    composed here by hand with that set: weight columns gathered for the
+    current set, the current set size passed to the output.  MixQ article,
+    "MixQ的解决方案": Fig. 9 (outliers recur in fixed channels) and the amax
+    paragraph (re-detect only when the amax of the uncached channels exceeds
+    the threshold)."""
+    from oracle.mixq_oracle import OracleLayer, run_layer
+    layer_cls = layer_cls or OracleLayer
+    M, K, N, steps, tau, ldo = 6, 192, 40, 9, 6.0, 32
+    r = _rng(41)
+    W = _wcase(41, N, K)
+    pers = np.sort(r.choice(K, 4, replace=False))
+    rest = np.setdiff1d(np.arange(K), pers)
+    events = {1: r.choice(rest, 2, replace=False), 4: r.choice(rest, 3, replace=False),
+              6: r.choice(rest, 1, replace=False)}
+    quiet = {3, 5}  # steps on which the persistent channels stay below tau
+    layer = layer_cls(W=W, bits=8, tau=tau, k_cap=ldo, ldo=ldo, oracle=o)
+    Wq, s_w = o.quantize_weight(W, 8)
+    seen = np.zeros(K, bool)
+    fires = []
+    for st in range(steps):
+        X = np.clip(r.standard_normal((M, K)), -4, 4).astype(np.float32)
+        if st not in quiet:
+            X[:, pers] = r.uniform(20, 100, (M, pers.size)) * np.where(
+                r.random((M, pers.size)) < .5, -1, 1)
+        if st in events:
+            e = events[st]
+            X[:, e] = r.uniform(20, 100, (M, e.size))
+        X = X.astype(np.float16)
+        over = (np.abs(X.astype(np.float64)) > tau).any(axis=0)
+        fire = bool((over & ~seen).any())
+        seen |= over
+        res = layer.step(X)
+        assert res.flag == int(fire), st
+        assert (res.in_set.astype(bool) == seen).all(), st
+        assert res.count == int(seen.sum()), st
+        assert np.array_equal(res.idx, np.flatnonzero(seen)), st
+        cur = seen.astype(np.uint8)
+        Xq, s_x, X_out = o.quantize_act(X, cur, ldo)
+        W_out = o.gather_weight_cols(W, cur, ldo)
+        acc = o.int_gemm(Xq, Wq)
+        Y = o.output(acc, s_x, s_w, X_out, W_out, int(seen.sum()))
+        assert np.array_equal(res.Xq, Xq) and np.array_equal(res.s_x, s_x), st
+        assert np.array_equal(res.X_out, X_out), st
+        assert np.array_equal(res.acc, acc), st
+        assert np.array_equal(res.Y, Y), st
+        fires.append(fire)
+    assert fires == [True, True, False, False, True, False, True, False, False], fires
+    # run_layer: one call on an empty set is that same composition
+    X = X.astype(np.float16)
+    one = run_layer(X, W, bits=8, tau=tau, k_cap=ldo, ldo=ldo, oracle=o)
+    cur = (np.abs(X.astype(np.float64)) > tau).any(axis=0).astype(np.uint8)
+    Xq, s_x, X_out = o.quantize_act(X, cur, ldo)
+    Y = o.output(o.int_gemm(Xq, Wq), s_x, s_w, X_out, o.gather_weight_cols(W, cur, ldo),
+                 int(cur.sum()))
+    assert one.count == int(cur.sum()) and np.array_equal(one.Y, Y)
+
+
 def pin_sampled_output(o):
     """The per-pair entry point against an int64 matrix product and an FP64
     sum over the outlier columns, at random (row, col) pairs."""
@@ -766,7 +832,7 @@ ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode
             pin_int_gemm_bruteforce, pin_split_identity, pin_output_vs_dequant,
             pin_output_vs_truth_bound, pin_no_outlier_textbook, pin_all_outlier,
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
-            pin_decode_sequence, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
+            pin_decode_sequence, pin_layer_driver, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
             pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals,
             pin_residual_add, pin_swiglu, pin_progressive_levels, pin_progressive_no_overflow,
             pin_mixed_feature]

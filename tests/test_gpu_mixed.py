@@ -5,7 +5,6 @@ progressive INT4 one; each product writes its own columns of Y.  Checked:
 every row's codes, group entries and scales bit for bit against the oracle's
 mixed codes, the outlier columns, both products' int32 accumulators bit for
 bit, every Y column written, Y within 1e-3 * max|Y|."""
-import os
 
 import numpy as np
 import pytest
@@ -22,16 +21,6 @@ pytestmark = pytest.mark.gpu
 def orc():
     return Oracle()
 
-
-@pytest.fixture
-def tile(request):
-    old = os.environ.get("MIXQ_GEMM_TILE")
-    os.environ["MIXQ_GEMM_TILE"] = request.param
-    yield request.param
-    if old is None:
-        del os.environ["MIXQ_GEMM_TILE"]
-    else:
-        os.environ["MIXQ_GEMM_TILE"] = old
 
 
 def unpack_u4(packed: np.ndarray, K: int) -> np.ndarray:
@@ -106,7 +95,7 @@ def check_pack(orc, g, W, sal, W_out):
     return codes, scales
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11", "13", "14", "15"],
+@pytest.mark.parametrize("tile", ["auto", "256x256", "128x128", "256x256_swp", "256x256_kpair", "128x128_kpair", "128x128_swp"],
                          indirect=True)
 @pytest.mark.parametrize("M,K,N,S,n_act", [(37, 256, 128, 5, 3), (130, 1024, 384, 100, 9),
                                            (257, 2048, 520, 129, 0), (64, 1024, 256, 0, 40),

@@ -5,7 +5,6 @@ activation codes and scales, the FP16 outlier matrices, the weight codes and
 scales, and the INT32 accumulators.  Within max|dY| <= 1e-3 * max|Y|: the
 fp32 output.  Small cases are compared element by element; the full-size
 workloads on all of the quantized data and on sampled outputs."""
-import os
 
 import numpy as np
 import pytest
@@ -18,27 +17,13 @@ from oracle import Oracle, OracleLayer
 
 pytestmark = pytest.mark.gpu
 
-TILES = {"auto": "0", "256x256": "1", "128x128": "2", "256x256_lds3": "3", "256x128": "4",
-         "256x256_lds4": "5", "256x256_pf2": "6", "256x128_pf2": "7", "256x256_adirect": "8",
-         "256x128_adirect": "9", "256x256_swp": "10", "256x128_swp": "11",
-         "256x256_kpair": "12", "256x256_kpin": "13", "128x128_kpair": "14",
-         "128x128_swp": "15"}
+TILES = list(mixq.GEMM_VARIANTS)
 
 
 @pytest.fixture(scope="module")
 def orc():
     return Oracle()
 
-
-@pytest.fixture
-def tile(request):
-    old = os.environ.get("MIXQ_GEMM_TILE")
-    os.environ["MIXQ_GEMM_TILE"] = TILES[request.param]
-    yield request.param
-    if old is None:
-        del os.environ["MIXQ_GEMM_TILE"]
-    else:
-        os.environ["MIXQ_GEMM_TILE"] = old
 
 
 def full_compare(orc, X, W, bits, tau, k_cap, layer=None, olayer=None, tag=""):
@@ -88,11 +73,9 @@ SMALL = [  # M, K, N, planted outlier channels, bits
 ]
 
 
-@pytest.mark.parametrize("tile", list(TILES), indirect=True)
+@pytest.mark.parametrize("tile", TILES, indirect=True)
 @pytest.mark.parametrize("M,K,N,n_out,bits", SMALL)
 def test_small_random(orc, tile, M, K, N, n_out, bits):
-    if tile.startswith("256x256_lds") and bits == 4:
-        pytest.skip("INT4 weights always take the register-staged loader")
     X, W, _ = workloads.random_case(7, M, K, N, n_out)
     full_compare(orc, X, W, bits, 6.0, min(K, 128), tag=f"small[{tile}]")
 

@@ -2,7 +2,6 @@
 oracle: the packed 4-bit values, the group table (s2 | z << 8) and the
 first-level scales bit for bit, the int32 accumulators of the product with
 the rebuilt INT8 codes bit for bit, and Y within 1e-3 * max|Y|."""
-import os
 
 import numpy as np
 import pytest
@@ -19,16 +18,6 @@ pytestmark = pytest.mark.gpu
 def orc():
     return Oracle()
 
-
-@pytest.fixture
-def tile(request):
-    old = os.environ.get("MIXQ_GEMM_TILE")
-    os.environ["MIXQ_GEMM_TILE"] = request.param
-    yield request.param
-    if old is None:
-        del os.environ["MIXQ_GEMM_TILE"]
-    else:
-        os.environ["MIXQ_GEMM_TILE"] = old
 
 
 def unpack_u4(packed: np.ndarray, K: int) -> np.ndarray:
@@ -75,7 +64,7 @@ def check_codes(orc, g, W):
     return q8p, s1
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "4", "6", "8", "10", "11", "15"], indirect=True)
+@pytest.mark.parametrize("tile", ["auto", "256x256", "128x128", "256x256_swp", "128x128_swp"], indirect=True)
 @pytest.mark.parametrize("M,K,N,n_out", [(37, 256, 128, 3), (130, 1024, 384, 9),
                                          (257, 2048, 520, 0), (64, 4096, 256, 40)])
 def test_progressive_random(orc, tile, M, K, N, n_out):

@@ -4,7 +4,6 @@ scales and outlier columns equal the oracle's rows in the documented
 interleaved order, the int32 accumulators are bit-exact in that order, and
 the fp16 silu(gate) * up is within 1e-3 * max of the oracle's float64 SwiGLU
 of its Y (fp16 rounding alone is 2^-11 relative)."""
-import os
 
 import numpy as np
 import pytest
@@ -23,16 +22,6 @@ TOL = 1e-3
 def orc():
     return Oracle()
 
-
-@pytest.fixture
-def tile(request):
-    old = os.environ.get("MIXQ_GEMM_TILE")
-    os.environ["MIXQ_GEMM_TILE"] = request.param
-    yield request.param
-    if old is None:
-        del os.environ["MIXQ_GEMM_TILE"]
-    else:
-        os.environ["MIXQ_GEMM_TILE"] = old
 
 
 def packed_order(N):
@@ -101,7 +90,7 @@ def check_swiglu(orc, X, W, bits=8, tau=6.0, k_cap=64, ws=False, tag=""):
     return g
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "13", "14"], indirect=True)
+@pytest.mark.parametrize("tile", ["auto", "256x256", "128x128", "256x256_kpair", "128x128_kpair"], indirect=True)
 @pytest.mark.parametrize("M,K,N,n_out", [(37, 512, 128, 3), (130, 1024, 384, 9),
                                          (257, 2048, 512, 0)])
 def test_swiglu_random(orc, tile, M, K, N, n_out):
@@ -109,7 +98,7 @@ def test_swiglu_random(orc, tile, M, K, N, n_out):
     check_swiglu(orc, X, W, tag=f"tile{tile}")
 
 
-@pytest.mark.parametrize("tile", ["0", "10"], indirect=True)
+@pytest.mark.parametrize("tile", ["auto", "256x256_swp"], indirect=True)
 def test_swiglu_int4(orc, tile):
     X, W, _ = workloads.random_case(seed=44, M=100, K=1024, N=512, n_out=5)
     check_swiglu(orc, X, W, bits=4, tag=f"int4 tile{tile}")

@@ -194,3 +194,60 @@ def test_prologue_mutant_is_caught(fn, name, old, new):
         except (AssertionError, OverflowError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught mutant {name}"
+
+
+# Mistakes planted in the decode driver (``OracleLayer.step``): the set not
+# carried from call to call, the weight's outlier columns gathered for the
+# previous set, a wrong set size passed to the output.
+DRIVER_MUTANTS = [
+    ("driver_set_not_persisted",
+     "o.update_outlier_set(X, self.tau, before, self.k_cap)",
+     "o.update_outlier_set(X, self.tau, np.zeros_like(before), self.k_cap)"),
+    ("driver_wout_previous_set",
+     "W_out = o.gather_weight_cols(self.W, self.in_set, self.ldo)",
+     "W_out = o.gather_weight_cols(self.W, before, self.ldo)"),
+    ("driver_wrong_count",
+     "res.Y = o.output(res.acc, s_x, self.s_w, X_out, W_out, count)",
+     "res.Y = o.output(res.acc, s_x, self.s_w, X_out, W_out, max(count - 1, 0))"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", DRIVER_MUTANTS, ids=[m[0] for m in DRIVER_MUTANTS])
+def test_driver_mutant_is_caught(name, old, new):
+    import inspect
+    import textwrap
+
+    import numpy as np
+
+    from oracle import mixq_oracle
+
+    src = textwrap.dedent(inspect.getsource(mixq_oracle.OracleLayer.step))
+    assert src.count(old) == 1, f"mutation site not found: {old!r}"
+    ns = {"np": np, "LayerResult": mixq_oracle.LayerResult}
+    exec(compile(src.replace(old, new), f"<{name}>", "exec"), ns)
+
+    class Mutant(mixq_oracle.OracleLayer):
+        step = ns["step"]
+
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_layer_driver(Oracle(), layer_cls=Mutant)
+
+
+def test_driver_unmutated_copy_passes():
+    """The copy mechanism itself leaves a working driver: the same source
+    recompiled without a change passes the pin."""
+    import inspect
+    import textwrap
+
+    import numpy as np
+
+    from oracle import mixq_oracle
+
+    src = textwrap.dedent(inspect.getsource(mixq_oracle.OracleLayer.step))
+    ns = {"np": np, "LayerResult": mixq_oracle.LayerResult}
+    exec(compile(src, "<copy>", "exec"), ns)
+
+    class Copy(mixq_oracle.OracleLayer):
+        step = ns["step"]
+
+    oracle_pins.pin_layer_driver(Oracle(), layer_cls=Copy)
