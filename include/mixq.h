@@ -59,10 +59,12 @@ extern "C" {
 enum {
     MIXQ_OK = 0,
     MIXQ_ERR_INVALID_ARG = 1,        /* null pointer, size <= 0, bad enum, ...   */
-    MIXQ_ERR_UNSUPPORTED_SHAPE = 2,  /* K not a multiple of 64, or too large    */
+    MIXQ_ERR_UNSUPPORTED_SHAPE = 2,  /* K not a multiple of 64, or a size whose
+                                        byte offsets would leave 32 bits        */
     MIXQ_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950            */
     MIXQ_ERR_NO_DEVICE = 4,          /* no HIP device visible                    */
-    MIXQ_ERR_HIP = 5                 /* a HIP launch reported an error          */
+    MIXQ_ERR_HIP = 5,                /* a HIP launch reported an error          */
+    MIXQ_ERR_WORKSPACE = 6           /* a workspace was given but is too small   */
 };
 
 /* ---- limits --------------------------------------------------------------- */
@@ -82,6 +84,9 @@ enum {
 #define MIXQ_OUT_F32 0               /* Y fp32 [M, N]                            */
 #define MIXQ_OUT_SWIGLU_F16 1        /* gated weight: Y fp16 [M, N/2] =
                                         silu(gate) * up                          */
+#define MIXQ_OUT_F16 2               /* Y fp16 [M, N]: the fp32 output rounded to
+                                        nearest, ties to even                    */
+#define MIXQ_OUT_BF16 3              /* Y bf16 [M, N]: likewise                   */
 
 /* mixq_pack_weight modes */
 #define MIXQ_PACK_FULL 0             /* quantize all of W and gather outliers   */
@@ -101,7 +106,9 @@ typedef struct mixq_act_state {
     int32_t *flag;     /* [1]      MIXQ_FLAG_* bits of the last quantize call        */
     uint32_t *bitmap;  /* [mixq_bitmap_words(K)]  bit k%32 of word k/32 = channel k  */
     uint32_t *work;    /* [mixq_state_work_words(K)]  library scratch: detection
-                          bits, rank prefix of the bitmap, counters               */
+                          bits, rank prefix of the bitmap, counters, and the
+                          serial of the committed set (unique per commit within
+                          the process, 0 for the empty set of a zeroed state)  */
     int32_t k_cap;     /* host value: capacity of the set, 0 <= k_cap <= K           */
 } mixq_act_state;
 
@@ -125,8 +132,8 @@ typedef struct mixq_weight {
     float *s_w;        /* [N] per-output-channel scale                            */
     uint16_t *w_out;   /* fp16 [N, mixq_outlier_ld(k_cap)]: W at the outlier
                           channels in set order, then zeros                       */
-    int32_t *k_out;    /* [MIXQ_GATHER_SLOTS] set size each slice of w_out was
-                          gathered for; zero-fill once                            */
+    int32_t *k_out;    /* [MIXQ_GATHER_SLOTS] serial of the state set each slice
+                          of w_out was gathered for; zero-fill once               */
     int32_t bits;      /* 8 or 4                                                  */
     int64_t N, K;
     int32_t k_cap;     /* must equal the k_cap of the states it is used with      */
@@ -284,8 +291,11 @@ int mixq_add_rmsnorm_quantize_act(const uint16_t *R, int64_t ldr, const uint16_t
  *   state  the activation state whose set selects the outlier columns
  *   mode   MIXQ_PACK_FULL: everything.  MIXQ_PACK_OUTLIER_COLS: re-gather
  *          w_out only, decided on the device (no host sync): it runs when
- *          *state->count differs from *w->k_out, and is a no-op otherwise.
- *          Call it after each mixq_quantize_act and before mixq_gemm.
+ *          the serial of the state's committed set differs from the one the
+ *          columns were gathered for, and is a no-op otherwise -- a set that
+ *          grew, a reset state, or another state whose set has the same size
+ *          all count as changed.  Call it after each mixq_quantize_act and
+ *          before mixq_gemm.
  *   w      the packed weight; w->N, w->K, w->bits, w->k_cap must match;
  *          w->gated selects the row order (see mixq_weight) and must be the
  *          same in the FULL call and every OUTLIER_COLS call
@@ -321,7 +331,11 @@ int mixq_pack_weight(const uint16_t *W, int64_t N, int64_t K, int32_t bits,
  *   acc_debug       NULL, or int32 [M, N] device: also receives acc, in
  *                   packed row order
  * Errors: as mixq_quantize_act; MIXQ_ERR_INVALID_ARG also for a w->rmap
- *         that mixq_pack_weight would reject.
+ *         that mixq_pack_weight would reject; MIXQ_ERR_UNSUPPORTED_SHAPE also
+ *         when 256 rows of Y span 2^31 bytes or more (ldy * 4 * 256 for fp32
+ *         output, ldy * 2 * 256 for 16-bit output: the kernel's store offsets
+ *         within a tile are 32-bit), or when the launch would need more than
+ *         2^31 - 1 blocks.
  */
 int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
               const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
@@ -346,16 +360,17 @@ int mixq_gemm(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  * without ws); with ws, that launch also splits K two or four ways in the
  * same way, so that its blocks fill the device.
  *
- * Otherwise, or when ws is NULL or smaller than required, the call is
- * mixq_gemm.
+ * Otherwise, or when ws is NULL, the call is mixq_gemm.
  *
- *   ws        device memory of ws_bytes, 16-byte aligned; its first 4096 bytes
- *             (tile counters) must be zero-filled once by the caller, after
- *             which every completed call leaves them zero.  Calls sharing a
- *             ws must not overlap (one stream, or serialized).
- *   ws_bytes  at least mixq_gemm_workspace_bytes(M, N, K, bits) for the split
- *             (N = w->N)
- * Other arguments and errors: as mixq_gemm.
+ *   ws        NULL, or device memory of ws_bytes, 16-byte aligned; its first
+ *             4096 bytes (tile counters) must be zero-filled once by the
+ *             caller, after which every completed call leaves them zero.
+ *             Calls sharing a ws must not overlap (one stream, or serialized).
+ *   ws_bytes  at least mixq_gemm_workspace_bytes(M, N, K, bits) (N = w->N)
+ * Other arguments: as mixq_gemm.
+ * Errors: as mixq_gemm; MIXQ_ERR_WORKSPACE when ws is given and the product
+ *         splits but ws_bytes is below what the split needs (nothing is
+ *         enqueued).
  */
 int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  const mixq_act_state *state, const mixq_weight *w, int64_t M, float *Y,
@@ -363,7 +378,11 @@ int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
 
 /*
  * mixq_gemm_ex -- mixq_gemm_ws with a choice of output.  MIXQ_OUT_F32 is
- * mixq_gemm_ws.  MIXQ_OUT_SWIGLU_F16 is for the fused gate-and-up
+ * mixq_gemm_ws.  MIXQ_OUT_F16 and MIXQ_OUT_BF16 write the same layer output
+ * as 16-bit values, each the fp32 result rounded to nearest with ties to
+ * even (the pages' systems hand 16-bit activations to the next layer; the
+ * FP6 explainer, section 3, runs its linear layers into pre-allocated fp16
+ * outputs).  MIXQ_OUT_SWIGLU_F16 is for the fused gate-and-up
  * projection of a LLaMA MLP (the gated linear layer the FP6 explainer's
  * section 3 runs as one double-output kernel): w must be packed gated, and
  * the epilogue writes, for each token m and output j < N/2,
@@ -374,13 +393,14 @@ int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  * outputs never reach memory.
  *
  *   Y         MIXQ_OUT_F32: fp32 [M, ldy], ldy >= N.
+ *             MIXQ_OUT_F16 / MIXQ_OUT_BF16: fp16 / bf16 [M, ldy], ldy >= N.
  *             MIXQ_OUT_SWIGLU_F16: fp16 [M, ldy], ldy >= N/2.
- *   out_mode  MIXQ_OUT_F32 or MIXQ_OUT_SWIGLU_F16
+ *   out_mode  one of the four MIXQ_OUT_* modes
  *   acc_debug as mixq_gemm, in the packed (interleaved) column order
  * Other arguments: as mixq_gemm_ws (ws may be NULL).
- * Errors: as mixq_gemm; MIXQ_ERR_INVALID_ARG also for an unknown out_mode,
- *         MIXQ_OUT_SWIGLU_F16 with a weight not packed gated or with a row
- *         subset, or ldy < N/2.
+ * Errors: as mixq_gemm_ws; MIXQ_ERR_INVALID_ARG also for an unknown
+ *         out_mode, MIXQ_OUT_SWIGLU_F16 with a weight not packed gated, any
+ *         16-bit output with a row subset, or ldy below the output's columns.
  */
 int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  const mixq_act_state *state, const mixq_weight *w, int64_t M, void *Y,
@@ -393,6 +413,23 @@ int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  * product, two or four for the tail of a large one); 0 when nothing is
  * split. */
 size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
+
+/*
+ * mixq_set_gemm_variant -- testing hook.  Every later GEMM call in the
+ * process uses kernel variant `variant` (1..6) instead of the automatic
+ * choice (0, the default and the only mode meant for use): 1 = 256 x 256
+ * tiles with 64-byte K steps, 2 = 128 x 128 tiles with 64-byte K steps,
+ * 3 = 256 x 256 software-pipelined (INT4 weights), 4 = 256 x 256 with
+ * 128-byte K pairs (INT8 weights), 5 = 128 x 128 with 128-byte K pairs (INT8;
+ * K split under mixq_gemm_ws), 6 = 128 x 128 software-pipelined (INT4).  A
+ * variant whose loader does not fit the call (K not a multiple of 128, or
+ * the other weight width) falls back to one that does.  All variants give
+ * bit-identical accumulators; the hook lets tests cover each of them on
+ * small shapes.  Not thread-safe with respect to GEMM calls in flight on
+ * other host threads.
+ * Errors: MIXQ_ERR_INVALID_ARG for an id outside 0..6.
+ */
+int mixq_set_gemm_variant(int32_t variant);
 
 /* Text of a status code (static storage). */
 const char *mixq_status_string(int status);

@@ -45,6 +45,7 @@ struct ActArgs {
     int32_t* rank;      // work[words, 2 words): exclusive popcount prefix of bitmap
     uint32_t* marker;   // work[2 words]
     uint32_t* arrive;   // work[2 words + 1]
+    uint32_t* set_id;   // work[2 words + 2]: serial of the committed set (0 = empty)
     int32_t k_cap;
     int32_t words;
     int32_t nchunks;  // K / 8
@@ -629,6 +630,19 @@ __device__ int scan_popcounts(const uint32_t* src, int words, int* prefix, int* 
 
 constexpr int kReqThreads = 256;
 
+// Serial numbers of committed sets, unique within the process on each device
+// (0 is never issued: it names the empty set of a zero-filled state).  A
+// packed weight records the serial its outlier columns were gathered for, so
+// a set that changed -- grown, reset, or another state's set of the same
+// size -- is always told apart from the one the columns hold.
+__device__ uint32_t g_set_serial = 0u;
+
+__device__ __forceinline__ uint32_t next_set_serial() {
+    uint32_t s = atomicAdd(&g_set_serial, 1u) + 1u;
+    if (s == 0u) s = atomicAdd(&g_set_serial, 1u) + 1u;  // after 2^32 commits: skip 0
+    return s;
+}
+
 template <int CPT, bool NORM>
 __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
     if (*a.marker == 0u) {
@@ -677,7 +691,10 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
         a.pending[w] = 0u;
     }
     if (threadIdx.x == 0) {
-        if (!overflow) *a.count = total;
+        if (!overflow) {
+            *a.count = total;
+            *a.set_id = next_set_serial();
+        }
         *a.flag = overflow ? MIXQ_FLAG_OVERFLOW : MIXQ_FLAG_FIRED;
         *a.marker = 0u;
         *a.arrive = 0u;
@@ -798,6 +815,7 @@ int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_
     a.rank = reinterpret_cast<int32_t*>(state->work + words);
     a.marker = state->work + 2 * words;
     a.arrive = state->work + 2 * words + 1;
+    a.set_id = state->work + 2 * words + 2;
     a.k_cap = state->k_cap;
     a.words = words;
     a.nchunks = (int32_t)(K / 8);

@@ -72,10 +72,14 @@ extern "C" {
 
 size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits) {
     using namespace mixq;
-    const int S = split_plan(M, N, K, bits, 256);
+    // the plan of the current device (256 compute units on a whole MI355X;
+    // fewer on a partition), or 256 when no gfx950 device is current
+    const int cus = check_device_cached() == MIXQ_OK && device_cu_count() > 0 ? device_cu_count()
+                                                                               : 256;
+    const int S = split_plan(M, N, K, bits, cus);
     if (S > 1) return (size_t)split_workspace_bytes(M, N, S);
     int St = 1;
-    const int n_split = tail_plan(M, N, K, 256, &St);
+    const int n_split = tail_plan(M, N, K, cus, &St);
     if (n_split > 0 && St > 1) return (size_t)tail_workspace_bytes(M, N, n_split, St);
     return 0;
 }
@@ -100,10 +104,11 @@ const char* mixq_status_string(int status) {
         case MIXQ_ERR_INVALID_ARG: return "invalid argument";
         case MIXQ_ERR_UNSUPPORTED_SHAPE:
             return "unsupported shape (K must be a positive multiple of 64 up to 65536; "
-                   "buffers 16-byte aligned)";
+                   "buffers 16-byte aligned; byte offsets within a tile below 2^31)";
         case MIXQ_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
         case MIXQ_ERR_NO_DEVICE: return "no HIP device";
         case MIXQ_ERR_HIP: return "HIP launch error";
+        case MIXQ_ERR_WORKSPACE: return "workspace too small for the split this product takes";
         default: return "unknown status";
     }
 }

@@ -32,7 +32,7 @@
 //   Tile order: consecutive block ids go to different XCDs (round-robin), so
 //   block ids are remapped to give each XCD a compact rectangle of tiles that
 //   share A rows and B rows in its L2.
-#include <stdlib.h>
+#include <atomic>
 
 #include "mixq_internal.h"
 
@@ -67,7 +67,7 @@ struct GemmArgs {
     int32_t ksplit;
     int32_t* sync;  // [tiles] arrival counters, zero between calls
     int32_t* part;  // [tiles][2] int32 partial tiles
-    int32_t out_mode;  // MIXQ_OUT_F32, or MIXQ_OUT_SWIGLU_F16 (Y then holds fp16)
+    int32_t out_mode;  // MIXQ_OUT_F32 / _F16 / _BF16, or MIXQ_OUT_SWIGLU_F16 (16-bit Y)
     // progressive INT4 (null: symmetric per-channel INT4): per row and group
     // of 128 channels, s2 | z << 8
     const uint16_t* gsz;
@@ -103,14 +103,14 @@ __device__ __forceinline__ uint32_t prog_decode4(uint32_t u4, u16x2 s2v, u16x2 c
     return (re | (ro << 8)) ^ 0x80808080u;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // Buffer resource over [base, base + bytes): loads past the end return 0,
 // which covers the ragged last tile rows without clamping.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // s_waitcnt with only the vector-memory counter constrained (<= n, n < 64).
 #define MIXQ_WAIT_VMCNT(n) \
@@ -156,8 +156,9 @@ struct Cfg {
     static_assert(BM % (16 * kNW) == 0 && BN % (32 * kNW) == 0, "loader mismatch");
 };
 
-// STAGES == 2: global -> VGPR -> LDS, double-buffered LDS.
-// STAGES >= 3: global -> LDS directly (buffer_load ... lds), STAGES-deep ring.
+// STAGES == 2: global -> VGPR -> LDS, two 64-byte K tile buffers.
+// STAGES == 4: the K-pair loaders (PF 5 and 6): two pair buffers of 128-byte
+// rows, held as four arrays.
 // Large tiles hold 256 int32 accumulators per lane, so one wave per SIMD is
 // all that fits; saying so lets the scheduler spend registers on overlapping
 // LDS reads with MFMAs instead of saving them for an occupancy it cannot get.
@@ -175,27 +176,27 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, WM, WN>(), waves_per_eu<
 void gemm_kernel(GemmArgs a) {
     using C = Cfg<BM, BN, WM, WN, BITS>;
     static_assert(!PROG || BITS == 4, "progressive groups are INT4");
-    static_assert(STAGES == 2 || BITS == 8, "INT4 weights use the register-staged loader");
-    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+    static_assert(STAGES == 2 || (STAGES == 4 && (PF == 5 || PF == 6)), "loader / stages");
+    static_assert(PF == 1 || PF == 4 || PF == 5 || PF == 6, "loader variant");
     // One array per stage (A tile, then B tile): the compiler then tracks each
     // stage's pending global->LDS transfers separately and waits only for the
     // right ones.
     constexpr int kStageBytes = (BM + BN) * kBK;
     __shared__ __attribute__((aligned(1024))) uint8_t sS0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t sS1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sS2[STAGES > 2 ? kStageBytes : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t sS3[STAGES > 3 ? kStageBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sS2[STAGES == 4 ? kStageBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sS3[STAGES == 4 ? kStageBytes : 16];
     uint8_t* const sA0 = sS0;
     uint8_t* const sA1 = sS1;
     uint8_t* const sB0 = sS0 + BM * kBK;
     uint8_t* const sB1 = sS1 + BM * kBK;
-    uint8_t* const As[4] = {sS0, sS1, sS2, sS3};
-    uint8_t* const Bs[4] = {sS0 + BM * kBK, sS1 + BM * kBK, sS2 + BM * kBK, sS3 + BM * kBK};
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / WN, wn = wave % WN;
+    // size of the outlier set (read once, long before the epilogue needs it)
+    const int count = *a.count;
 
     // ---- block id -> tile, XCD-aware ------------------------------------------
     int bid = blockIdx.x;
@@ -224,6 +225,28 @@ void gemm_kernel(GemmArgs a) {
     const __amdgpu_buffer_rsrc_t rB =
         make_rsrc(static_cast<const uint8_t*>(a.wq) + (int64_t)n0 * wrow_bytes,
                   (int64_t)(BITS == 8 ? rows_b : (rows_b + 31) / 32 * 32) * wrow_bytes);
+
+    // ---- the tile's scales, staged in LDS by transfers issued now -----------------
+    // Every loader waits for its first operand loads before its first LDS
+    // write, which (loads complete in order) covers these earlier transfers,
+    // and the barrier after it makes each wave's share visible; the epilogue
+    // reads them with no wait of its own.  Rows past M or N read zero (buffer
+    // range check); their outputs are never stored.
+    __shared__ __attribute__((aligned(16))) float sx_t[BM];
+    __shared__ __attribute__((aligned(16))) float sw_t[BN];
+    {
+        [[maybe_unused]] const __amdgpu_buffer_rsrc_t rSx = make_rsrc(a.s_x + m0, (int64_t)rows_a * 4);
+        [[maybe_unused]] const __amdgpu_buffer_rsrc_t rSw = make_rsrc(a.s_w + n0, (int64_t)rows_b * 4);
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts exist only in the device pass
+        // one wave instruction stages 64 consecutive scales
+        for (int q = wave; q < BM / kWave; q += C::kNW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSx, (lds_ptr_t)(sx_t + q * kWave), 4,
+                                                     lane * 4, q * kWave * 4, 0, 0);
+        for (int q = wave; q < BN / kWave; q += C::kNW)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSw, (lds_ptr_t)(sw_t + q * kWave), 4,
+                                                     lane * 4, q * kWave * 4, 0, 0);
+#endif
+    }
 
     // ---- per-lane load slots ------------------------------------------------------
     // Wave instruction i fills rows R0..R0+15 (R0 = (i*NW + wave)*16); lane l
@@ -558,19 +581,6 @@ void gemm_kernel(GemmArgs a) {
                 }
             }
         };
-        // B-only staging (used when A fragments come straight from memory)
-        auto bload = [&](int kt, Regs& R) {
-            if constexpr (BITS == 8) {
-#pragma unroll
-                for (int i = 0; i < C::kBI; ++i)
-                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB[i], kt * kBK, 0);
-            } else {
-#pragma unroll
-                for (int i = 0; i < C::kBI4; ++i)
-                    R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, voffB4[i], kt * 1024, 0);
-                gzload(kt, R);
-            }
-        };
         if constexpr (PF == 4) {
             // Cross-tile software pipeline.  Iteration k multiplies tile k from
             // fragments already in registers while it (a) reads tile k+1's
@@ -662,82 +672,6 @@ void gemm_kernel(GemmArgs a) {
                 if (k + 5 < KTs) gload(kb + k + 5, S1);
                 __syncthreads();
             }
-        } else if constexpr (PF == 3) {
-            // A fragments are loaded from global memory directly into the
-            // MFMA operand layout (one tile ahead, two register sets); only B
-            // goes through LDS (two tiles ahead).  This halves the LDS
-            // traffic, which otherwise competes with the MFMAs for issue
-            // slots and LDS bandwidth.  Lane l of fragment i, half ks reads
-            // row wm*WTM + 32*i + l%32, bytes 32*ks + 16*(l/32) of the tile.
-            int voffAd[C::kFM];
-#pragma unroll
-            for (int i = 0; i < C::kFM; ++i) voffAd[i] = (wm * C::kWTM + i * 32 + fr) * K + fh * 16;
-            typedef v4i AFrags[2][C::kFM];
-            auto aload = [&](int kt, AFrags& X) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int i = 0; i < C::kFM; ++i)
-                        X[ks][i] = __builtin_amdgcn_raw_buffer_load_b128(rA, voffAd[i] + ks * 32,
-                                                                         kt * kBK, 0);
-            };
-            auto mma_ra = [&](const AFrags& X, const uint8_t* Bb) {
-                v4i bf[2][C::kFN];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int j = 0; j < C::kFN; ++j)
-                        bf[ks][j] = *reinterpret_cast<const v4i*>(Bb + rdB[ks] + j * 32 * kBK);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int i = 0; i < C::kFM; ++i)
-#pragma unroll
-                        for (int j = 0; j < C::kFN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(X[ks][i], bf[ks][j],
-                                                                              acc[i][j], 0, 0, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, C::kFN, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, C::kFN, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::kFM * C::kFN, 0);
-            };
-            auto bstore = [&](const Regs& R, int buf) {
-                uint8_t* Bb = buf ? sB1 : sB0;
-                if constexpr (BITS == 8) {
-#pragma unroll
-                    for (int i = 0; i < C::kBI; ++i)
-                        *reinterpret_cast<v4i*>(&Bb[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
-                            R.b[i];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < C::kBI4; ++i) {
-                        const int row = (i * C::kNW + wave) * 32 + (lane >> 1);
-                        const int c2 = lane & 1;
-                        v4i lo, hi;
-                        decode4(R, i, lo, hi);
-                        *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2)]) = lo;
-                        *reinterpret_cast<v4i*>(&Bb[lds_off(row, 2 * c2 + 1)]) = hi;
-                    }
-                }
-            };
-            AFrags X0, X1;
-            Regs R0, R1;
-            aload(0, X0);
-            bload(0, R0);
-            bload(1, R1);
-            bstore(R0, 0);
-            __syncthreads();
-            for (int kt = 0; kt < KT; kt += 2) {  // KT even (host checks K % 128 == 0)
-                aload(kt + 1, X1);
-                if (kt + 2 < KT) bload(kt + 2, R0);
-                mma_ra(X0, sB0);
-                bstore(R1, 1);
-                __syncthreads();
-                if (kt + 2 < KT) aload(kt + 2, X0);
-                if (kt + 3 < KT) bload(kt + 3, R1);
-                mma_ra(X1, sB1);
-                if (kt + 2 < KT) bstore(R0, 0);
-                __syncthreads();
-            }
         } else if constexpr (PF == 1) {
             // this block's K tiles kb .. kb + KTs - 1 (a split K range on
             // 128 x 128 tiles; the host keeps each range a whole number of
@@ -755,74 +689,7 @@ void gemm_kernel(GemmArgs a) {
                 if (kt + 1 < KTs) lstore(R, cur ^ 1);
                 __syncthreads();
             }
-        } else {
-            // Tile kt+2 is loaded into the register set tile kt came from;
-            // tile kt+1, loaded an iteration earlier, goes to the other LDS
-            // buffer.  KT is even here (the host checks K % 128 == 0), so the
-            // loop body has no early exit and the accumulators stay put.
-            Regs R0, R1;
-            gload(0, R0);
-            gload(1, R1);
-            lstore(R0, 0);
-            __syncthreads();
-            for (int kt = 0; kt < KT; kt += 2) {
-                if (kt + 2 < KT) gload(kt + 2, R0);
-                mma_tile(sA0, sB0);
-                lstore(R1, 1);
-                __syncthreads();
-                if (kt + 3 < KT) gload(kt + 3, R1);
-                mma_tile(sA1, sB1);
-                if (kt + 2 < KT) lstore(R0, 0);
-                __syncthreads();
-            }
         }
-    } else {
-        // ---- direct global -> LDS, STAGES-deep ring -----------------------------------
-        // Iteration kt: wait until this wave's transfers for tile kt have
-        // landed (those of tiles kt+1 .. kt+STAGES-2 may stay in flight),
-        // barrier (every wave's tile kt has landed, and every wave is done
-        // with tile kt-1), refill the stage tile kt-1 used with tile
-        // kt+STAGES-1, multiply tile kt.  The barrier carries no memory fence,
-        // so the in-flight transfers are not drained.
-        constexpr int kLoads = C::kAI + C::kBI;  // transfers per thread per tile
-        auto issue = [&](int kt, uint8_t* Ab, uint8_t* Bb) {
-#if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts exist only in the device pass
-#pragma unroll
-            for (int i = 0; i < C::kAI; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rA, (lds_ptr_t)(Ab + ((i * C::kNW + wave) * 16) * kBK), 16, voffA[i], kt * kBK,
-                    0, 0);
-#pragma unroll
-            for (int i = 0; i < C::kBI; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rB, (lds_ptr_t)(Bb + ((i * C::kNW + wave) * 16) * kBK), 16, voffB[i], kt * kBK,
-                    0, 0);
-#endif
-        };
-#pragma unroll
-        for (int st = 0; st < STAGES - 1; ++st)
-            if (st < KT) issue(st, As[st], Bs[st]);
-        for (int kt0 = 0; kt0 < KT; kt0 += STAGES) {
-#pragma unroll
-            for (int st = 0; st < STAGES; ++st) {
-                const int kt = kt0 + st;
-                if (kt < KT) {
-                    if (kt + STAGES - 2 < KT) {
-                        if constexpr (STAGES == 4)
-                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoads) : "memory");
-                        else
-                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
-                    } else {
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    }
-                    __builtin_amdgcn_s_barrier();
-                    const int nxt = (st + STAGES - 1) % STAGES;
-                    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, As[nxt], Bs[nxt]);
-                    mma_tile(As[st], Bs[st]);
-                }
-            }
-        }
-        __syncthreads();
     }
 
     if (BM == kSplitTile && a.ksplit > 1) {
@@ -889,17 +756,53 @@ void gemm_kernel(GemmArgs a) {
         }
     }
 
-    // ---- epilogue: dequantize and scale in registers, in place ---------------------
+    // ---- epilogue -------------------------------------------------------------------
     // 32x32 fragment layout: lane l, element e -> row 8*(e/4) + 4*(l/32) + e%4, col l%32.
-    // The tile's scales are staged in LDS so that a lane reads its four
-    // consecutive rows' scales with one 16-byte LDS read.
-    __shared__ __attribute__((aligned(16))) float sx_t[BM];
-    __shared__ __attribute__((aligned(16))) float sw_t[BN];
-    for (int t = tid; t < BM; t += C::kThreads) sx_t[t] = a.s_x[min(m0 + t, a.M - 1)];
-    for (int t = tid; t < BN; t += C::kThreads) sw_t[t] = a.s_w[min(n0 + t, a.N - 1)];
-    __syncthreads();
-    const int count = *a.count;
-    const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+    // (1) The first round of outlier tiles (up to kRC chunks of 32 columns of
+    //     X_out and w_out) starts loading straight into the operand buffers the
+    //     K loop has freed -- one load latency, not one per chunk;
+    // (2) meanwhile the int32 accumulators are dequantized and scaled in place;
+    // (3) per fragment, the f16 outlier MFMAs accumulate onto the scaled tile
+    //     (its fp32 values are their C operand: one accumulator set), and in
+    //     the last round each finished fragment is stored at once, so that its
+    //     stores drain while the next fragment's MFMAs run.
+    constexpr int kRC = STAGES == 4 ? 4 : 2;  // outlier chunks per round (one per stage array)
+    const int nchunks = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN;
+    auto stage = [&](int c) __attribute__((always_inline)) -> uint8_t* { return c == 0 ? sS0 : c == 1 ? sS1 : c == 2 ? sS2 : sS3; };
+    const int ldb = a.ld_out * 2;  // bytes per outlier row
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rXo =
+        make_rsrc(reinterpret_cast<const uint8_t*>(a.X_out) + (int64_t)m0 * ldb,
+                  nchunks > 0 ? (int64_t)rows_a * ldb : 0);
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rWo =
+        make_rsrc(reinterpret_cast<const uint8_t*>(a.w_out) + (int64_t)n0 * ldb,
+                  nchunks > 0 ? (int64_t)rows_b * ldb : 0);
+    // chunk c0 + c of both tiles into stage array c, laid out like a 64-byte
+    // K tile: row r's 16-byte piece p at slot p ^ swz(r)
+    auto load_round = [&](int c0, int nch) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int c = 0; c < kRC; ++c) {
+            if (c < nch) {
+                uint8_t* stg = stage(c);
+#pragma unroll
+                for (int i = 0; i < C::kAI; ++i) {
+                    const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rXo, (lds_ptr_t)(stg + ((i * C::kNW + wave) * 16) * kBK), 16,
+                        row * ldb + (((lane & 3) ^ swz(row)) << 4), (c0 + c) * kBK, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < C::kBI; ++i) {
+                    const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rWo, (lds_ptr_t)(stg + BM * kBK + ((i * C::kNW + wave) * 16) * kBK), 16,
+                        row * ldb + (((lane & 3) ^ swz(row)) << 4), (c0 + c) * kBK, 0, 0);
+                }
+            }
+        }
+#endif
+    };
+    if (nchunks > 0) load_round(0, min(kRC, nchunks));
 
     if constexpr (DEBUG) {
 #pragma unroll
@@ -915,6 +818,7 @@ void gemm_kernel(GemmArgs a) {
                 }
             }
     }
+    // dequantize and scale in place: Y_low = (float(acc) * s_x) * s_w
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i) {
 #pragma unroll
@@ -933,62 +837,59 @@ void gemm_kernel(GemmArgs a) {
         }
     }
 
-    // ---- outlier product: fp16 x fp16 -> fp32, accumulated onto the dequantized tile --
-    if (kpad > 0) {
-        const int ldb = a.ld_out * 2;  // bytes per outlier row
-        const __amdgpu_buffer_rsrc_t rXo =
-            make_rsrc(reinterpret_cast<const uint8_t*>(a.X_out) + (int64_t)m0 * ldb,
-                      (int64_t)rows_a * ldb);
-        const __amdgpu_buffer_rsrc_t rWo =
-            make_rsrc(reinterpret_cast<const uint8_t*>(a.w_out) + (int64_t)n0 * ldb,
-                      (int64_t)rows_b * ldb);
-        for (int kt2 = 0; kt2 < kpad / 32; ++kt2) {
-#pragma unroll
-            for (int i = 0; i < C::kAI; ++i) {
-                const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
-                const int off = row * ldb + (((lane & 3) ^ swz(row)) << 4);
-                *reinterpret_cast<v4i*>(&sA0[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
-                    __builtin_amdgcn_raw_buffer_load_b128(rXo, off, kt2 * kBK, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < C::kBI; ++i) {
-                const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
-                const int off = row * ldb + (((lane & 3) ^ swz(row)) << 4);
-                *reinterpret_cast<v4i*>(&sB0[((i * C::kNW + wave) * 16) * kBK + lane * 16]) =
-                    __builtin_amdgcn_raw_buffer_load_b128(rWo, off, kt2 * kBK, 0);
-            }
-            __syncthreads();
+    // ---- outlier product: fp16 x fp16 -> fp32, accumulated onto the scaled tile -------
+    for (int c0 = 0; c0 < nchunks; c0 += kRC) {
+        const int nch = min(kRC, nchunks - c0);
+        if (c0 > 0) {
+            __syncthreads();  // every wave is done with the previous round's tiles
+            load_round(c0, nch);
+        }
+        MIXQ_WAIT_VMCNT(0);
+        __syncthreads();
+        // one chunk (32 columns) at a time: its B fragments of every column
+        // block and A fragments of every row block in registers, then the
+        // MFMAs with the two 16-column steps outermost, so that 16
+        // independent accumulations separate the two that share a fragment
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            const uint8_t* stg = stage(c);
+            v8h bfr[C::kFN][2], afr[C::kFM][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                v8h af[C::kFM], bf[C::kFN];
-#pragma unroll
-                for (int i = 0; i < C::kFM; ++i)
-                    af[i] = *reinterpret_cast<const v8h*>(&sA0[rdA[ks] + i * 32 * kBK]);
 #pragma unroll
                 for (int j = 0; j < C::kFN; ++j)
-                    bf[j] = *reinterpret_cast<const v8h*>(&sB0[rdB[ks] + j * 32 * kBK]);
+                    bfr[j][ks] = *reinterpret_cast<const v8h*>(stg + BM * kBK + rdB[ks] + j * 32 * kBK);
+#pragma unroll
+                for (int i = 0; i < C::kFM; ++i)
+                    afr[i][ks] = *reinterpret_cast<const v8h*>(stg + rdA[ks] + i * 32 * kBK);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
-                    for (int j = 0; j < C::kFN; ++j) {
-                        v16f yv = __builtin_bit_cast(v16f, acc[i][j]);
-                        yv = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], yv, 0, 0, 0);
-                        acc[i][j] = __builtin_bit_cast(v16i, yv);
-                    }
-            }
-            __syncthreads();
+                    for (int j = 0; j < C::kFN; ++j)
+                        acc[i][j] = __builtin_bit_cast(
+                            v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                      afr[i][ks], bfr[j][ks], __builtin_bit_cast(v16f, acc[i][j]),
+                                      0, 0, 0));
         }
     }
 
-    // ---- SwiGLU output: fp16 silu(gate) * up ------------------------------------------
-    // A gated weight interleaves 32-row blocks of gate and up rows, and every
-    // wave's column range is a multiple of 64, so fragments 2jj and 2jj+1 of a
-    // lane hold gate and up of the same (token, output) pairs.
+    // ---- stores ---------------------------------------------------------------------
+    // Offsets are 32-bit and relative to the tile's first row (the host keeps
+    // 256 rows of Y below 2^31 bytes); rows past M also fall outside the
+    // buffer.  The stores follow the outlier MFMAs in fragment order, so the
+    // first fragments' stores issue while the last MFMAs still run.
+    const int esz = a.out_mode == MIXQ_OUT_F32 ? 4 : 2;  // bytes per Y element
+    const int ldyb = (int)a.ldy * esz;
+    const __amdgpu_buffer_rsrc_t rY = make_rsrc(reinterpret_cast<const uint8_t*>(a.Y) +
+                                                    (int64_t)m0 * a.ldy * esz,
+                                                (int64_t)rows_a * a.ldy * esz);
     if (a.out_mode == MIXQ_OUT_SWIGLU_F16) {
-        const int ldyh = (int)a.ldy * 2;  // bytes per fp16 row
-        const __amdgpu_buffer_rsrc_t rH =
-            make_rsrc(reinterpret_cast<const uint8_t*>(a.Y) + (int64_t)m0 * ldyh,
-                      (int64_t)rows_a * ldyh);
+        // A gated weight interleaves 32-row blocks of gate and up rows, and
+        // every wave's column range is a multiple of 64, so fragments 2jj and
+        // 2jj+1 of a lane hold gate and up of the same (token, output) pairs.
 #pragma unroll
         for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
@@ -1005,20 +906,29 @@ void gemm_kernel(GemmArgs a) {
                         const float y = g / (1.0f + __expf(-g)) * u;
                         if (rl < rows_a)
                             __builtin_amdgcn_raw_buffer_store_b16(
-                                __builtin_bit_cast(unsigned short, (_Float16)y), rH,
-                                rl * ldyh + oc * 2, 0, 0);
+                                __builtin_bit_cast(unsigned short, (_Float16)y), rY,
+                                rl * ldyb + oc * 2, 0, 0);
                     }
                 }
             }
         return;
     }
-
-    // ---- store Y (fp32) ---------------------------------------------------------------
-    // Buffer stores relative to the tile's first row: 32-bit offsets, and rows
-    // past M fall outside the buffer as well as failing the explicit check.
-    const __amdgpu_buffer_rsrc_t rY =
-        make_rsrc(a.Y + (int64_t)m0 * a.ldy, (int64_t)rows_a * a.ldy * 4);
-    const int ldy4 = (int)a.ldy * 4;
+    if (!ROWS && a.out_mode == MIXQ_OUT_F32 && rows_a == BM && n0 + BN <= a.N) {
+        // a whole tile: no per-element test; the lane's column and half in the
+        // vector offset, the row (the same for the whole wave) in the scalar one
+        const int voff = 4 * fh * ldyb + (n0 + wn * C::kWTN + fr) * 4;
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        acc[i][j][e], rY, voff + j * 128,
+                        (wm * C::kWTM + i * 32 + 8 * (e >> 2) + (e & 3)) * ldyb, 0);
+        return;
+    }
+    const bool bf16 = a.out_mode == MIXQ_OUT_BF16;
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
@@ -1036,9 +946,21 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int rl = r0 + 8 * (e >> 2) + (e & 3);
-                    if (rl < rows_a)
-                        __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][e], rY, rl * ldy4 + ycol * 4,
-                                                              0, 0);
+                    if (rl < rows_a) {
+                        if (esz == 4) {
+                            __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][e], rY,
+                                                                  rl * ldyb + ycol * 4, 0, 0);
+                        } else {
+                            // 16-bit output: round to nearest, ties to even
+                            const float y = __int_as_float(acc[i][j][e]);
+                            const uint32_t u = __float_as_uint(y);
+                            const unsigned short h =
+                                bf16 ? (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16)
+                                     : __builtin_bit_cast(unsigned short, (_Float16)y);
+                            __builtin_amdgcn_raw_buffer_store_b16(h, rY, rl * ldyb + ycol * 2, 0,
+                                                                  0);
+                        }
+                    }
                 }
             }
         }
@@ -1059,42 +981,30 @@ int launch_cfg(GemmArgs a, bool debug, hipStream_t st) {
     return launch_status();
 }
 
-// Tile configurations; MIXQ_GEMM_TILE=<id> forces one (0 = automatic).
+// Kernel variants (ids of mixq_set_gemm_variant; 0 = automatic choice).
 enum {
     kCfgAuto = 0,
-    kCfg256x256 = 1,   // 4 waves of 128x128, register-staged
-    kCfg128x128 = 2,   // 4 waves of 64x64, register-staged
-    kCfg256x256D = 3,  // 4 waves of 128x128, direct-to-LDS, 3 stages
-    kCfg256x128 = 4,   // 4 waves of 128x64, register-staged
-    kCfg256x256D4 = 5, // 4 waves of 128x128, direct-to-LDS, 4 stages
-    kCfg256x256P2 = 6, // 4 waves of 128x128, register-staged, loads two tiles ahead
-    kCfg256x128P2 = 7, // 4 waves of 128x64, register-staged, loads two tiles ahead
-    kCfg256x256AD = 8, // 4 waves of 128x128, A fragments from global, B via LDS
-    kCfg256x128AD = 9, // 4 waves of 128x64, A fragments from global, B via LDS
-    kCfg256x256SP = 10,  // 4 waves of 128x128, cross-tile software pipeline
-    kCfg256x128SP = 11,  // 4 waves of 128x64, cross-tile software pipeline
-    kCfg256x256KP = 12,  // 4 waves of 128x128, 128-byte K pairs (whole-line loads)
-    kCfg256x256KS = 13,  // as 12, issue order pinned slot by slot
-    kCfg128x128KP = 14,  // 4 waves of 64x64, 128-byte K pairs
-    kCfg128x128SP = 15,  // 4 waves of 64x64, cross-tile software pipeline (INT4 weights)
+    kCfg256x256 = 1,    // 4 waves of 128x128, 64-byte K steps, register-staged (any K)
+    kCfg128x128 = 2,    // 4 waves of 64x64, 64-byte K steps, register-staged (any K)
+    kCfg256x256SP = 3,  // 4 waves of 128x128, cross-tile software pipeline (INT4 weights)
+    kCfg256x256KS = 4,  // 4 waves of 128x128, 128-byte K pairs, issue order pinned (INT8)
+    kCfg128x128KP = 5,  // 4 waves of 64x64, 128-byte K pairs (INT8; split K for thin products)
+    kCfg128x128SP = 6,  // 4 waves of 64x64, cross-tile software pipeline (INT4 weights)
+    kCfgCount = 7,
 };
 
-int forced_cfg() {
-    const char* e = getenv("MIXQ_GEMM_TILE");
-    return e ? atoi(e) : 0;
-}
+std::atomic<int> g_forced_variant{0};
 
 int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
-    const int f = forced_cfg();
-    if ((f == kCfg256x256P2 || f == kCfg256x128P2 || f == kCfg256x256AD || f == kCfg256x128AD ||
-         f == kCfg256x256SP || f == kCfg256x128SP || f == kCfg256x256KP ||
-         f == kCfg256x256KS || f == kCfg128x128KP || f == kCfg128x128SP) &&
-        K % 128 != 0)
-        return kCfg128x128;
-    if (f == kCfg128x128SP && bits == 8) return kCfg128x128KP;
-    if ((f == kCfg256x256KP || f == kCfg256x256KS) && bits == 4) return kCfg256x256SP;
-    if (f == kCfg128x128KP && bits == 4) return kCfg128x128;
-    if (f >= 1 && f <= 15 && !(bits == 4 && (f == kCfg256x256D || f == kCfg256x256D4))) return f;
+    const int f = g_forced_variant.load(std::memory_order_relaxed);
+    if (f != kCfgAuto) {
+        // a forced variant falls back where its loader does not apply
+        if (f >= kCfg256x256SP && K % 128 != 0) return kCfg128x128;
+        if (f == kCfg128x128SP && bits == 8) return kCfg128x128KP;
+        if (f == kCfg256x256KS && bits == 4) return kCfg256x256SP;
+        if (f == kCfg128x128KP && bits == 4) return kCfg128x128;
+        return f;
+    }
     // Large 256x256 tiles (software-pipelined when K allows) once they give
     // about one tile per CU; 128x128 tiles (K pairs for INT8 weights) for
     // thinner products.
@@ -1108,29 +1018,13 @@ int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
 
 template <bool ROWS = false>
 int launch_w8(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
-    if constexpr (ROWS) {
-        // row subsets: the configurations their shapes are given
-        switch (cfg) {
-            case kCfg256x256KS: return launch_cfg<256, 256, 2, 2, 8, 4, 6, false, true>(a, debug, st);
-            case kCfg128x128KP: return launch_cfg<128, 128, 2, 2, 8, 4, 5, false, true>(a, debug, st);
-            default: return launch_cfg<128, 128, 2, 2, 8, 2, 1, false, true>(a, debug, st);
-        }
-    }
     switch (cfg) {
-        case kCfg256x256: return launch_cfg<256, 256, 2, 2, 8, 2>(a, debug, st);
-        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 8, 2>(a, debug, st);
-        case kCfg256x256D: return launch_cfg<256, 256, 2, 2, 8, 3>(a, debug, st);
-        case kCfg256x256D4: return launch_cfg<256, 256, 2, 2, 8, 4>(a, debug, st);
-        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 8, 2, 2>(a, debug, st);
-        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 8, 2, 2>(a, debug, st);
-        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 8, 2, 3>(a, debug, st);
-        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 8, 2, 3>(a, debug, st);
-        case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 8, 2, 4>(a, debug, st);
-        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 8, 2, 4>(a, debug, st);
-        case kCfg256x256KP: return launch_cfg<256, 256, 2, 2, 8, 4, 5>(a, debug, st);
-        case kCfg256x256KS: return launch_cfg<256, 256, 2, 2, 8, 4, 6>(a, debug, st);
-        case kCfg128x128KP: return launch_cfg<128, 128, 2, 2, 8, 4, 5>(a, debug, st);
-        default: return launch_cfg<128, 128, 2, 2, 8, 2>(a, debug, st);
+        case kCfg256x256KS: return launch_cfg<256, 256, 2, 2, 8, 4, 6, false, ROWS>(a, debug, st);
+        case kCfg128x128KP: return launch_cfg<128, 128, 2, 2, 8, 4, 5, false, ROWS>(a, debug, st);
+        case kCfg256x256:
+            if constexpr (!ROWS) return launch_cfg<256, 256, 2, 2, 8, 2>(a, debug, st);
+            [[fallthrough]];
+        default: return launch_cfg<128, 128, 2, 2, 8, 2, 1, false, ROWS>(a, debug, st);
     }
 }
 
@@ -1138,13 +1032,7 @@ template <bool PROG, bool ROWS = false>
 int launch_w4_t(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
     switch (cfg) {
         case kCfg256x256: return launch_cfg<256, 256, 2, 2, 4, 2, 1, PROG, ROWS>(a, debug, st);
-        case kCfg256x128: return launch_cfg<256, 128, 2, 2, 4, 2, 1, PROG, ROWS>(a, debug, st);
-        case kCfg256x256P2: return launch_cfg<256, 256, 2, 2, 4, 2, 2, PROG, ROWS>(a, debug, st);
-        case kCfg256x128P2: return launch_cfg<256, 128, 2, 2, 4, 2, 2, PROG, ROWS>(a, debug, st);
-        case kCfg256x256AD: return launch_cfg<256, 256, 2, 2, 4, 2, 3, PROG, ROWS>(a, debug, st);
-        case kCfg256x128AD: return launch_cfg<256, 128, 2, 2, 4, 2, 3, PROG, ROWS>(a, debug, st);
         case kCfg256x256SP: return launch_cfg<256, 256, 2, 2, 4, 2, 4, PROG, ROWS>(a, debug, st);
-        case kCfg256x128SP: return launch_cfg<256, 128, 2, 2, 4, 2, 4, PROG, ROWS>(a, debug, st);
         case kCfg128x128SP: return launch_cfg<128, 128, 2, 2, 4, 2, 4, PROG, ROWS>(a, debug, st);
         default: return launch_cfg<128, 128, 2, 2, 4, 2, 1, PROG, ROWS>(a, debug, st);
     }
@@ -1173,7 +1061,9 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
               int32_t out_mode = MIXQ_OUT_F32) {
     if (!Xq || !s_x || !state || !w || !Y) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !w->wq || !w->s_w) return MIXQ_ERR_INVALID_ARG;
-    if (out_mode != MIXQ_OUT_F32 && out_mode != MIXQ_OUT_SWIGLU_F16) return MIXQ_ERR_INVALID_ARG;
+    if (out_mode != MIXQ_OUT_F32 && out_mode != MIXQ_OUT_SWIGLU_F16 && out_mode != MIXQ_OUT_F16 &&
+        out_mode != MIXQ_OUT_BF16)
+        return MIXQ_ERR_INVALID_ARG;
     if (out_mode == MIXQ_OUT_SWIGLU_F16 && (w->gated != 1 || w->N % 64 != 0))
         return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || w->bits != 4 || !w->gsz))
@@ -1187,7 +1077,7 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
                     (w->bits == 4 && w->group == 0)))
         return MIXQ_ERR_INVALID_ARG;
     // Y columns: N, N / 2 for SwiGLU, n_out for a row subset
-    const int64_t ny = w->rmap ? w->n_out : out_mode == MIXQ_OUT_F32 ? w->N : w->N / 2;
+    const int64_t ny = w->rmap ? w->n_out : out_mode == MIXQ_OUT_SWIGLU_F16 ? w->N / 2 : w->N;
     if (M <= 0 || w->N <= 0 || w->K <= 0 || ldy < ny) return MIXQ_ERR_INVALID_ARG;
     if (w->bits != 8 && w->bits != 4) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap < 0 || state->k_cap > w->K || w->k_cap != state->k_cap)
@@ -1195,6 +1085,12 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     if (state->k_cap > 0 && (!X_out || !w->w_out)) return MIXQ_ERR_INVALID_ARG;
     if (!valid_k(w->K)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (M > (1 << 30) || w->N > (1 << 30)) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    // Y stores use 32-bit byte offsets from the tile's first row (256 rows at
+    // most); the grid is one dimension (128 x 128 tiles, K split up to 4 ways)
+    if (ldy * (out_mode == MIXQ_OUT_F32 ? 4 : 2) * 256 > (int64_t)0x7FFFFFFF)
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    if (((M + 127) / 128) * ((w->N + 127) / 128) * 4 > (int64_t)0x7FFFFFFF)
+        return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (((uintptr_t)Xq & 15u) || ((uintptr_t)w->wq & 15u) || ((uintptr_t)X_out & 15u) ||
         ((uintptr_t)w->w_out & 15u) || ((uintptr_t)ws & 15u))
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
@@ -1229,12 +1125,13 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.n_out = w->rmap ? w->n_out : 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-    const int f = forced_cfg();
+    const int f = g_forced_variant.load(std::memory_order_relaxed);
     const int pc = pick_cfg(M, w->N, w->K, w->bits);
     const int S = ws && (f == kCfgAuto || f == kCfg128x128KP) && pc == kCfg128x128KP
                       ? split_plan(M, w->N, w->K, w->bits, device_cu_count())
                       : 1;
-    if (S > 1 && (int64_t)ws_bytes >= split_workspace_bytes(M, w->N, S)) {
+    if (S > 1 && (int64_t)ws_bytes < split_workspace_bytes(M, w->N, S)) return MIXQ_ERR_WORKSPACE;
+    if (S > 1) {
         a.ksplit = S;
         a.sync = static_cast<int32_t*>(ws);
         a.part = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + kSplitSyncBytes);
@@ -1259,7 +1156,9 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
         GemmArgs a2 = a;
         a.n_end = n_split;
         a2.n_begin = n_split;
-        if (St > 1 && ws && (int64_t)ws_bytes >= tail_workspace_bytes(M, w->N, n_split, St)) {
+        if (St > 1 && ws && (int64_t)ws_bytes < tail_workspace_bytes(M, w->N, n_split, St))
+            return MIXQ_ERR_WORKSPACE;
+        if (St > 1 && ws) {
             a2.ksplit = St;
             a2.sync = static_cast<int32_t*>(ws);
             a2.part = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + kSplitSyncBytes);
@@ -1273,6 +1172,12 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
 
 }  // namespace
 }  // namespace mixq
+
+extern "C" int mixq_set_gemm_variant(int32_t variant) {
+    if (variant < 0 || variant >= mixq::kCfgCount) return MIXQ_ERR_INVALID_ARG;
+    mixq::g_forced_variant.store(variant, std::memory_order_relaxed);
+    return MIXQ_OK;
+}
 
 extern "C" int mixq_gemm(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
                          const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,

@@ -169,20 +169,23 @@ __global__ __launch_bounds__(kThreads) void quantize_weight_kernel(const uint16_
 
 // w_out[n, j] = W[n, idx[j]] for j < count, zeros up to the padded width.
 // Block b owns rows b, b + G, b + 2G, ... (G = gridDim.x, fixed for a given N)
-// and slot k_out[b], the set size its rows were last gathered for: it runs
-// when forced or when that differs from the state's count.  No block reads
-// another block's slot, so the check needs no atomics.
+// and slot k_out[b], the serial of the set its rows were last gathered for
+// (the state's work area holds the serial of its committed set, unique per
+// commit): it runs when forced or when that differs from the state's serial.
+// No block reads another block's slot, so the check needs no atomics.
 __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* __restrict__ W,
                                                                int64_t N, int32_t K,
                                                                const int32_t* __restrict__ idx,
                                                                const int32_t* __restrict__ count_p,
+                                                               const uint32_t* __restrict__ set_id_p,
                                                                uint16_t* __restrict__ w_out,
                                                                int32_t ld_out, int32_t* k_out,
                                                                int force, int gated,
                                                                const int32_t* __restrict__ rmap,
                                                                int64_t n_out) {
     const int count = *count_p;
-    if (!force && k_out[blockIdx.x] == count) return;
+    const int32_t set_id = (int32_t)*set_id_p;
+    if (!force && k_out[blockIdx.x] == set_id) return;
     const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
     const int64_t G = gridDim.x;
     const int64_t my_rows = (N - blockIdx.x + G - 1) / G;
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void gather_cols_kernel(const uint16_t* _
         w_out[n * ld_out + j] = (live && j < count) ? W[srow * (int64_t)K + idx[j]] : (uint16_t)0;
     }
     __syncthreads();
-    if (threadIdx.x == 0) k_out[blockIdx.x] = count;
+    if (threadIdx.x == 0) k_out[blockIdx.x] = set_id;
 }
 
 template <int CPT>
@@ -234,7 +237,7 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     if (!w->wq || !w->s_w || !w->k_out) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap < 0 || state->k_cap > K) return MIXQ_ERR_INVALID_ARG;
     if (state->k_cap > 0 && (!w->w_out || !state->idx)) return MIXQ_ERR_INVALID_ARG;
-    if (!state->count) return MIXQ_ERR_INVALID_ARG;
+    if (!state->count || !state->work) return MIXQ_ERR_INVALID_ARG;
     if (w->gated != 0 && w->gated != 1) return MIXQ_ERR_INVALID_ARG;
     if (w->group != 0 && (w->group != MIXQ_PROGRESSIVE_GROUP || bits != 4 || !w->gsz))
         return MIXQ_ERR_INVALID_ARG;
@@ -264,7 +267,8 @@ extern "C" int mixq_pack_weight(const uint16_t* W, int64_t N, int64_t K, int32_t
     const int ld_out = (int)outlier_ld(state->k_cap);
     const int grid = (int)(N < MIXQ_GATHER_SLOTS ? N : MIXQ_GATHER_SLOTS);
     hipLaunchKernelGGL(gather_cols_kernel, dim3(grid), dim3(kThreads), 0, st, W, N, (int32_t)K,
-                       state->idx, state->count, w->w_out, ld_out, w->k_out,
+                       state->idx, state->count, state->work + 2 * bitmap_words(K) + 2,
+                       w->w_out, ld_out, w->k_out,
                        mode == MIXQ_PACK_FULL ? 1 : 0, w->gated, w->rmap,
                        (int64_t)w->n_out);
     return launch_status();

@@ -19,13 +19,16 @@ LIB_PATH = os.path.join(_PKG, "libmixq.so")
 
 MIXQ_OK = 0
 STATUS = {0: "MIXQ_OK", 1: "MIXQ_ERR_INVALID_ARG", 2: "MIXQ_ERR_UNSUPPORTED_SHAPE",
-          3: "MIXQ_ERR_UNSUPPORTED_DEVICE", 4: "MIXQ_ERR_NO_DEVICE", 5: "MIXQ_ERR_HIP"}
+          3: "MIXQ_ERR_UNSUPPORTED_DEVICE", 4: "MIXQ_ERR_NO_DEVICE", 5: "MIXQ_ERR_HIP",
+          6: "MIXQ_ERR_WORKSPACE"}
 FLAG_FIRED = 1
 FLAG_OVERFLOW = 2
 PACK_FULL = 0
 PACK_OUTLIER_COLS = 1
 OUT_F32 = 0
 OUT_SWIGLU_F16 = 1
+OUT_F16 = 2
+OUT_BF16 = 3
 PROGRESSIVE_GROUP = 128
 OUTLIER_ALIGN = 32
 K_MULTIPLE = 64
@@ -102,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.mixq_check_device.restype = ctypes.c_int
         L.mixq_version.argtypes = []
         L.mixq_version.restype = ctypes.c_int
+        L.mixq_set_gemm_variant.argtypes = [I32]
+        L.mixq_set_gemm_variant.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -117,6 +122,18 @@ def _ptr(t: torch.Tensor | None):
 
 def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# GEMM kernel variants (ids of mixq_set_gemm_variant; testing hook)
+GEMM_VARIANTS = {"auto": 0, "256x256": 1, "128x128": 2, "256x256_swp": 3, "256x256_kpair": 4,
+                 "128x128_kpair": 5, "128x128_swp": 6}
+
+
+def set_gemm_variant(variant: int | str) -> None:
+    """Force one GEMM kernel variant for every later call (0 / "auto" =
+    the automatic choice); for tests that cover each variant."""
+    v = GEMM_VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    _check("mixq_set_gemm_variant", lib().mixq_set_gemm_variant(v))
 
 
 def outlier_ld(k_cap: int) -> int:
@@ -313,8 +330,9 @@ def gemm(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None, state:
 def gemm_ex(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None,
             state: OutlierState, pw: PackedWeight, Y: torch.Tensor, out_mode: int,
             acc_debug: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> None:
-    """mixq_gemm_ex: OUT_F32 (Y fp32 [M, >= N]) or OUT_SWIGLU_F16 (a gated
-    weight; Y fp16 [M, >= N/2] = silu(gate) * up)."""
+    """mixq_gemm_ex: OUT_F32 (Y fp32 [M, >= N]), OUT_F16 / OUT_BF16 (Y fp16 /
+    bf16 [M, >= N], the fp32 output rounded to nearest even) or
+    OUT_SWIGLU_F16 (a gated weight; Y fp16 [M, >= N/2] = silu(gate) * up)."""
     M = Xq.shape[0]
     st = state.c()
     w = pw.c()

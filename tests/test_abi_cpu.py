@@ -175,6 +175,52 @@ def test_gemm_validation(args, code):
     assert rc == code
 
 
+def _gemm(**args):
+    w = args.get("w", _weight())
+    st = _state()
+    return mixq.lib().mixq_gemm(ctypes.c_void_p(args.get("Xq", 0x20000)), ctypes.c_void_p(0x30000),
+                                ctypes.c_void_p(args.get("xo", 0x40000)), ctypes.byref(st),
+                                ctypes.byref(w), args.get("M", 4),
+                                ctypes.c_void_p(args.get("Y", 0x50000)), args.get("ldy", 16), None,
+                                None)
+
+
+def test_gemm_32bit_offsets():
+    """Y stores take 32-bit byte offsets within a tile of at most 256 rows,
+    and the grid is one dimension: sizes beyond either are refused before
+    anything is launched (FP6 explainer, section 2.3: unsupported shapes get
+    an explicit error)."""
+    import torch
+    assert _gemm(ldy=1 << 21) == 2                       # 256 rows x ldy x 4 B = 2^31
+    assert _gemm(ldy=(1 << 21) + 12345) == 2
+    # a row subset with 2^30 packed rows and 2^30 tokens: 2^46 blocks
+    big = _weight(N=1 << 30, n_out=16, rmap=0x600000)
+    assert _gemm(w=big, M=1 << 30, ldy=16) == 2
+    # the SwiGLU output is 2 bytes per element: twice the columns fit
+    L = mixq.lib()
+    gw = _weight(N=64, gated=1)
+    st = _state()
+    rc = L.mixq_gemm_ex(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+                        ctypes.byref(st), ctypes.byref(gw), 4, ctypes.c_void_p(0x50000), 1 << 22,
+                        mixq.OUT_SWIGLU_F16, None, None, 0, None)
+    assert rc == 2
+    if not torch.cuda.is_available():
+        assert _gemm(ldy=(1 << 21) - 1) == 4             # the largest row stride that fits
+        rc = L.mixq_gemm_ex(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000),
+                            ctypes.c_void_p(0x40000), ctypes.byref(st), ctypes.byref(gw), 4,
+                            ctypes.c_void_p(0x50000), (1 << 22) - 1, mixq.OUT_SWIGLU_F16, None,
+                            None, 0, None)
+        assert rc == 4
+
+
+def test_status_strings():
+    L = mixq.lib()
+    for code, name in mixq.STATUS.items():
+        text = L.mixq_status_string(code).decode()
+        assert text and text != "unknown status", name
+    assert L.mixq_status_string(99).decode() == "unknown status"
+
+
 def test_gemm_workspace_bytes():
     """Split-K plan (256 compute units): only thin INT8 products with K a
     multiple of 256; 4 KiB of counters plus two 64 KiB partial tiles per

@@ -273,6 +273,25 @@ def test_split_k(orc, M, K, N, n_out):
     assert int(g.ws[:1024].abs().sum().cpu()) == 0, "tile counters not cleared"
 
 
+def test_undersized_workspace_is_refused(orc):
+    """A workspace that is given but smaller than the split needs is an
+    explicit error (MIXQ_ERR_WORKSPACE) and enqueues nothing: Y keeps its
+    contents."""
+    M, K, N = 64, 4096, 1024
+    need = mixq.gemm_workspace_bytes(M, N, K, 8)
+    assert need > 4096
+    X, W, _ = workloads.random_case(seed=5, M=M, K=K, N=N, n_out=2)
+    g = GpuLayer(W, 8, 6.0, 64, M)
+    g.quantize(X)
+    g.regather()
+    small = torch.zeros((need - 16) // 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(mixq.MixqError) as e:
+        mixq.gemm(g.Xq, g.s_x, g.X_out, g.state, g.pw, g.Y, None, small)
+    assert e.value.code == 6
+    torch.cuda.synchronize()
+    assert torch.isnan(g.Y).all(), "a refused call wrote Y"
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M", [1, 7, 16])
 def test_few_tokens_full_weight(orc, M, bits):

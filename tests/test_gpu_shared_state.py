@@ -71,3 +71,53 @@ def test_one_state_three_weights(orc):
             say(f"[shared] step {step} N={n} bits={bits} group={group} count={r.count} "
                 f"max|dY|/max|Y|={err:.2e}")
     assert r.count == 6
+
+
+def _planted(seed, M, K, chans):
+    """N(0,1) tokens (clipped below the threshold) with the given channels
+    planted at U(20, 100) * sign: exactly those channels exceed tau."""
+    r = np.random.default_rng(seed)
+    X = np.clip(r.standard_normal((M, K)), -4, 4).astype(np.float32)
+    X[:, chans] = r.uniform(20, 100, (M, len(chans))) * np.where(r.random((M, len(chans))) < .5, -1, 1)
+    return X.astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("how", ["reset", "second_state"])
+def test_same_size_set_regathers(orc, bits, how):
+    """A weight whose outlier columns were gathered for one set, then used
+    with a set of the same size but other channels -- after the state is
+    reset, or through a second state -- must re-gather them (MixQ article,
+    Fig. 11: the outlier columns are those of the current set, in order).
+    Y and the int32 accumulators against the oracle for both sets."""
+    M, K, N, k_cap = 96, 1024, 320, 32
+    ld = mixq.outlier_ld(k_cap)
+    set_a = [5, 77, 300, 901]
+    set_b = [6, 78, 301, 902]  # same size, other channels
+    XA, XB = _planted(31, M, K, set_a), _planted(32, M, K, set_b)
+    W = (np.random.default_rng(33).standard_normal((N, K)) * 0.05).astype(np.float16)
+    Wd = to_dev(W)
+    q, s = orc.quantize_weight(W, bits)
+    pw = mixq.PackedWeight.create(N, K, bits, k_cap)
+    st_a = mixq.OutlierState.create(K, k_cap)
+    st_b = st_a if how == "reset" else mixq.OutlierState.create(K, k_cap)
+    mixq.pack_weight(Wd, st_a, pw, mixq.PACK_FULL)
+    Xq = torch.empty(M, K, dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    Xo = torch.zeros(M * ld, dtype=torch.float16, device="cuda")
+    for X, st, chans in ((XA, st_a, set_a), (XB, st_b, set_b)):
+        if st is st_a and X is XB:
+            st.reset()
+        mixq.quantize_act(to_dev(X), 6.0, st, Xq, sx, Xo)
+        mixq.pack_weight(Wd, st, pw, mixq.PACK_OUTLIER_COLS)
+        Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        dbg = torch.zeros(M, N, dtype=torch.int32, device="cuda")
+        mixq.gemm(Xq, sx, Xo, st, pw, Y, dbg, None)
+        torch.cuda.synchronize()
+        r = OracleLayer(W=W, bits=bits, tau=6.0, k_cap=k_cap, ldo=ld, oracle=orc).step(X)
+        assert r.idx.tolist() == chans and int(st.count.cpu()[0]) == len(chans)
+        wo = pw.w_out_view().cpu().numpy().view(np.uint16)
+        assert np.array_equal(wo, orc.gather_weight_cols(W, r.in_set, ld)), how
+        assert np.array_equal(dbg.cpu().numpy(), r.acc)
+        err = check_y(Y.cpu().numpy(), r.Y)
+        say(f"[regather] {how} bits={bits} set={chans} max|dY|/max|Y|={err:.2e}")
