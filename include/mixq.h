@@ -407,6 +407,34 @@ int mixq_gemm_ex(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
                  int64_t ldy, int32_t out_mode, int32_t *acc_debug, void *ws, size_t ws_bytes,
                  void *stream);
 
+/*
+ * mixq_gemm_noalloc -- mixq_gemm_ex with no workspace argument and no
+ * allocation of any kind, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The split-K workspace that mixq_gemm_ex takes from the caller
+ * is a file-scope device array of the library instead, of
+ * mixq_gemm_scratch_bytes() bytes: 4096 bytes of tile counters and 512
+ * partial tiles of 64 KiB (32 MiB + 4 KiB), which covers every split the
+ * library plans on a 256-CU MI355X (at most two partials per compute unit).
+ * Every GPU the library runs on holds its own copy until the process ends.
+ * The first call on a device takes the array's address
+ * (hipGetSymbolAddress) and clears its counters with a fill kernel on
+ * `stream`; later calls launch only the GEMM.  Calls on one device share
+ * the array: two of them that overlap in time (different streams without
+ * ordering) race and give wrong results -- order them.
+ *
+ *   Arguments: as mixq_gemm_ex without ws / ws_bytes.
+ * Errors: as mixq_gemm_ex; MIXQ_ERR_WORKSPACE if a product's split needed
+ *         more than the array holds (not reachable on a 256-CU device);
+ *         MIXQ_ERR_HIP if the array's address cannot be taken.
+ */
+int mixq_gemm_noalloc(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
+                      const mixq_act_state *state, const mixq_weight *w, int64_t M, void *Y,
+                      int64_t ldy, int32_t out_mode, int32_t *acc_debug, void *stream);
+
+/* Bytes of the device array mixq_gemm_noalloc uses in place of ws. */
+size_t mixq_gemm_scratch_bytes(void);
+
 /* Workspace bytes mixq_gemm_ws needs to split this product on a device with
  * 256 compute units (MI355X): 4096 bytes of tile counters plus, per split
  * 128 x 128 output tile, one 64 KiB partial tile per part (two for a thin

@@ -33,6 +33,7 @@
 //   block ids are remapped to give each XCD a compact rectangle of tiles that
 //   share A rows and B rows in its L2.
 #include <atomic>
+#include <mutex>
 
 #include "mixq_internal.h"
 
@@ -1055,10 +1056,56 @@ int launch_bits(const GemmArgs& a, int cfg, bool debug, hipStream_t st) {
 namespace mixq {
 namespace {
 
+// ---- the GEMM with the library's own split-K workspace -----------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops): the split-K workspace of mixq_gemm_ex lives in a
+// file-scope device array instead of caller memory.  Each device that runs
+// the library holds its own copy for the life of the process; its address
+// is taken once per device with hipGetSymbolAddress (the array's name is
+// only a host-side handle) and kept.  The tile counters at its start must
+// be zero before a call; every completed call leaves them zero, and the
+// first call on a device clears them with a fill kernel on its stream.
+
+constexpr size_t kScratchBytes = (size_t)kSplitSyncBytes + 512 * (size_t)kSplitSlotBytes;
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Device address of this device's scratch array (cleared on first use), or
+// null on a HIP error.
+void* scratch_ptr(hipStream_t st) {
+    static std::mutex mu;
+    static void* ptr[64];
+    static bool ready[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ready[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        hipLaunchKernelGGL(clear_words_kernel, dim3(4), dim3(256), 0, st, static_cast<uint32_t*>(p),
+                           (int)(kSplitSyncBytes / 4));
+        if (hipGetLastError() != hipSuccess) return nullptr;
+        ptr[dev] = p;
+        ready[dev] = true;
+    }
+    return ptr[dev];
+}
+
+
 int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
               const mixq_act_state* state, const mixq_weight* w, int64_t M, float* Y,
               int64_t ldy, int32_t* acc_debug, void* ws, size_t ws_bytes, void* stream,
-              int32_t out_mode = MIXQ_OUT_F32) {
+              int32_t out_mode = MIXQ_OUT_F32, bool own_ws = false) {
     if (!Xq || !s_x || !state || !w || !Y) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !w->wq || !w->s_w) return MIXQ_ERR_INVALID_ARG;
     if (out_mode != MIXQ_OUT_F32 && out_mode != MIXQ_OUT_SWIGLU_F16 && out_mode != MIXQ_OUT_F16 &&
@@ -1127,6 +1174,22 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
 
     const int f = g_forced_variant.load(std::memory_order_relaxed);
     const int pc = pick_cfg(M, w->N, w->K, w->bits);
+    if (own_ws) {
+        // the library's scratch array stands in for ws, set up only when the
+        // plan below splits K (the same conditions)
+        ws = nullptr;
+        ws_bytes = 0;
+        int St0 = 1;
+        const bool split = (f == kCfgAuto || f == kCfg128x128KP) && pc == kCfg128x128KP &&
+                           split_plan(M, w->N, w->K, w->bits, device_cu_count()) > 1;
+        const bool tail = f == kCfgAuto && (pc == kCfg256x256KS || pc == kCfg256x256SP) &&
+                          tail_plan(M, w->N, w->K, device_cu_count(), &St0) > 0 && St0 > 1;
+        if (split || tail) {
+            ws = scratch_ptr(st);
+            if (!ws) return MIXQ_ERR_HIP;
+            ws_bytes = kScratchBytes;
+        }
+    }
     const int S = ws && (f == kCfgAuto || f == kCfg128x128KP) && pc == kCfg128x128KP
                       ? split_plan(M, w->N, w->K, w->bits, device_cu_count())
                       : 1;
@@ -1198,4 +1261,14 @@ extern "C" int mixq_gemm_ex(const int8_t* Xq, const float* s_x, const uint16_t* 
                             size_t ws_bytes, void* stream) {
     return mixq::gemm_impl(Xq, s_x, X_out, state, w, M, static_cast<float*>(Y), ldy, acc_debug,
                            ws, ws_bytes, stream, out_mode);
+}
+
+extern "C" size_t mixq_gemm_scratch_bytes(void) { return mixq::kScratchBytes; }
+
+extern "C" int mixq_gemm_noalloc(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
+                                 const mixq_act_state* state, const mixq_weight* w, int64_t M,
+                                 void* Y, int64_t ldy, int32_t out_mode, int32_t* acc_debug,
+                                 void* stream) {
+    return mixq::gemm_impl(Xq, s_x, X_out, state, w, M, static_cast<float*>(Y), ldy, acc_debug,
+                           nullptr, 0, stream, out_mode, /*own_ws=*/true);
 }

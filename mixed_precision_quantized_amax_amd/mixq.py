@@ -105,6 +105,11 @@ def lib() -> ctypes.CDLL:
         L.mixq_check_device.restype = ctypes.c_int
         L.mixq_version.argtypes = []
         L.mixq_version.restype = ctypes.c_int
+        L.mixq_gemm_noalloc.argtypes = [P, P, P, ctypes.POINTER(ActState),
+                                        ctypes.POINTER(Weight), I64, P, I64, I32, P, P]
+        L.mixq_gemm_noalloc.restype = ctypes.c_int
+        L.mixq_gemm_scratch_bytes.argtypes = []
+        L.mixq_gemm_scratch_bytes.restype = ctypes.c_size_t
         L.mixq_set_gemm_variant.argtypes = [I32]
         L.mixq_set_gemm_variant.restype = ctypes.c_int
         _lib = L
@@ -122,6 +127,20 @@ def _ptr(t: torch.Tensor | None):
 
 def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def gemm_noalloc(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None,
+                 state: OutlierState, pw: PackedWeight, Y: torch.Tensor,
+                 out_mode: int = OUT_F32, acc_debug: torch.Tensor | None = None) -> None:
+    """mixq_gemm_noalloc: mixq_gemm_ex with the library's own device
+    workspace (no workspace argument, nothing allocated)."""
+    M = Xq.shape[0]
+    st = state.c()
+    w = pw.c()
+    rc = lib().mixq_gemm_noalloc(_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(st),
+                                 ctypes.byref(w), M, _ptr(Y), Y.stride(0), int(out_mode),
+                                 _ptr(acc_debug), _stream(Y.device))
+    _check("mixq_gemm_noalloc", rc)
 
 
 # GEMM kernel variants (ids of mixq_set_gemm_variant; testing hook)
