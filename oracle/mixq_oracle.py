@@ -131,6 +131,10 @@ class Oracle:
         return mixed_feature_quantize_weight(W, salient, group, oracle=self)
 
     # -- the operation after the layer ---------------------------------------------
+    def round_16bit(self, Y, kind: str):
+        """See ``round_16bit`` below."""
+        return round_16bit(Y, kind)
+
     def swiglu(self, Y):
         """Returns silu(gate) * up in float64; see ``swiglu`` below."""
         return swiglu(Y)
@@ -291,6 +295,30 @@ def _rne_div(a, b):
     r2 = 2 * (a - q * b)           # twice the remainder, in [0, 2b)
     up = (r2 > b) | ((r2 == b) & (q % 2 == 1))
     return q + up
+
+
+def round_16bit(Y, kind: str):
+    """The layer output handed on in 16 bits: each value of the oracle's
+    float64 Y rounded once to the nearest fp16 ("f16") or bf16 ("bf16")
+    value, ties to even (the 16-bit output modes; the pages' systems pass
+    16-bit activations to the next layer).  Finite values in range are a
+    precondition.  Returns float64 values that are exactly representable in
+    the chosen format.
+
+    A nonzero y = f * 2^E with f in [1, 2); a format with p significant bits
+    and least normal exponent e_min has quantum 2^(max(E, e_min) - (p - 1)),
+    and the result is that quantum times the nearest integer to y / quantum
+    (half to even).  p = 11, e_min = -14 for fp16; p = 8, e_min = -126 for
+    bf16."""
+    y = np.asarray(Y, np.float64)
+    p, emin = {"f16": (11, -14), "bf16": (8, -126)}[kind]
+    out = np.zeros_like(y)
+    nz = y != 0
+    _, e = np.frexp(y[nz])           # y = m * 2^e, m in [0.5, 1): E = e - 1
+    E = np.maximum(e - 1, emin)
+    q = np.ldexp(1.0, E - (p - 1))   # quantum (a power of two: y / q is exact)
+    out[nz] = np.rint(y[nz] / q) * q  # rint: half to even
+    return out
 
 
 def swiglu(Y):

@@ -702,6 +702,36 @@ def pin_residual_add(o):
     assert 0 < (hb > base.astype(np.float64) + half.astype(np.float64)).sum() < 64
 
 
+def pin_round_16bit(o):
+    """The 16-bit output rule: fp16 against NumPy's (independent) float64 ->
+    float16 conversion, bf16 against torch's float32 -> bfloat16 conversion
+    on values exact in float32, and both against exact rationals on values
+    built to fall on, just beside and halfway between representable values
+    (ties to even), subnormal fp16 values and powers of two."""
+    import torch
+    r = _rng(77)
+    y = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-6, 4, 4000),
+                        [0.0, -0.0, 1.0, -1.0, 65504.0, 2.0 ** -24, 3 * 2.0 ** -25, 2.0 ** -14]])
+    assert np.array_equal(o.round_16bit(y, "f16"), y.astype(np.float16).astype(np.float64))
+    y32 = y.astype(np.float32).astype(np.float64)
+    tb = torch.from_numpy(y32.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(o.round_16bit(y32, "bf16"), tb)
+    # exact rationals: k halfway points between neighbours q*n and q*(n+1)
+    for kind, p in (("f16", 11), ("bf16", 8)):
+        for E in (-3, 0, 5):
+            q = Fraction(2) ** (E - (p - 1))
+            for n in (2 ** (p - 1), 2 ** (p - 1) + 1, 2 ** p - 2, 2 ** p - 1):
+                for num, want in ((Fraction(1, 2), n + (n % 2)),      # a tie: to the even one
+                                  (Fraction(1, 2) - Fraction(1, 2 ** 20), n),
+                                  (Fraction(1, 2) + Fraction(1, 2 ** 20), n + 1)):
+                    v = (n + num) * q
+                    got = Fraction(float(o.round_16bit(np.array([float(v)]), kind)[0]))
+                    assert got == want * q, (kind, E, n, num)
+    # a value that rounds up into the next binade keeps the even rule
+    assert o.round_16bit(np.array([2047.5]), "f16")[0] == 2048.0
+    assert o.round_16bit(np.array([255.5]), "bf16")[0] == 256.0
+
+
 def pin_swiglu(o):
     """silu(g) * u against SciPy's logistic function (an independent
     routine): silu(g) = g * expit(g); plus silu(0) = 0, up = 0 gives 0,
@@ -834,5 +864,5 @@ ALL_PINS = [pin_golden_act, pin_golden_weight, pin_golden_layer, pin_half_decode
             pin_sign_symmetry, pin_pow2_scaling, pin_permutation, pin_overflow,
             pin_decode_sequence, pin_layer_driver, pin_sampled_output, pin_rmsnorm_fsum, pin_rmsnorm_bound,
             pin_rmsnorm_invariants, pin_rmsnorm_closed_form, pin_rmsnorm_exact_rationals,
-            pin_residual_add, pin_swiglu, pin_progressive_levels, pin_progressive_no_overflow,
+            pin_residual_add, pin_round_16bit, pin_swiglu, pin_progressive_levels, pin_progressive_no_overflow,
             pin_mixed_feature]

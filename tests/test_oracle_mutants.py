@@ -151,6 +151,13 @@ MIXED_MUTANTS = [
     ("mixed_int4_values_not_rebuilt", "q4p, s4, *_ = progressive_quantize_weight(Wh, group)",
      "_, s4, q4p, *_ = progressive_quantize_weight(Wh, group)"),
 ]
+ROUND16_MUTANTS = [
+    ("round16_ties_away", "out[nz] = np.rint(y[nz] / q) * q",
+     "out[nz] = np.sign(y[nz]) * np.floor(np.abs(y[nz] / q) + 0.5) * q"),
+    ("round16_truncates", "out[nz] = np.rint(y[nz] / q) * q", "out[nz] = np.trunc(y[nz] / q) * q"),
+    ("round16_fp16_precision", '"f16": (11, -14)', '"f16": (10, -14)'),
+    ("round16_bf16_as_f16", '"bf16": (8, -126)', '"bf16": (11, -14)'),
+]
 PIN_KEY = {"progressive_quantize_weight": "progressive",
            "mixed_feature_quantize_weight": "mixed_feature"}
 
@@ -160,10 +167,11 @@ PIN_KEY = {"progressive_quantize_weight": "progressive",
                          [("residual_add", *m) for m in RES_MUTANTS] +
                          [("swiglu", *m) for m in SWIGLU_MUTANTS] +
                          [("progressive_quantize_weight", *m) for m in PROG_MUTANTS] +
-                         [("mixed_feature_quantize_weight", *m) for m in MIXED_MUTANTS],
+                         [("mixed_feature_quantize_weight", *m) for m in MIXED_MUTANTS] +
+                         [("round_16bit", *m) for m in ROUND16_MUTANTS],
                          ids=[m[0] for m in RMS_MUTANTS] + [m[0] for m in RES_MUTANTS] +
                          [m[0] for m in SWIGLU_MUTANTS] + [m[0] for m in PROG_MUTANTS] +
-                         [m[0] for m in MIXED_MUTANTS])
+                         [m[0] for m in MIXED_MUTANTS] + [m[0] for m in ROUND16_MUTANTS])
 def test_prologue_mutant_is_caught(fn, name, old, new):
     import inspect
     import textwrap
