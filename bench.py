@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_I8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_F16_TFLOPS = 2500.0    # MI355X dense FP16 MFMA, published
+PEAK_CLOCK_GHZ = 2.4        # MI355X peak engine clock (the published peaks' clock)
 METRIC = "mixed-precision GEMM effective TOPS + % of INT8 MFMA peak (LLaMA shapes)"
 CACHE_DEFEAT_BYTES = 768 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
@@ -40,6 +42,49 @@ GEMM_SRC = os.path.join(ROOT, "mixed_precision_quantized_amax_amd", "csrc", "mix
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def launch_times(stream, n: int, fn) -> dict:
+    """Durations (us) of n launches of fn, each bracketed by its own HIP
+    event pair on the launch stream: median, mean, min and 90th percentile."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
+    return {"median_us": round(float(np.median(t)), 2), "mean_us": round(float(t.mean()), 2),
+            "min_us": round(float(t.min()), 2), "p90_us": round(float(np.percentile(t, 90)), 2),
+            "launches": n}
+
+
+def clock_of(stream, fn, n: int = 30) -> dict:
+    """Engine clock of the GEMM kernel itself: its blocks record the shader
+    clock (s_memtime) and the 100 MHz real-time counter at entry and exit
+    (mixq_set_clock_record); the clock of a block is the ratio of the two
+    deltas.  Median and range over the blocks of the last of n launches."""
+    import torch
+    from mixed_precision_quantized_amax_amd import mixq
+    buf = torch.zeros(4 * 4096, dtype=torch.int64, device="cuda")
+    mixq.set_clock_record(buf)
+    try:
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+    finally:
+        mixq.set_clock_record(None)
+    c = buf.view(-1, 4).cpu().numpy()
+    c = c[c[:, 3] > c[:, 2]]
+    f = (c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6) / 1e9
+    span_us = (c[:, 3].max() - c[:, 2].min()) / 100.0
+    return {"ghz_median": round(float(np.median(f)), 3), "ghz_min": round(float(f.min()), 3),
+            "ghz_max": round(float(f.max()), 3), "blocks": int(c.shape[0]),
+            "block_us_median": round(float(np.median(c[:, 3] - c[:, 2])) / 100.0, 2),
+            "kernel_span_us": round(float(span_us), 2)}
 
 
 def gemm_source_sha() -> str:
@@ -145,28 +190,18 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0):
     torch.cuda.synchronize()
     graph_ms_step = t0.elapsed_time(t1) / steps
 
-    # GEMM kernel duration: back-to-back launches bracketed by events on the
-    # launch stream (the host enqueues faster than the kernel runs)
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record(stream)
-    for i in range(steps):
-        steps_c[i % copies].gemm()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    gemm_ms = g0.elapsed_time(g1) / steps
-    # activation side (quantize + gather gate), also back to back
-    torch.cuda.synchronize()
-    g0.record(stream)
-    for i in range(steps):
-        steps_c[i % copies].act()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    act_ms = g0.elapsed_time(g1) / steps
+    # GEMM kernel duration, one event pair around each launch on its stream:
+    # clean cache (the copies rotate, as in the steps) and hot (one copy)
+    nl = max(50, steps)
+    gemm_clean = launch_times(stream, nl, lambda i: steps_c[i % copies].gemm())
+    gemm_hot = launch_times(stream, nl, lambda i: steps_c[0].gemm())
+    act_t = launch_times(stream, nl, lambda i: steps_c[i % copies].act())
+    # engine clock of the GEMM itself: each block's shader-clock and 100 MHz
+    # real-time stamps at entry and exit, over the last of 30 clean launches
+    clk = clock_of(stream, lambda i: steps_c[i % copies].gemm())
     flag = int(state.flag.cpu()[0])
-    return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm_ms=gemm_ms, act_ms=act_ms,
-                count=count, flag=flag, copies=copies)
+    return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm=gemm_clean, gemm_hot=gemm_hot,
+                act=act_t, clock=clk, count=count, flag=flag, copies=copies)
 
 
 def run_mixed(wl, steps: int, warmup: int, salient):
@@ -388,7 +423,10 @@ def run_decode_sequence(wl, repeats: int = 3):
     """The outlier-locality decode sequence: every step runs the whole layer on
     a new batch, the cached set carrying over; the set is re-detected only on
     steps whose uncached amax crosses the threshold.  Inputs for all steps are
-    generated up front and resident on the GPU.  Returns per-step time."""
+    generated up front and resident on the GPU.  Returns per-step time (median
+    of `repeats` timed passes, each from an empty set), the steps whose gate
+    fired (read after every step of one more, untimed pass) and the GEMM and
+    activation side per launch at the steady set."""
     import torch
     from mixed_precision_quantized_amax_amd import mixq, workloads
 
@@ -404,24 +442,36 @@ def run_decode_sequence(wl, repeats: int = 3):
     Xo = torch.zeros(wl.M * ld, dtype=torch.float16, device=dev)
     Y = torch.empty(wl.M, wl.N, dtype=torch.float32, device=dev)
     ws = mixq.gemm_workspace(wl.M, wl.N, wl.K, wl.bits, dev)  # split K
-    times, fired = [], 0
-    for rep in range(repeats):
+    stream = torch.cuda.current_stream(dev)
+
+    def fresh():
         state = mixq.OutlierState.create(wl.K, k_cap, dev)   # fresh, empty set
         pw = mixq.PackedWeight.create(wl.N, wl.K, wl.bits, k_cap, dev)
         mixq.pack_weight(W, state, pw, mixq.PACK_FULL)
-        steps = [mixq.LayerStep(X, wl.tau, state, W, pw, Xq, sx, Xo, Y, ws=ws) for X in Xs]
+        return state, [mixq.LayerStep(X, wl.tau, state, W, pw, Xq, sx, Xo, Y, ws=ws) for X in Xs]
+
+    state, steps = fresh()
+    fired = []
+    for t, st in enumerate(steps):
+        st()
+        if int(state.flag.cpu()[0]) & mixq.FLAG_FIRED:
+            fired.append(t)
+    times = []
+    for rep in range(repeats):
+        state, steps = fresh()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0.record(stream)
         for st in steps:
             st()
-        e1.record()
+        e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / wl.steps)
-        count = int(state.count.cpu()[0])
-    ms = float(np.median(times))
-    return dict(ms_step=ms, count=count)
+    count = int(state.count.cpu()[0])
+    gemm = launch_times(stream, 50, lambda i: steps[-1].gemm())
+    act = launch_times(stream, 50, lambda i: steps[-1].act())
+    return dict(ms_step=float(np.median(times)), count=count, fired=fired, gemm=gemm, act=act)
 
 
 def copy_calibration(nbytes: int = 256 << 20):
@@ -485,7 +535,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (for scaling byte counters)")
     ap.add_argument("--all", action="store_true",
-                    help="also measure the other workload shapes and the decode sequence")
+                    help="also measure progressive INT4 and output-feature mixed precision")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the LLaMA shapes, the INT4 prefill and the decode sequence")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -511,9 +563,16 @@ def main():
     r = run_gpu(wl, args.steps, args.warmup)
     ops = wl.ops
     value = ops / (r["ms_step"] / 1e3) / 1e12
-    gemm_tops = ops / (r["gemm_ms"] / 1e3) / 1e12
+    g = r["gemm"]
+    gemm_tops = ops / (g["mean_us"] / 1e6) / 1e12
     alg_bytes = algorithmic_bytes(wl, r["count"])
     traffic = gemm_traffic(wl.name)
+    clk = r["clock"]
+    kp = (r["count"] + 31) // 32 * 32
+    # the method's own work on its own units: 2MN(K-k) INT8 ops plus 2MNk
+    # FP16 flops (the kernel issues 2MN*kpad of the latter)
+    t_roof_us = (2.0 * wl.M * wl.N * (wl.K - r["count"]) / (PEAK_I8_TOPS * 1e12)
+                 + 2.0 * wl.M * wl.N * r["count"] / (PEAK_F16_TFLOPS * 1e12)) * 1e6
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -534,33 +593,57 @@ def main():
                    "threshold": wl.tau, "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * value / PEAK_I8_TOPS, 2),
         "gemm_tops": round(gemm_tops, 2),
-        "gemm_us": round(r["gemm_ms"] * 1e3, 2),
-        "act_quant_us": round(r["act_ms"] * 1e3, 2),
-        "act_quant_gbs": round((2 + 1) * wl.M * wl.K / (r["act_ms"] / 1e3) / 1e9, 1),
+        "gemm_us": g["mean_us"],
+        "gemm_us_median": g["median_us"],
+        "gemm_launches": g,
+        "gemm_hot_cache": dict(r["gemm_hot"], tops=round(ops / (r["gemm_hot"]["mean_us"] / 1e6)
+                                                         / 1e12, 2)),
+        "act_quant_us": r["act"]["mean_us"],
+        "act_quant": r["act"],
+        "engine_clock": dict(clk, pct_of_measured_clock_peak=round(
+            100.0 * gemm_tops / (PEAK_I8_TOPS * clk["ghz_median"] / PEAK_CLOCK_GHZ), 2)),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_I8_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "traffic_source": "rocprofv3 TCC FETCH_SIZE + WRITE_SIZE per GEMM launch "
+                                       "(L2 to fabric: HBM plus Infinity Cache hits), scaled by "
+                                       "a copy of known size",
+                     "t_roof_us": round(t_roof_us, 2),
+                     "frac_mixed": round(t_roof_us / g["mean_us"], 4),
                      "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
     }
     out["fused_rmsnorm_act"] = run_fused_norm(wl, args.steps, min(args.warmup, 50))
     out["swiglu_gate_up"] = run_swiglu(wl, max(20, args.steps // 2), min(args.warmup, 50))
-    if args.all:
-        others = {}
+    others = {}
+    if not args.no_workloads:
         for name in ("llama7b_up", "llama70b_up", "prefill_w4"):
             w2 = workloads.WORKLOADS[name]
-            r2 = run_gpu(w2, max(10, args.steps // 2), args.warmup)
+            r2 = run_gpu(w2, max(20, args.steps // 2), min(args.warmup, 100))
             others[name] = {"step_tops": round(w2.ops / (r2["ms_step"] / 1e3) / 1e12, 1),
-                            "gemm_tops": round(w2.ops / (r2["gemm_ms"] / 1e3) / 1e12, 1),
-                            "gemm_us": round(r2["gemm_ms"] * 1e3, 1),
-                            "act_quant_us": round(r2["act_ms"] * 1e3, 1),
+                            "gemm_tops": round(w2.ops / (r2["gemm"]["mean_us"] / 1e6) / 1e12, 1),
+                            "gemm_us": r2["gemm"]["mean_us"],
+                            "gemm_us_median": r2["gemm"]["median_us"],
+                            "gemm_hot_us": r2["gemm_hot"]["mean_us"],
+                            "act_quant_us": r2["act"]["mean_us"],
+                            "engine_clock_ghz": r2["clock"]["ghz_median"],
                             "ms_per_step": round(r2["ms_step"], 4)}
+        dwl = workloads.WORKLOADS["decode_seq"]
+        d = run_decode_sequence(dwl)
+        others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),
+                                "ms_per_step": round(d["ms_step"], 4),
+                                "gemm_us": d["gemm"]["mean_us"],
+                                "gemm_us_median": d["gemm"]["median_us"],
+                                "act_quant_us": d["act"]["mean_us"],
+                                "fired_steps": d["fired"], "gate_firings": len(d["fired"]),
+                                "outlier_channels_final": d["count"]}
+    if args.all:
         w4 = workloads.WORKLOADS["prefill_w4"]
         r4 = run_gpu(w4, max(10, args.steps // 2), args.warmup, group=128)
         others["prefill_w4_progressive"] = {
             "step_tops": round(w4.ops / (r4["ms_step"] / 1e3) / 1e12, 1),
-            "gemm_tops": round(w4.ops / (r4["gemm_ms"] / 1e3) / 1e12, 1),
-            "gemm_us": round(r4["gemm_ms"] * 1e3, 1),
-            "act_quant_us": round(r4["act_ms"] * 1e3, 1),
+            "gemm_tops": round(w4.ops / (r4["gemm"]["mean_us"] / 1e6) / 1e12, 1),
+            "gemm_us": r4["gemm"]["mean_us"],
+            "act_quant_us": r4["act"]["mean_us"],
             "ms_per_step": round(r4["ms_step"], 4),
             "weights": "progressive group-wise INT4, groups of 128 (rebuilt to INT8 in the loader)"}
         sal = workloads.make_salient(w4.N)
@@ -574,11 +657,7 @@ def main():
             "weights": f"{r5['rows'][0]} of {w4.N} output features 8-bit (an INT8 row subset), "
                        f"{r5['rows'][1]} progressive INT4; two products into one Y; "
                        "TOPS count 2*M*N*K"}
-        dwl = workloads.WORKLOADS["decode_seq"]
-        d = run_decode_sequence(dwl)
-        others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),
-                                "ms_per_step": round(d["ms_step"], 4),
-                                "outlier_channels_final": d["count"]}
+    if others:
         out["workloads"] = others
     if not args.no_cpu_baseline:
         try:

@@ -459,6 +459,20 @@ size_t mixq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits);
  */
 int mixq_set_gemm_variant(int32_t variant);
 
+/*
+ * mixq_set_clock_record -- measurement hook.  While buf is set, every later
+ * GEMM launch in the process has its blocks b < n_blocks write four int64
+ * stamps to buf[4b .. 4b+3]: the shader-clock counter (s_memtime) at the
+ * block's entry and exit, then the 100 MHz real-time counter
+ * (s_memrealtime) at entry and exit, so that the engine clock of the
+ * product itself is (clock delta) / (real-time delta / 100 MHz).  Each
+ * launch overwrites the records of the last.  buf: device memory of
+ * 4 * n_blocks int64; (NULL, 0) turns the hook off (the default).
+ * Errors: MIXQ_ERR_INVALID_ARG for a null buf with n_blocks > 0 or the
+ *         reverse, or n_blocks < 0.
+ */
+int mixq_set_clock_record(int64_t *buf, int32_t n_blocks);
+
 /* Text of a status code (static storage). */
 const char *mixq_status_string(int status);
 

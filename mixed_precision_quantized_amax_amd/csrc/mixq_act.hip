@@ -373,20 +373,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     __shared__ uint32_t red[2][kRB][W];
     __shared__ double rsum[NORM ? 2 : 1][kRB][W][2];
     __shared__ int any_det;
-    build_keep_lut(lut);
-    for (int w = threadIdx.x; w < a.words; w += kGateThreads) {
-        newbits[w] = 0u;
-        sbits[w] = a.bitmap[w];
-    }
-    if constexpr (NORM) {
-        uint4* const g4 = reinterpret_cast<uint4*>(dyn + 2 * a.words);
-        for (int c = threadIdx.x; c < a.nchunks; c += kGateThreads)
-            g4[c] = *reinterpret_cast<const uint4*>(a.gamma + (int64_t)c * 8);
-    }
-    if (threadIdx.x == 0) any_det = 0;
     const int set_size = *a.count;
-    __syncthreads();
-
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int slot = wave / W, part = wave % W;
@@ -403,26 +390,55 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     const uint16_t ggam = (NORM && gset) ? a.gamma[gch] : 0;
     typedef uint4 XV[CPT];
     typedef uint32_t WV[CPT];
-    auto load_seg = [&](int64_t row, int s, XV& xv, WV& wv) {
+    // X chunks of one segment of a token's part (global loads only)
+    auto load_x = [&](int64_t row, int s, XV& xv) {
         const bool valid = row < a.M;
         const uint16_t* xr = a.X + (valid ? row : 0) * a.ldx;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = chunk(s, i);
-            if (valid && c < a.nchunks) {
-                xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
-                wv[i] = sbits[c >> 2];
-            } else {
-                xv[i] = make_uint4(0, 0, 0, 0);
-                wv[i] = 0u;
-            }
+            xv[i] = (valid && c < a.nchunks) ? *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)
+                                             : make_uint4(0, 0, 0, 0);
         }
     };
+    // the cached-set bits of the same chunks (from the bitmap staged in LDS)
+    auto load_bits = [&](int s, WV& wv) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = chunk(s, i);
+            wv[i] = c < a.nchunks ? sbits[c >> 2] : 0u;
+        }
+    };
+    auto load_seg = [&](int64_t row, int s, XV& xv, WV& wv) {
+        load_x(row, s, xv);
+        load_bits(s, wv);
+    };
     // the first segment of a token's part and its first gather value
-    auto load_row = [&](int64_t row, XV& xv, WV& wv, uint16_t& gv) {
-        load_seg(row, 0, xv, wv);
+    auto load_row = [&](int64_t row, XV& xv, uint16_t& gv) {
+        load_x(row, 0, xv);
         if (gset && row < a.M) gv = a.X[row * a.ldx + gch];
     };
+    // The first token's loads go out before the cached set is staged in LDS,
+    // so that the two memory latencies overlap (the set's bits are read
+    // from LDS only when the amax needs them).
+    XV xa, xb;
+    WV wa, wb;
+    uint16_t ga = 0, gb2 = 0;
+    int64_t r0 = (int64_t)blockIdx.x * kRB;
+    if (!RES && r0 < a.M) load_row(r0 + slot, xa, ga);
+    build_keep_lut(lut);
+    for (int w = threadIdx.x; w < a.words; w += kGateThreads) {
+        newbits[w] = 0u;
+        sbits[w] = a.bitmap[w];
+    }
+    if constexpr (NORM) {
+        uint4* const g4 = reinterpret_cast<uint4*>(dyn + 2 * a.words);
+        for (int c = threadIdx.x; c < a.nchunks; c += kGateThreads)
+            g4[c] = *reinterpret_cast<const uint4*>(a.gamma + (int64_t)c * 8);
+    }
+    if (threadIdx.x == 0) any_det = 0;
+    __syncthreads();
+
     // RES: the matching D chunks and gather value
     auto load_d = [&](int64_t row, XV& dv, uint16_t& gd) {
         const bool valid = row < a.M;
@@ -442,6 +458,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         const uint16_t* xr = a.X + (valid ? row : 0) * a.ldx;
         uint16_t* orow = (a.ld_out && valid) ? a.X_out + row * (int64_t)a.ld_out : nullptr;
         auto keep_of = [&](int i, int c) -> uint4 { return lut[(wv[i] >> ((c & 3) * 8)) & 0xFFu]; };
+        load_bits(0, wv);
 
         if constexpr (RES) {
             uint16_t* hr = a.H + (valid ? row : 0) * a.ldh;
@@ -570,26 +587,20 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     const int64_t stride = (int64_t)gridDim.x * kRB;
     if constexpr (RES) {
         int par = 0;
-        for (int64_t r0 = (int64_t)blockIdx.x * kRB; r0 < a.M; r0 += stride) {
-            XV xa, da;
-            WV wa;
-            uint16_t ga = 0, gd = 0;
-            load_row(r0 + slot, xa, wa, ga);
+        for (; r0 < a.M; r0 += stride) {
+            XV da;
+            uint16_t gd = 0;
+            load_row(r0 + slot, xa, ga);
             load_d(r0 + slot, da, gd);
             process(r0 + slot, xa, wa, ga, par, &da, gd);
             par ^= 1;
         }
     } else {
-    XV xa, xb;
-    WV wa, wb;
-    uint16_t ga = 0, gb2 = 0;
-    int64_t r0 = (int64_t)blockIdx.x * kRB;
-    if (r0 < a.M) load_row(r0 + slot, xa, wa, ga);
     for (; r0 < a.M; r0 += 2 * stride) {
-        if (r0 + stride < a.M) load_row(r0 + stride + slot, xb, wb, gb2);
+        if (r0 + stride < a.M) load_row(r0 + stride + slot, xb, gb2);
         process(r0 + slot, xa, wa, ga, 0, nullptr, 0);
         if (r0 + stride >= a.M) break;
-        if (r0 + 2 * stride < a.M) load_row(r0 + 2 * stride + slot, xa, wa, ga);
+        if (r0 + 2 * stride < a.M) load_row(r0 + 2 * stride + slot, xa, ga);
         process(r0 + stride + slot, xb, wb, gb2, 1, nullptr, 0);
     }
     }

@@ -78,6 +78,10 @@ struct GemmArgs {
     const int32_t* rmap;
     int32_t n_out;
     int32_t wbits;  // 8 or 4 (host side: which launcher)
+    // measurement hook (null: off): block b < clk_n writes its shader-clock
+    // and 100 MHz real-time stamps at entry and exit to clk[4b .. 4b+3]
+    int64_t* clk;
+    int32_t clk_n;
 };
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -198,6 +202,22 @@ void gemm_kernel(GemmArgs a) {
     const int wm = wave / WN, wn = wave % WN;
     // size of the outlier set (read once, long before the epilogue needs it)
     const int count = *a.count;
+    int64_t clk_t0 = 0, clk_r0 = 0;
+    if (a.clk) {
+        clk_t0 = (int64_t)__builtin_amdgcn_s_memtime();
+        clk_r0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+    }
+    auto clk_end = [&]() __attribute__((always_inline)) {
+        if (a.clk && tid == 0 && (int)blockIdx.x < a.clk_n) {
+            const int64_t t1 = (int64_t)__builtin_amdgcn_s_memtime();
+            const int64_t r1 = (int64_t)__builtin_amdgcn_s_memrealtime();
+            int64_t* c = a.clk + 4 * (int64_t)blockIdx.x;
+            c[0] = clk_t0;
+            c[1] = t1;
+            c[2] = clk_r0;
+            c[3] = r1;
+        }
+    };
 
     // ---- block id -> tile, XCD-aware ------------------------------------------
     int bid = blockIdx.x;
@@ -740,7 +760,10 @@ void gemm_kernel(GemmArgs a) {
                 __hip_atomic_store(a.sync + tbid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        if (!second) return;
+        if (!second) {
+            clk_end();
+            return;
+        }
         for (int t = 0; t < S; ++t) {
             if (t == split) continue;
 #pragma unroll
@@ -912,6 +935,7 @@ void gemm_kernel(GemmArgs a) {
                     }
                 }
             }
+        clk_end();
         return;
     }
     if (!ROWS && a.out_mode == MIXQ_OUT_F32 && rows_a == BM && n0 + BN <= a.N) {
@@ -927,6 +951,7 @@ void gemm_kernel(GemmArgs a) {
                     __builtin_amdgcn_raw_buffer_store_b32(
                         acc[i][j][e], rY, voff + j * 128,
                         (wm * C::kWTM + i * 32 + 8 * (e >> 2) + (e & 3)) * ldyb, 0);
+        clk_end();
         return;
     }
     const bool bf16 = a.out_mode == MIXQ_OUT_BF16;
@@ -965,6 +990,7 @@ void gemm_kernel(GemmArgs a) {
                 }
             }
         }
+    clk_end();
 }
 
 template <int BM, int BN, int WM, int WN, int BITS, int STAGES, int PF = 1, bool PROG = false,
@@ -995,6 +1021,8 @@ enum {
 };
 
 std::atomic<int> g_forced_variant{0};
+std::atomic<int64_t*> g_clock_buf{nullptr};
+std::atomic<int32_t> g_clock_n{0};
 
 int pick_cfg(int64_t M, int64_t N, int64_t K, int bits) {
     const int f = g_forced_variant.load(std::memory_order_relaxed);
@@ -1163,6 +1191,8 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
     a.n_begin = 0;
     a.n_end = a.N;
     a.wbits = w->bits;
+    a.clk = g_clock_buf.load(std::memory_order_relaxed);
+    a.clk_n = a.clk ? g_clock_n.load(std::memory_order_relaxed) : 0;
     a.ksplit = 1;
     a.sync = nullptr;
     a.part = nullptr;
@@ -1235,6 +1265,13 @@ int gemm_impl(const int8_t* Xq, const float* s_x, const uint16_t* X_out,
 
 }  // namespace
 }  // namespace mixq
+
+extern "C" int mixq_set_clock_record(int64_t* buf, int32_t n_blocks) {
+    if ((buf == nullptr) != (n_blocks == 0) || n_blocks < 0) return MIXQ_ERR_INVALID_ARG;
+    mixq::g_clock_n.store(n_blocks, std::memory_order_relaxed);
+    mixq::g_clock_buf.store(buf, std::memory_order_relaxed);
+    return MIXQ_OK;
+}
 
 extern "C" int mixq_set_gemm_variant(int32_t variant) {
     if (variant < 0 || variant >= mixq::kCfgCount) return MIXQ_ERR_INVALID_ARG;

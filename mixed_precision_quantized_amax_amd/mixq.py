@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
         L.mixq_gemm_noalloc.restype = ctypes.c_int
         L.mixq_gemm_scratch_bytes.argtypes = []
         L.mixq_gemm_scratch_bytes.restype = ctypes.c_size_t
+        L.mixq_set_clock_record.argtypes = [P, I32]
+        L.mixq_set_clock_record.restype = ctypes.c_int
         L.mixq_set_gemm_variant.argtypes = [I32]
         L.mixq_set_gemm_variant.restype = ctypes.c_int
         _lib = L
@@ -153,6 +155,18 @@ def set_gemm_variant(variant: int | str) -> None:
     the automatic choice); for tests that cover each variant."""
     v = GEMM_VARIANTS[variant] if isinstance(variant, str) else int(variant)
     _check("mixq_set_gemm_variant", lib().mixq_set_gemm_variant(v))
+
+
+def set_clock_record(buf: torch.Tensor | None) -> None:
+    """Measurement hook: while ``buf`` (int64 device tensor of 4 * n) is
+    set, GEMM blocks b < n write their entry/exit shader-clock and 100 MHz
+    real-time stamps to buf[4b:4b+4]; None turns it off."""
+    if buf is None:
+        _check("mixq_set_clock_record", lib().mixq_set_clock_record(None, 0))
+    else:
+        assert buf.dtype == torch.int64 and buf.numel() % 4 == 0
+        _check("mixq_set_clock_record",
+               lib().mixq_set_clock_record(ctypes.c_void_p(buf.data_ptr()), buf.numel() // 4))
 
 
 def outlier_ld(k_cap: int) -> int:
