@@ -84,7 +84,13 @@ struct GemmArgs {
     int32_t clk_n;
 };
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 64-byte rows: 16-byte piece c of row r sits at slot c ^ swz(r).  With 64
+// banks of 4 bytes and 16 lanes served per pass, four rows share a bank line
+// (rows r and r + 4 the same banks); swz gives the four rows of each such
+// class distinct slots within any 16 consecutive rows, so fragment reads (16
+// rows, one piece) and the INT4 loader's writes (8 rows, two pieces) are
+// conflict-free.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ swz(r)) << 4); }
 
 // Sign-extend eight 4-bit codes held as the low nibbles of four bytes.
@@ -341,8 +347,14 @@ void gemm_kernel(GemmArgs a) {
         // i.e. whole L2 lines: with 64-byte row pieces every request moves
         // half a line and the L2 delivers markedly fewer bytes per clock.
         // LDS holds two pair buffers, each A[BM][128] + B[BN][128]; chunk c of
-        // row r sits at slot c ^ (r & 7), which keeps both the linear
-        // per-lane writes and the 32-row fragment reads on distinct banks.
+        // row r sits at slot c ^ ((r >> 1) & 7).  gfx950's LDS serves a
+        // 16-byte read for 16 lanes at a time from 64 banks of 4 bytes, so a
+        // 256-byte bank line holds two 128-byte rows (even rows in one half,
+        // odd rows in the other); the 16 rows of a fragment read's lane group
+        // then fall on 16 distinct bank quads, and the linear per-lane writes
+        // are conflict-free as well.  (The swizzle c ^ (r & 7), conflict-free
+        // for 32 banks, put rows r and r + 8 on the same banks: the counters
+        // showed a bank-conflict cycle for every two LDS instructions.)
         // Tiles (64 bytes of K) alternate between two fragment register sets:
         //   phase A of pair p: MFMAs of tile 2p; read tile 2p+1 (pair p, upper
         //     half); write pair p+1's B rows; load pair p+2's B rows; barrier.
@@ -362,20 +374,25 @@ void gemm_kernel(GemmArgs a) {
         // this block's K range: pairs pb .. pb + KP - 1
         const int KP = K / kPR / a.ksplit;
         const int pb = split * KP;
-        // load lane -> row (i*NW + wave)*8 + lane/8 (so row & 7 == lane/8), LDS slot lane%8,
-        // holding chunk (lane%8) ^ (lane/8); the LDS write of a wave instruction is linear
+        // load lane -> row (i*NW + wave)*8 + lane/8, LDS slot lane%8, holding
+        // chunk (lane%8) ^ ((row >> 1) & 7); the LDS write of a wave
+        // instruction is linear
         const int lr = lane >> 3, ls = lane & 7;
         int voff[kPI];
 #pragma unroll
-        for (int i = 0; i < kPI; ++i) voff[i] = ((i * C::kNW + wave) * 8 + lr) * K + ((ls ^ lr) << 4);
+        for (int i = 0; i < kPI; ++i) {
+            const int row = (i * C::kNW + wave) * 8 + lr;
+            voff[i] = row * K + ((ls ^ ((row >> 1) & 7)) << 4);
+        }
         const int wr = wave * 8 * kPR + lane * 16;  // + i * NW * 8 * kPR
-        // fragment reads: tile half h, K half ks -> chunk 4h + 2ks + fh of row r, r & 7 == fr & 7
+        // fragment reads: tile half h, K half ks -> chunk 4h + 2ks + fh of row
+        // r, (r >> 1) & 7 == (fr >> 1) & 7 (fragment rows start on multiples of 32)
         int rdA2[2][2], rdB2[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int sl = ((4 * h + 2 * ks + fh) ^ (fr & 7)) << 4;
+                const int sl = ((4 * h + 2 * ks + fh) ^ ((fr >> 1) & 7)) << 4;
                 rdA2[h][ks] = (wm * C::kWTM + fr) * kPR + sl;
                 rdB2[h][ks] = (wn * C::kWTN + fr) * kPR + sl;
             }
