@@ -144,6 +144,9 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0):
     ws = mixq.gemm_workspace(wl.M, packs[0].N, wl.K, wl.bits, dev)
     steps_c = [mixq.LayerStep(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws)
                for c in range(copies)]
+    # the same steps with the quantize and the column gather as separate calls
+    steps_u = [mixq.LayerStep(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws,
+                              fused=False) for c in range(copies)]
 
     def step(i, ev=None):
         s = steps_c[i % copies]
@@ -196,12 +199,14 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0):
     gemm_clean = launch_times(stream, nl, lambda i: steps_c[i % copies].gemm())
     gemm_hot = launch_times(stream, nl, lambda i: steps_c[0].gemm())
     act_t = launch_times(stream, nl, lambda i: steps_c[i % copies].act())
+    act_u = launch_times(stream, nl, lambda i: steps_u[i % copies].act())
     # engine clock of the GEMM itself: each block's shader-clock and 100 MHz
     # real-time stamps at entry and exit, over the last of 30 clean launches
     clk = clock_of(stream, lambda i: steps_c[i % copies].gemm())
     flag = int(state.flag.cpu()[0])
     return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm=gemm_clean, gemm_hot=gemm_hot,
-                act=act_t, clock=clk, count=count, flag=flag, copies=copies)
+                act=act_t, act_separate=act_u, clock=clk, count=count, flag=flag,
+                copies=copies)
 
 
 def run_mixed(wl, steps: int, warmup: int, salient):
@@ -599,7 +604,8 @@ def main():
         "gemm_hot_cache": dict(r["gemm_hot"], tops=round(ops / (r["gemm_hot"]["mean_us"] / 1e6)
                                                          / 1e12, 2)),
         "act_quant_us": r["act"]["mean_us"],
-        "act_quant": r["act"],
+        "act_quant": dict(r["act"], calls="mixq_quantize_act_regather (gate + re-quantize/regather)",
+                          separate_calls_mean_us=r["act_separate"]["mean_us"]),
         "engine_clock": dict(clk, pct_of_measured_clock_peak=round(
             100.0 * gemm_tops / (PEAK_I8_TOPS * clk["ghz_median"] / PEAK_CLOCK_GHZ), 2)),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_I8_TOPS,

@@ -213,6 +213,23 @@ int mixq_quantize_act(const uint16_t *X, int64_t M, int64_t K, int64_t ldx, floa
                       void *stream);
 
 /*
+ * mixq_quantize_act_regather -- mixq_quantize_act followed by
+ * mixq_pack_weight(W, w->N, K, w->bits, state, MIXQ_PACK_OUTLIER_COLS, w),
+ * in two kernel launches instead of three: the launch that re-quantizes
+ * after a firing gate also re-gathers the weight's outlier columns (MixQ
+ * article, Fig. 11), and on a call whose set stands it checks them (no-op
+ * unless they hold another set).  Results are those of the two calls.
+ *
+ *   X, M, K, ldx, threshold, state, Xq, s_x, X_out   as mixq_quantize_act
+ *   W, w      as mixq_pack_weight (w->K == K, w->k_cap == state->k_cap)
+ * Errors: as mixq_quantize_act and mixq_pack_weight.
+ */
+int mixq_quantize_act_regather(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                               float threshold, const mixq_act_state *state, int8_t *Xq,
+                               float *s_x, uint16_t *X_out, const uint16_t *W,
+                               const mixq_weight *w, void *stream);
+
+/*
  * mixq_rmsnorm_quantize_act -- mixq_quantize_act applied to the RMS-normalised
  * tokens, in the same pass over memory: the amax that the quantization needs
  * is fused into the operation before the layer (MixQ article, "MixQ的解决方案",

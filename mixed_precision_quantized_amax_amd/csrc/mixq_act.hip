@@ -46,6 +46,7 @@ struct ActArgs {
     uint32_t* marker;   // work[2 words]
     uint32_t* arrive;   // work[2 words + 1]
     uint32_t* set_id;   // work[2 words + 2]: serial of the committed set (0 = empty)
+    uint32_t* pend_id;  // work[2 words + 3]: serial the pending set will commit under
     int32_t k_cap;
     int32_t words;
     int32_t nchunks;  // K / 8
@@ -343,6 +344,19 @@ __device__ bool wave_row(const ActArgs& a, int64_t row, const uint32_t* set_word
     return __any(det);
 }
 
+// Serial numbers of committed sets, unique within the process on each device
+// (0 is never issued: it names the empty set of a zero-filled state).  A
+// packed weight records the serial its outlier columns were gathered for, so
+// a set that changed -- grown, reset, or another state's set of the same
+// size -- is always told apart from the one the columns hold.
+__device__ uint32_t g_set_serial = 0u;
+
+__device__ __forceinline__ uint32_t next_set_serial() {
+    uint32_t s = atomicAdd(&g_set_serial, 1u) + 1u;
+    if (s == 0u) s = atomicAdd(&g_set_serial, 1u) + 1u;  // after 2^32 commits: skip 0
+    return s;
+}
+
 constexpr int kGateThreads = 256;
 
 // The steady-state pass: W waves per token, each owning a contiguous part of
@@ -609,7 +623,10 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     if (any_det) {  // block-uniform: only blocks whose tokens crossed the gate
         for (int w = threadIdx.x; w < a.words; w += kGateThreads)
             if (newbits[w]) atomicOr(&a.pending[w], newbits[w]);
-        if (threadIdx.x == 0) atomicOr(a.marker, 1u);
+        // the first block to raise the marker draws the serial that the grown
+        // set will be committed under (a fused regather needs it before the
+        // commit)
+        if (threadIdx.x == 0 && atomicOr(a.marker, 1u) == 0u) *a.pend_id = next_set_serial();
     }
 }
 
@@ -641,23 +658,69 @@ __device__ int scan_popcounts(const uint32_t* src, int words, int* prefix, int* 
 
 constexpr int kReqThreads = 256;
 
-// Serial numbers of committed sets, unique within the process on each device
-// (0 is never issued: it names the empty set of a zero-filled state).  A
-// packed weight records the serial its outlier columns were gathered for, so
-// a set that changed -- grown, reset, or another state's set of the same
-// size -- is always told apart from the one the columns hold.
-__device__ uint32_t g_set_serial = 0u;
+// One packed weight whose outlier columns the re-quantize launch also
+// gathers (mixq_quantize_act_regather): the last `blocks` blocks of the grid
+// take that role.  blocks == 0: no weight.  Block b of the role owns packed
+// rows b, b + blocks, ... and gather slot k_out[b], as in mixq_pack_weight's
+// gather (the same row-to-slot map, so either may serve a later call).
+struct GatherArgs {
+    const uint16_t* W;     // fp16 [n_out or N, K]
+    int64_t N;             // packed rows
+    uint16_t* w_out;       // [N, ld_out]
+    int32_t* k_out;        // [MIXQ_GATHER_SLOTS]
+    int32_t gated;
+    const int32_t* rmap;   // row subset, or null
+    int64_t n_out;
+    int32_t blocks;
+};
 
-__device__ __forceinline__ uint32_t next_set_serial() {
-    uint32_t s = atomicAdd(&g_set_serial, 1u) + 1u;
-    if (s == 0u) s = atomicAdd(&g_set_serial, 1u) + 1u;  // after 2^32 commits: skip 0
-    return s;
+// packed row n's outlier columns for the channels of set_words (ranks from
+// prefix), zeros from `total` up to the padded width
+__device__ void gather_row_from_words(const ActArgs& a, const GatherArgs& g, int64_t n,
+                                      const uint32_t* set_words, const int32_t* prefix,
+                                      int total) {
+    const int64_t srow = g.rmap ? (int64_t)g.rmap[n] : src_row(n, g.N, g.gated);
+    const bool live = !g.rmap || (srow >= 0 && srow < g.n_out);
+    uint16_t* out = g.w_out + n * (int64_t)a.ld_out;
+    for (int w = threadIdx.x; w < a.words; w += blockDim.x) {
+        uint32_t bits = set_words[w];
+        int j = prefix[w];
+        while (bits) {
+            const int ch = w * 32 + __builtin_ctz(bits);
+            out[j++] = live ? g.W[srow * (int64_t)a.K + ch] : (uint16_t)0;
+            bits &= bits - 1u;
+        }
+    }
+    const int kpad = (total + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+    for (int j = total + threadIdx.x; j < kpad; j += blockDim.x) out[j] = 0;
+}
+
+// the gather role on a call whose set did not change: re-gather only if this
+// slot's rows hold another set's columns (first use, or another state)
+__device__ void gather_committed(const ActArgs& a, const GatherArgs& g, int b) {
+    const int32_t serial = (int32_t)*a.set_id;
+    if (g.k_out[b] == serial) return;
+    const int count = *a.count;
+    const int kpad = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+    for (int64_t n = b; n < g.N; n += g.blocks) {
+        const int64_t srow = g.rmap ? (int64_t)g.rmap[n] : src_row(n, g.N, g.gated);
+        const bool live = !g.rmap || (srow >= 0 && srow < g.n_out);
+        uint16_t* out = g.w_out + n * (int64_t)a.ld_out;
+        for (int j = threadIdx.x; j < kpad; j += blockDim.x)
+            out[j] = (live && j < count) ? g.W[srow * (int64_t)a.K + a.idx[j]] : (uint16_t)0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) g.k_out[b] = serial;
 }
 
 template <int CPT, bool NORM>
-__global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
+__global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a, GatherArgs g) {
+    const int nreq = gridDim.x - g.blocks;  // blocks of the re-quantize role
+    const bool gather_role = (int)blockIdx.x >= nreq;
     if (*a.marker == 0u) {
+        // the gate did not fire: the set stands (and flag = 0)
         if (blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
+        if (gather_role) gather_committed(a, g, blockIdx.x - nreq);
         return;
     }
     extern __shared__ uint32_t dyn[];
@@ -668,18 +731,34 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
     __shared__ uint4 lut[kLutEntries];
     build_keep_lut(lut);
 
+    // every block forms the grown set itself (the cached set or-ed with the
+    // pending detections; every gate block finished before this launch)
     for (int w = threadIdx.x; w < a.words; w += kReqThreads) neww[w] = a.bitmap[w] | a.pending[w];
     __syncthreads();
     const int total = scan_popcounts(neww, a.words, prefix, tot);
     const bool overflow = total > a.k_cap;
-    if (!overflow) {
-        const int wave = threadIdx.x / kWave;
-        const int64_t stride = (int64_t)gridDim.x * (kReqThreads / kWave);
-        for (int64_t row = (int64_t)blockIdx.x * (kReqThreads / kWave) + wave; row < a.M;
-             row += stride)
-            wave_row<CPT, false, NORM>(a, row, neww, prefix, total, lut, nullptr);
+    if (!gather_role) {
+        if (!overflow) {
+            const int wave = threadIdx.x / kWave;
+            const int64_t stride = (int64_t)nreq * (kReqThreads / kWave);
+            for (int64_t row = (int64_t)blockIdx.x * (kReqThreads / kWave) + wave; row < a.M;
+                 row += stride)
+                wave_row<CPT, false, NORM>(a, row, neww, prefix, total, lut, nullptr);
+        }
+    } else {
+        const int b = blockIdx.x - nreq;
+        if (overflow) {
+            // the set is left as it was (capacity): the committed columns
+            gather_committed(a, g, b);
+        } else {
+            for (int64_t n = b; n < g.N; n += g.blocks)
+                gather_row_from_words(a, g, n, neww, prefix, total);
+            __syncthreads();
+            if (threadIdx.x == 0) g.k_out[b] = (int32_t)*a.pend_id;
+        }
     }
-    // arrival (fired calls only): the last block commits
+    // arrival (fired calls only), over both roles: the last block commits,
+    // once no block reads the state any more
     __syncthreads();
     if (threadIdx.x == 0) {
         __threadfence();
@@ -704,7 +783,7 @@ __global__ __launch_bounds__(kReqThreads) void requant_kernel(ActArgs a) {
     if (threadIdx.x == 0) {
         if (!overflow) {
             *a.count = total;
-            *a.set_id = next_set_serial();
+            *a.set_id = *a.pend_id;
         }
         *a.flag = overflow ? MIXQ_FLAG_OVERFLOW : MIXQ_FLAG_FIRED;
         *a.marker = 0u;
@@ -717,7 +796,7 @@ static_assert(MIXQ_NORM_K_MAX == kGateWaves * kWave * 16 * 8,
               "the fused RMSNorm keeps a whole token in registers");
 
 template <int CPT_G, int CPT_R, bool NORM, bool RES>
-int launch_act(const ActArgs& a, hipStream_t st) {
+int launch_act(const ActArgs& a, const GatherArgs& g, hipStream_t st) {
     constexpr int kRowsPerBlock = kGateThreads / kWave / kGateWaves;
     int64_t g1 = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
     // Up to 2048 blocks (all variants fit four blocks per CU: at most 127
@@ -745,20 +824,20 @@ int launch_act(const ActArgs& a, hipStream_t st) {
         ar.X = a.H;
         ar.ldx = a.ldh;
     }
-    hipLaunchKernelGGL((requant_kernel<CPT_R, NORM>), dim3((int)g2), dim3(kReqThreads),
-                       (size_t)a.words * 8, st, ar);
+    hipLaunchKernelGGL((requant_kernel<CPT_R, NORM>), dim3((int)g2 + g.blocks), dim3(kReqThreads),
+                       (size_t)a.words * 8, st, ar, g);
     return launch_status();
 }
 
 template <int CPT_G, bool NORM, bool RES>
-int launch_act_r(const ActArgs& a, int64_t K, hipStream_t st) {
+int launch_act_r(const ActArgs& a, const GatherArgs& g, int64_t K, hipStream_t st) {
     // requant: one wave per token, the whole row in registers up to K = 8192
     const int64_t per_lane = (K / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) return launch_act<CPT_G, 1, NORM, RES>(a, st);
-    if (per_lane <= 2) return launch_act<CPT_G, 2, NORM, RES>(a, st);
-    if (per_lane <= 4) return launch_act<CPT_G, 4, NORM, RES>(a, st);
-    if (per_lane <= 8) return launch_act<CPT_G, 8, NORM, RES>(a, st);
-    return launch_act<CPT_G, 16, NORM, RES>(a, st);
+    if (per_lane <= 1) return launch_act<CPT_G, 1, NORM, RES>(a, g, st);
+    if (per_lane <= 2) return launch_act<CPT_G, 2, NORM, RES>(a, g, st);
+    if (per_lane <= 4) return launch_act<CPT_G, 4, NORM, RES>(a, g, st);
+    if (per_lane <= 8) return launch_act<CPT_G, 8, NORM, RES>(a, g, st);
+    return launch_act<CPT_G, 16, NORM, RES>(a, g, st);
 }
 
 }  // namespace
@@ -781,7 +860,8 @@ inline bool overlaps(const uint16_t* p, const uint16_t* q, int64_t M, int64_t K,
 int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
              float eps, float* rstd, float threshold, const mixq_act_state* state, int8_t* Xq,
              float* s_x, uint16_t* X_out, void* stream, const uint16_t* D = nullptr,
-             int64_t ldd = 0, uint16_t* H = nullptr, int64_t ldh = 0) {
+             int64_t ldd = 0, uint16_t* H = nullptr, int64_t ldh = 0,
+             const uint16_t* W = nullptr, const mixq_weight* w = nullptr) {
     if (!X || !state || !Xq || !s_x) return MIXQ_ERR_INVALID_ARG;
     if (!state->idx && state->k_cap > 0) return MIXQ_ERR_INVALID_ARG;
     if (!state->count || !state->flag || !state->bitmap || !state->work)
@@ -807,6 +887,26 @@ int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_
                 ((uintptr_t)H & 15u) != 0))
         return MIXQ_ERR_UNSUPPORTED_SHAPE;
     if (M > (int64_t)1 << 31) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+    // a weight whose outlier columns the same launches re-gather: the checks
+    // of mixq_pack_weight's OUTLIER_COLS mode
+    GatherArgs g{};
+    if (w) {
+        if (!W || w->K != K || w->k_cap != state->k_cap || !w->k_out || !state->work ||
+            (state->k_cap > 0 && (!w->w_out || !state->idx)) || w->N <= 0 ||
+            (w->bits != 8 && w->bits != 4) || (w->gated != 0 && w->gated != 1) ||
+            (w->rmap && (w->gated || w->n_out < 1)))
+            return MIXQ_ERR_INVALID_ARG;
+        if (w->N > (int64_t)1 << 31 || ((uintptr_t)W & 15u) != 0) return MIXQ_ERR_UNSUPPORTED_SHAPE;
+        g.W = W;
+        g.N = w->N;
+        g.w_out = w->w_out;
+        g.k_out = w->k_out;
+        g.gated = w->gated;
+        g.rmap = w->rmap;
+        g.n_out = w->n_out;
+        g.blocks = (int32_t)(w->N < MIXQ_GATHER_SLOTS ? w->N : MIXQ_GATHER_SLOTS);
+        if (state->k_cap == 0) g.blocks = 0;  // no outlier columns to hold
+    }
     int rc = check_device_cached();
     if (rc != MIXQ_OK) return rc;
 
@@ -827,6 +927,7 @@ int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_
     a.marker = state->work + 2 * words;
     a.arrive = state->work + 2 * words + 1;
     a.set_id = state->work + 2 * words + 2;
+    a.pend_id = state->work + 2 * words + 3;
     a.k_cap = state->k_cap;
     a.words = words;
     a.nchunks = (int32_t)(K / 8);
@@ -847,24 +948,24 @@ int act_call(const uint16_t* X, int64_t M, int64_t K, int64_t ldx, const uint16_
     // registers of its kGateWaves waves up to K = 32768
     const int64_t per_lane = (K / 8 + kWave * kGateWaves - 1) / (kWave * kGateWaves);
     if (res) {
-        if (per_lane <= 1) return launch_act_r<1, true, true>(a, K, st);
-        if (per_lane <= 2) return launch_act_r<2, true, true>(a, K, st);
-        if (per_lane <= 4) return launch_act_r<4, true, true>(a, K, st);
-        if (per_lane <= 8) return launch_act_r<8, true, true>(a, K, st);
-        return launch_act_r<16, true, true>(a, K, st);
+        if (per_lane <= 1) return launch_act_r<1, true, true>(a, g, K, st);
+        if (per_lane <= 2) return launch_act_r<2, true, true>(a, g, K, st);
+        if (per_lane <= 4) return launch_act_r<4, true, true>(a, g, K, st);
+        if (per_lane <= 8) return launch_act_r<8, true, true>(a, g, K, st);
+        return launch_act_r<16, true, true>(a, g, K, st);
     }
     if (norm) {
-        if (per_lane <= 1) return launch_act_r<1, true, false>(a, K, st);
-        if (per_lane <= 2) return launch_act_r<2, true, false>(a, K, st);
-        if (per_lane <= 4) return launch_act_r<4, true, false>(a, K, st);
-        if (per_lane <= 8) return launch_act_r<8, true, false>(a, K, st);
-        return launch_act_r<16, true, false>(a, K, st);
+        if (per_lane <= 1) return launch_act_r<1, true, false>(a, g, K, st);
+        if (per_lane <= 2) return launch_act_r<2, true, false>(a, g, K, st);
+        if (per_lane <= 4) return launch_act_r<4, true, false>(a, g, K, st);
+        if (per_lane <= 8) return launch_act_r<8, true, false>(a, g, K, st);
+        return launch_act_r<16, true, false>(a, g, K, st);
     }
-    if (per_lane <= 1) return launch_act_r<1, false, false>(a, K, st);
-    if (per_lane <= 2) return launch_act_r<2, false, false>(a, K, st);
-    if (per_lane <= 4) return launch_act_r<4, false, false>(a, K, st);
-    if (per_lane <= 8) return launch_act_r<8, false, false>(a, K, st);
-    return launch_act_r<16, false, false>(a, K, st);
+    if (per_lane <= 1) return launch_act_r<1, false, false>(a, g, K, st);
+    if (per_lane <= 2) return launch_act_r<2, false, false>(a, g, K, st);
+    if (per_lane <= 4) return launch_act_r<4, false, false>(a, g, K, st);
+    if (per_lane <= 8) return launch_act_r<8, false, false>(a, g, K, st);
+    return launch_act_r<16, false, false>(a, g, K, st);
 }
 
 }  // namespace
@@ -875,6 +976,15 @@ extern "C" int mixq_quantize_act(const uint16_t* X, int64_t M, int64_t K, int64_
                                  float* s_x, uint16_t* X_out, void* stream) {
     return mixq::act_call(X, M, K, ldx, nullptr, 0.0f, nullptr, threshold, state, Xq, s_x, X_out,
                           stream);
+}
+
+extern "C" int mixq_quantize_act_regather(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                          float threshold, const mixq_act_state* state,
+                                          int8_t* Xq, float* s_x, uint16_t* X_out,
+                                          const uint16_t* W, const mixq_weight* w, void* stream) {
+    if (!W || !w) return MIXQ_ERR_INVALID_ARG;
+    return mixq::act_call(X, M, K, ldx, nullptr, 0.0f, nullptr, threshold, state, Xq, s_x, X_out,
+                          stream, nullptr, 0, nullptr, 0, W, w);
 }
 
 extern "C" int mixq_rmsnorm_quantize_act(const uint16_t* H, int64_t M, int64_t K, int64_t ldh,

@@ -1111,6 +1111,7 @@ namespace {
 // be zero before a call; every completed call leaves them zero, and the
 // first call on a device clears them with a fill kernel on its stream.
 
+// every plan on 256 CUs fits: at most two 128 x 128 partial tiles per compute unit
 constexpr size_t kScratchBytes = (size_t)kSplitSyncBytes + 512 * (size_t)kSplitSlotBytes;
 
 __device__ __align__(256) uint8_t scratch[kScratchBytes];

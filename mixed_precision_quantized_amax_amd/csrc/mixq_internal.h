@@ -96,6 +96,15 @@ inline int launch_status() {
 }
 
 // ---- device side -------------------------------------------------------------
+// Source row of packed row n: n itself, or for a gated weight ([W_gate;
+// W_up], N = 2I) the 32-row blocks of gate and up rows interleaved, so that
+// the GEMM epilogue finds gate j and up j in neighbouring fragments.
+__device__ __forceinline__ int64_t src_row(int64_t n, int64_t N, int gated) {
+    if (!gated) return n;
+    const int64_t blk = n >> 6, within = n & 63;
+    return within < 32 ? blk * 32 + within : N / 2 + blk * 32 + (within - 32);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     _Float16 v;
     __builtin_memcpy(&v, &h, 2);

@@ -20,14 +20,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-// Source row of packed row n: n itself, or for a gated weight ([W_gate;
-// W_up], N = 2I) the 32-row blocks of gate and up rows interleaved, so that
-// the epilogue finds gate j and up j in neighbouring fragments.
-__device__ __forceinline__ int64_t src_row(int64_t n, int64_t N, int gated) {
-    if (!gated) return n;
-    const int64_t blk = n >> 6, within = n & 63;
-    return within < 32 ? blk * 32 + within : N / 2 + blk * 32 + (within - 32);
-}
 
 // PROG: progressive INT4 (QServe page, progressive group quantization):
 // first level to INT8 with the range 119, then per group of 128 channels (16

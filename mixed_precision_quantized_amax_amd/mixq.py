@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.mixq_quantize_act.argtypes = [P, I64, I64, I64, ctypes.c_float,
                                         ctypes.POINTER(ActState), P, P, P, P]
         L.mixq_quantize_act.restype = ctypes.c_int
+        L.mixq_quantize_act_regather.argtypes = [P, I64, I64, I64, ctypes.c_float,
+                                                 ctypes.POINTER(ActState), P, P, P, P,
+                                                 ctypes.POINTER(Weight), P]
+        L.mixq_quantize_act_regather.restype = ctypes.c_int
         L.mixq_rmsnorm_quantize_act.argtypes = [P, I64, I64, I64, P, ctypes.c_float,
                                                 ctypes.c_float, ctypes.POINTER(ActState), P, P,
                                                 P, P, P]
@@ -280,6 +284,20 @@ def quantize_act(X: torch.Tensor, tau: float, state: OutlierState, Xq: torch.Ten
     _check("mixq_quantize_act", rc)
 
 
+def quantize_act_regather(X: torch.Tensor, tau: float, state: OutlierState, Xq: torch.Tensor,
+                          s_x: torch.Tensor, X_out: torch.Tensor | None, W: torch.Tensor,
+                          pw: PackedWeight) -> None:
+    """mixq_quantize_act followed by mixq_pack_weight(PACK_OUTLIER_COLS) for
+    one weight, in two kernel launches instead of three."""
+    M, K = X.shape
+    st = state.c()
+    w = pw.c()
+    rc = lib().mixq_quantize_act_regather(_ptr(X), M, K, X.stride(0), ctypes.c_float(tau),
+                                          ctypes.byref(st), _ptr(Xq), _ptr(s_x), _ptr(X_out),
+                                          _ptr(W), ctypes.byref(w), _stream(X.device))
+    _check("mixq_quantize_act_regather", rc)
+
+
 def rmsnorm_quantize_act(H: torch.Tensor, gamma: torch.Tensor, eps: float, tau: float,
                          state: OutlierState, Xq: torch.Tensor, s_x: torch.Tensor,
                          X_out: torch.Tensor | None, rstd: torch.Tensor) -> None:
@@ -378,14 +396,17 @@ def gemm_ex(Xq: torch.Tensor, s_x: torch.Tensor, X_out: torch.Tensor | None,
 
 class LayerStep:
     """One layer step (quantize, outlier-column gather, GEMM) with every
-    ctypes argument built once, so that a hot loop pays only the three
-    foreign calls and their kernel launches."""
+    ctypes argument built once, so that a hot loop pays only the foreign
+    calls and their kernel launches.  ``fused`` (the default) quantizes and
+    re-gathers the weight's outlier columns in one call
+    (mixq_quantize_act_regather: two launches); otherwise mixq_quantize_act
+    and mixq_pack_weight(PACK_OUTLIER_COLS) run separately (three)."""
 
     def __init__(self, X: torch.Tensor, tau: float, state: OutlierState, W: torch.Tensor,
                  pw: PackedWeight, Xq: torch.Tensor, s_x: torch.Tensor,
                  X_out: torch.Tensor | None, Y: torch.Tensor,
                  acc_debug: torch.Tensor | None = None, stream=None,
-                 ws: torch.Tensor | None = None):
+                 ws: torch.Tensor | None = None, fused: bool = True):
         L = lib()
         dev = X.device
         s = ctypes.c_void_p(stream if stream is not None
@@ -394,31 +415,38 @@ class LayerStep:
         self._st = state.c()
         self._w = pw.c()
         M = X.shape[0]
-        self._calls = [
-            ("mixq_quantize_act", L.mixq_quantize_act,
-             (_ptr(X), M, state.K, X.stride(0), ctypes.c_float(tau), ctypes.byref(self._st),
-              _ptr(Xq), _ptr(s_x), _ptr(X_out), s)),
-            ("mixq_pack_weight", L.mixq_pack_weight,
-             (_ptr(W), pw.N, pw.K, pw.bits, ctypes.byref(self._st), PACK_OUTLIER_COLS,
-              ctypes.byref(self._w), s)),
+        if fused:
+            self._act = [
+                ("mixq_quantize_act_regather", L.mixq_quantize_act_regather,
+                 (_ptr(X), M, state.K, X.stride(0), ctypes.c_float(tau), ctypes.byref(self._st),
+                  _ptr(Xq), _ptr(s_x), _ptr(X_out), _ptr(W), ctypes.byref(self._w), s))]
+        else:
+            self._act = [
+                ("mixq_quantize_act", L.mixq_quantize_act,
+                 (_ptr(X), M, state.K, X.stride(0), ctypes.c_float(tau), ctypes.byref(self._st),
+                  _ptr(Xq), _ptr(s_x), _ptr(X_out), s)),
+                ("mixq_pack_weight", L.mixq_pack_weight,
+                 (_ptr(W), pw.N, pw.K, pw.bits, ctypes.byref(self._st), PACK_OUTLIER_COLS,
+                  ctypes.byref(self._w), s))]
+        self._gemm = (
             ("mixq_gemm", L.mixq_gemm,
              (_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(self._st), ctypes.byref(self._w),
               M, _ptr(Y), Y.stride(0), _ptr(acc_debug), s)) if ws is None else
             ("mixq_gemm_ws", L.mixq_gemm_ws,
              (_ptr(Xq), _ptr(s_x), _ptr(X_out), ctypes.byref(self._st), ctypes.byref(self._w),
               M, _ptr(Y), Y.stride(0), _ptr(acc_debug), _ptr(ws),
-              ws.numel() * ws.element_size(), s)),
-        ]
+              ws.numel() * ws.element_size(), s)))
+        self._calls = self._act + [self._gemm]
 
     def act(self):
         """The activation side and the gather: everything before the GEMM."""
-        for name, fn, args in self._calls[:2]:
+        for name, fn, args in self._act:
             rc = fn(*args)
             if rc:
                 _check(name, rc)
 
     def gemm(self):
-        name, fn, args = self._calls[2]
+        name, fn, args = self._gemm
         rc = fn(*args)
         if rc:
             _check(name, rc)
