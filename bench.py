@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -114,8 +115,9 @@ def algorithmic_bytes(wl, k: int) -> int:
             + 2 * kp * (wl.M + wl.N) + 4 * wl.M * wl.N)
 
 
-def run_gpu(wl, steps: int, warmup: int, group: int = 0):
-    """group: 0, or the progressive INT4 group size (INT4 workloads)."""
+def run_gpu(wl, steps: int, warmup: int, group: int = 0, counters: bool = False):
+    """group: 0, or the progressive INT4 group size (INT4 workloads).
+    counters: run the warmup and timed steps only (a byte-counter pass)."""
     import torch
     from mixed_precision_quantized_amax_amd import mixq, workloads
 
@@ -166,11 +168,13 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0):
     log(f"[bench] outlier channels detected: {count}; weight copies: {copies}")
     # one captured graph per buffer copy: a replay launches the step's four
     # kernels without a host round trip per kernel
-    graphs = [mixq.LayerGraph(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws)
-              for c in range(copies)]
+    graphs = [] if counters else [
+        mixq.LayerGraph(Xs[c], wl.tau, state, W, packs[c], Xq[c], sx[c], Xo[c], Y, ws=ws)
+        for c in range(copies)]
     for i in range(warmup):
         step(i)
-    graphs[0].replay()
+    if graphs:
+        graphs[0].replay()
     torch.cuda.synchronize()
 
     # timed region: whole steps through the three library calls
@@ -183,6 +187,8 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0):
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
+    if counters:
+        return dict(ms_step=ms_step, count=count, copies=copies)
 
     # the same steps replayed from the captured graphs, for comparison
     torch.cuda.synchronize()
@@ -491,6 +497,90 @@ def copy_calibration(nbytes: int = 256 << 20):
     log(f"[bench] calibration copy: {nbytes} bytes, 3 times")
 
 
+COUNTER_WORKLOADS = ("prefill_w8", "prefill_w4")
+
+
+def kernel_short_name(k: str) -> str:
+    """'void ns::(anonymous namespace)::gemm_kernel<256, ...>(Args)' ->
+    'gemm_kernel<256, ...>'."""
+    k = k.replace("(anonymous namespace)::", "")
+    if k.startswith("void "):
+        k = k[5:]
+    head, sep, tail = k.split("(")[0].partition("<")
+    return head.split("::")[-1] + sep + tail
+
+
+def read_counter_csv(path: str, counter: str, n_calib: int = 3) -> dict:
+    """Mean value per dispatch of one counter, per kernel, from a rocprofv3
+    --pmc CSV (one row per dispatch and counter).  The first n_calib
+    dispatches of the run are the calibration copies, under the key 'copy'."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                rows.append((int(row["Dispatch_Id"]), kernel_short_name(row["Kernel_Name"]),
+                             float(row["Counter_Value"])))
+    rows.sort()
+    vals = {}
+    for i, (_, name, v) in enumerate(rows):
+        if i < n_calib:
+            if "copyBuffer" not in name:
+                raise SystemExit(f"dispatch {i} is {name}, not the calibration copy")
+            name = "copy"
+        vals.setdefault(name, []).append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, out_json: str, out_txt: str,
+                    nbytes: int = 256 << 20):
+    """HBM bytes per GEMM launch of each counter workload from a FETCH_SIZE
+    pass and a WRITE_SIZE pass of ``bench.py --counters``.  Both counters
+    are in KiB per dispatch; each is scaled so that the calibration copy
+    (nbytes read, nbytes written) reads nbytes."""
+    from mixed_precision_quantized_amax_amd import workloads
+    fe = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    wr = read_counter_csv(write_csv, "WRITE_SIZE")
+    rs = nbytes / 1024.0 / fe["copy"][0]
+    ws_ = nbytes / 1024.0 / wr["copy"][0]
+    gemms = sorted(k for k in fe if k.startswith("gemm_kernel"))
+    lines = [f"calibration copy ({nbytes >> 20} MiB read + {nbytes >> 20} MiB written): "
+             f"FETCH_SIZE {fe['copy'][0]:.0f} KiB, WRITE_SIZE {wr['copy'][0]:.0f} KiB",
+             f"scale factors: read {rs:.4f}, write {ws_:.4f}"]
+    res = {}
+    for name in COUNTER_WORKLOADS:
+        wl = workloads.WORKLOADS[name]
+        # INT8 weights: template BITS 8; INT4: 4 (the only GEMM of each pass)
+        kern = [k for k in gemms if re.match(rf"gemm_kernel<\d+, \d+, \d+, \d+, {wl.bits},", k)]
+        if len(kern) != 1:
+            raise SystemExit(f"{name}: expected one GEMM kernel, found {kern}")
+        f_kib, n = fe[kern[0]]
+        w_kib = wr[kern[0]][0]
+        hbm = int(f_kib * 1024 * rs + w_kib * 1024 * ws_)
+        alg = algorithmic_bytes(wl, wl.n_outliers)
+        res[name] = {"hbm_bytes_per_launch": hbm, "fetch_kib": round(f_kib, 1),
+                     "write_kib": round(w_kib, 1), "read_scale": round(rs, 4),
+                     "write_scale": round(ws_, 4), "dispatches": n}
+        lines.append(f"{name} {kern[0]} ({n} dispatches): FETCH_SIZE {f_kib:.0f} KiB -> "
+                     f"{f_kib * rs / 1024:.1f} MiB read; WRITE_SIZE {w_kib:.0f} KiB -> "
+                     f"{w_kib * ws_ / 1024:.1f} MiB written; HBM bytes per launch {hbm} "
+                     f"({hbm / 2**20:.1f} MiB), algorithmic {alg} ({alg / 2**20:.1f} MiB), "
+                     f"ratio {hbm / alg:.2f}")
+    for k in sorted(fe):
+        if k.startswith(("gate_quant", "requant", "gather_cols")):
+            lines.append(f"{k} ({fe[k][1]} dispatches): FETCH {fe[k][0]:.0f} KiB -> "
+                         f"{fe[k][0] * rs / 1024:.1f} MiB read; WRITE {wr.get(k, (0, 0))[0]:.0f} "
+                         f"KiB -> {wr.get(k, (0, 0))[0] * ws_ / 1024:.1f} MiB written")
+    lines.append(f"gemm source sha256[:16]: {gemm_source_sha()}")
+    with open(out_json, "w") as f:
+        json.dump({"workloads": res, "gemm_source_sha": gemm_source_sha(),
+                   "note": "HBM bytes per mixq_gemm launch from rocprofv3 FETCH_SIZE/WRITE_SIZE, "
+                           f"scaled by a {nbytes >> 20} MiB copy"}, f, indent=1)
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def run_cpu_baseline(wl, target_s: float = 12.0):
     """The CPU oracle on a row sample of the workload: gate and quantization
     of the sampled tokens, the integer product against all N weight rows, and
@@ -539,11 +629,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (for scaling byte counters)")
+    ap.add_argument("--counters", action="store_true",
+                    help="byte-counter pass: the calibration copy, then --steps whole steps "
+                         "of each counter workload and nothing else")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "OUT_TXT"),
+                    help="write the GEMM's HBM bytes per launch from two --counters passes")
     ap.add_argument("--all", action="store_true",
                     help="also measure progressive INT4 and output-feature mixed precision")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the LLaMA shapes, the INT4 prefill and the decode sequence")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -553,8 +652,13 @@ def main():
 
     from mixed_precision_quantized_amax_amd import workloads
     wl = workloads.WORKLOADS[args.workload]
-    if args.copy_calibration:
+    if args.copy_calibration or args.counters:
         copy_calibration()
+    if args.counters:
+        for name in COUNTER_WORKLOADS:
+            r = run_gpu(workloads.WORKLOADS[name], args.steps, args.warmup, counters=True)
+            log(f"[bench] counters {name}: {args.steps} steps, {r['ms_step']:.4f} ms/step")
+        return
     if wl.steps > 1:
         d = run_decode_sequence(wl)
         tops = wl.ops / (d["ms_step"] / 1e3) / 1e12

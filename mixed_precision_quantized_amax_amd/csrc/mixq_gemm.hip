@@ -875,6 +875,13 @@ void gemm_kernel(GemmArgs a) {
                     acc[i][j][4 * q + r] =
                         __float_as_int(((float)acc[i][j][4 * q + r] * sxe[r]) * swj);
             }
+            // 256 x 256 tiles: the accumulators fill the 256 AGPRs; left to
+            // itself the allocator moves the scaled tile into VGPRs, which
+            // do not hold it beside the epilogue's other values, and spills
+            // (200-400 bytes per lane, written to HBM).  Keeping each scaled
+            // fragment in AGPRs (the outlier MFMAs read and write them there,
+            // the stores take them from there) leaves no spill.
+            if constexpr (C::kFM * C::kFN * 16 == 256) asm volatile("" : "+a"(acc[i][j]));
         }
     }
 

@@ -48,3 +48,39 @@ def test_cpu_baseline_record():
     assert r["kind"] == "oracle" and r["unit"] == "TOPS"
     assert r["value"] > 0 and r["cores"] >= 1
     assert "tokens" in r["sample"]
+
+
+def _counter_csv(path, counter, rows):
+    cols = ["Correlation_Id", "Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name",
+            "Counter_Value"]
+    lines = [",".join(cols)]
+    for i, (name, v) in enumerate(rows):
+        lines.append(f'{i},{i},256,"{name}",{counter},{v}')
+    path.write_text("\n".join(lines) + "\n")
+
+
+def test_traffic_summary_scales_by_the_copy(tmp_path):
+    """Counters in KiB per dispatch, scaled so the 256 MiB calibration copy
+    reads and writes 256 MiB: a copy that reads 128 Ki 'KiB' gives a read
+    scale of 2; the GEMM's bytes are averaged over its dispatches."""
+    ns = "void mixq::(anonymous namespace)::"
+    g8 = ns + "gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>(mixq::GemmArgs)"
+    g4 = ns + "gemm_kernel<256, 256, 2, 2, 4, 2, 4, false, false, false>(mixq::GemmArgs)"
+    cp = "__amd_rocclr_copyBuffer"
+    fe, wr = tmp_path / "f.csv", tmp_path / "w.csv"
+    # three calibration copies first; a later (smaller) copy is not one of them
+    _counter_csv(fe, "FETCH_SIZE", [(cp, 131072)] * 3 + [(cp, 50), (g8, 100000), (g8, 102000),
+                                    (g4, 80000), (ns + "gate_quant_kernel<4, 4, false, false>"
+                                                  "(mixq::ActArgs)", 16000)])
+    _counter_csv(wr, "WRITE_SIZE", [(cp, 262144)] * 3 + [(cp, 9), (g8, 65536), (g8, 65536),
+                                    (g4, 65536)])
+    oj, ot = tmp_path / "t.json", tmp_path / "t.txt"
+    bench.traffic_summary(str(fe), str(wr), str(oj), str(ot))
+    t = json.loads(oj.read_text())
+    assert t["gemm_source_sha"] == bench.gemm_source_sha()
+    w8 = t["workloads"]["prefill_w8"]
+    assert w8["read_scale"] == 2.0 and w8["write_scale"] == 1.0 and w8["dispatches"] == 2
+    assert w8["hbm_bytes_per_launch"] == 101000 * 1024 * 2 + 65536 * 1024
+    assert t["workloads"]["prefill_w4"]["hbm_bytes_per_launch"] == 80000 * 2048 + 65536 * 1024
+    assert "gate_quant_kernel<4, 4, false, false> (1 dispatches)" in ot.read_text()
+    assert bench.kernel_short_name(g8) == "gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>"
