@@ -11,7 +11,9 @@ Cache cannot serve them from one step to the next.
 
 Prints one JSON line.  ``value`` is the step throughput in effective TOPS
 (2*M*N*K per step, outliers counted once).  ``roofline`` reports the GEMM
-kernel, timed with HIP events around each launch on its stream.
+kernel, timed with HIP events on its stream: one event pair around each of
+100 launches (median, spread) and one around the same launches back to back
+(``gemm_us``, without the per-launch event overhead).
 ``cpu_baseline`` times the CPU oracle on a bounded row sample of the same
 workload (only with --gpus 1, on rank 0).
 """
@@ -47,7 +49,11 @@ def log(*a):
 
 def launch_times(stream, n: int, fn) -> dict:
     """Durations (us) of n launches of fn, each bracketed by its own HIP
-    event pair on the launch stream: median, mean, min and 90th percentile."""
+    event pair on the launch stream: median, mean, min and 90th percentile.
+    Then the same n launches back to back between one event pair:
+    batch_us, their mean duration without the per-launch event overhead
+    (the recording of an event pair adds a few microseconds to the time
+    between them)."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]
@@ -58,34 +64,41 @@ def launch_times(stream, n: int, fn) -> dict:
         e1.record(stream)
     torch.cuda.synchronize()
     t = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
+    b0, b1 = evs[0]
+    b0.record(stream)
+    for i in range(n):
+        fn(i)
+    b1.record(stream)
+    torch.cuda.synchronize()
     return {"median_us": round(float(np.median(t)), 2), "mean_us": round(float(t.mean()), 2),
             "min_us": round(float(t.min()), 2), "p90_us": round(float(np.percentile(t, 90)), 2),
-            "launches": n}
+            "launches": n, "batch_us": round(b0.elapsed_time(b1) * 1e3 / n, 2)}
 
 
-def clock_of(stream, fn, n: int = 30) -> dict:
+def clock_buffer():
+    """Device buffer for mixq_set_clock_record: four int64 stamps per block."""
+    import torch
+    return torch.zeros(4 * 4096, dtype=torch.int64, device="cuda")
+
+
+def clock_summary(buf, event_us=None) -> dict:
     """Engine clock of the GEMM kernel itself: its blocks record the shader
     clock (s_memtime) and the 100 MHz real-time counter at entry and exit
     (mixq_set_clock_record); the clock of a block is the ratio of the two
-    deltas.  Median and range over the blocks of the last of n launches."""
-    import torch
-    from mixed_precision_quantized_amax_amd import mixq
-    buf = torch.zeros(4 * 4096, dtype=torch.int64, device="cuda")
-    mixq.set_clock_record(buf)
-    try:
-        for i in range(n):
-            fn(i)
-        torch.cuda.synchronize()
-    finally:
-        mixq.set_clock_record(None)
+    deltas.  The buffer holds the last recorded launch: median and range
+    over its blocks, the block duration, and the launch's span (first entry
+    to last exit), which must not exceed its event-timed duration."""
     c = buf.view(-1, 4).cpu().numpy()
     c = c[c[:, 3] > c[:, 2]]
     f = (c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6) / 1e9
     span_us = (c[:, 3].max() - c[:, 2].min()) / 100.0
-    return {"ghz_median": round(float(np.median(f)), 3), "ghz_min": round(float(f.min()), 3),
-            "ghz_max": round(float(f.max()), 3), "blocks": int(c.shape[0]),
-            "block_us_median": round(float(np.median(c[:, 3] - c[:, 2])) / 100.0, 2),
-            "kernel_span_us": round(float(span_us), 2)}
+    out = {"ghz_median": round(float(np.median(f)), 3), "ghz_min": round(float(f.min()), 3),
+           "ghz_max": round(float(f.max()), 3), "blocks": int(c.shape[0]),
+           "block_us_median": round(float(np.median(c[:, 3] - c[:, 2])) / 100.0, 2),
+           "kernel_span_us": round(float(span_us), 2)}
+    if event_us is not None:
+        out["event_us_same_launches"] = event_us
+    return out
 
 
 def gemm_source_sha() -> str:
@@ -202,13 +215,19 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0, counters: bool = False)
     # GEMM kernel duration, one event pair around each launch on its stream:
     # clean cache (the copies rotate, as in the steps) and hot (one copy)
     nl = max(50, steps)
-    gemm_clean = launch_times(stream, nl, lambda i: steps_c[i % copies].gemm())
+    # the clean-cache launches also record the engine clock (the stamps of
+    # the last one remain), so that clock and duration come from the same
+    # launches
+    cbuf = clock_buffer()
+    mixq.set_clock_record(cbuf)
+    try:
+        gemm_clean = launch_times(stream, nl, lambda i: steps_c[i % copies].gemm())
+    finally:
+        mixq.set_clock_record(None)
+    clk = clock_summary(cbuf, gemm_clean["batch_us"])
     gemm_hot = launch_times(stream, nl, lambda i: steps_c[0].gemm())
     act_t = launch_times(stream, nl, lambda i: steps_c[i % copies].act())
     act_u = launch_times(stream, nl, lambda i: steps_u[i % copies].act())
-    # engine clock of the GEMM itself: each block's shader-clock and 100 MHz
-    # real-time stamps at entry and exit, over the last of 30 clean launches
-    clk = clock_of(stream, lambda i: steps_c[i % copies].gemm())
     flag = int(state.flag.cpu()[0])
     return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm=gemm_clean, gemm_hot=gemm_hot,
                 act=act_t, act_separate=act_u, clock=clk, count=count, flag=flag,
@@ -631,7 +650,7 @@ def main():
                     help="also run a 256 MiB device copy (for scaling byte counters)")
     ap.add_argument("--counters", action="store_true",
                     help="byte-counter pass: the calibration copy, then --steps whole steps "
-                         "of each counter workload and nothing else")
+                         "of each counter workload, then the fused RMSNorm passes")
     ap.add_argument("--traffic-summary", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "OUT_TXT"),
                     help="write the GEMM's HBM bytes per launch from two --counters passes")
@@ -658,6 +677,9 @@ def main():
         for name in COUNTER_WORKLOADS:
             r = run_gpu(workloads.WORKLOADS[name], args.steps, args.warmup, counters=True)
             log(f"[bench] counters {name}: {args.steps} steps, {r['ms_step']:.4f} ms/step")
+        # the fused RMSNorm and residual-add passes at the headline shape
+        run_fused_norm(workloads.WORKLOADS[COUNTER_WORKLOADS[0]], args.steps, args.warmup)
+        log("[bench] counters: fused RMSNorm passes done")
         return
     if wl.steps > 1:
         d = run_decode_sequence(wl)
@@ -673,7 +695,7 @@ def main():
     ops = wl.ops
     value = ops / (r["ms_step"] / 1e3) / 1e12
     g = r["gemm"]
-    gemm_tops = ops / (g["mean_us"] / 1e6) / 1e12
+    gemm_tops = ops / (g["batch_us"] / 1e6) / 1e12
     alg_bytes = algorithmic_bytes(wl, r["count"])
     traffic = gemm_traffic(wl.name)
     clk = r["clock"]
@@ -702,14 +724,14 @@ def main():
                    "threshold": wl.tau, "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * value / PEAK_I8_TOPS, 2),
         "gemm_tops": round(gemm_tops, 2),
-        "gemm_us": g["mean_us"],
+        "gemm_us": g["batch_us"],
         "gemm_us_median": g["median_us"],
         "gemm_launches": g,
-        "gemm_hot_cache": dict(r["gemm_hot"], tops=round(ops / (r["gemm_hot"]["mean_us"] / 1e6)
+        "gemm_hot_cache": dict(r["gemm_hot"], tops=round(ops / (r["gemm_hot"]["batch_us"] / 1e6)
                                                          / 1e12, 2)),
-        "act_quant_us": r["act"]["mean_us"],
+        "act_quant_us": r["act"]["batch_us"],
         "act_quant": dict(r["act"], calls="mixq_quantize_act_regather (gate + re-quantize/regather)",
-                          separate_calls_mean_us=r["act_separate"]["mean_us"]),
+                          separate_calls_batch_us=r["act_separate"]["batch_us"]),
         "engine_clock": dict(clk, pct_of_measured_clock_peak=round(
             100.0 * gemm_tops / (PEAK_I8_TOPS * clk["ghz_median"] / PEAK_CLOCK_GHZ), 2)),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_I8_TOPS,
@@ -719,7 +741,7 @@ def main():
                                        "(L2 to fabric: HBM plus Infinity Cache hits), scaled by "
                                        "a copy of known size",
                      "t_roof_us": round(t_roof_us, 2),
-                     "frac_mixed": round(t_roof_us / g["mean_us"], 4),
+                     "frac_mixed": round(t_roof_us / g["batch_us"], 4),
                      "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
     }
     out["fused_rmsnorm_act"] = run_fused_norm(wl, args.steps, min(args.warmup, 50))
@@ -730,20 +752,20 @@ def main():
             w2 = workloads.WORKLOADS[name]
             r2 = run_gpu(w2, max(20, args.steps // 2), min(args.warmup, 100))
             others[name] = {"step_tops": round(w2.ops / (r2["ms_step"] / 1e3) / 1e12, 1),
-                            "gemm_tops": round(w2.ops / (r2["gemm"]["mean_us"] / 1e6) / 1e12, 1),
-                            "gemm_us": r2["gemm"]["mean_us"],
+                            "gemm_tops": round(w2.ops / (r2["gemm"]["batch_us"] / 1e6) / 1e12, 1),
+                            "gemm_us": r2["gemm"]["batch_us"],
                             "gemm_us_median": r2["gemm"]["median_us"],
-                            "gemm_hot_us": r2["gemm_hot"]["mean_us"],
-                            "act_quant_us": r2["act"]["mean_us"],
+                            "gemm_hot_us": r2["gemm_hot"]["batch_us"],
+                            "act_quant_us": r2["act"]["batch_us"],
                             "engine_clock_ghz": r2["clock"]["ghz_median"],
                             "ms_per_step": round(r2["ms_step"], 4)}
         dwl = workloads.WORKLOADS["decode_seq"]
         d = run_decode_sequence(dwl)
         others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),
                                 "ms_per_step": round(d["ms_step"], 4),
-                                "gemm_us": d["gemm"]["mean_us"],
+                                "gemm_us": d["gemm"]["batch_us"],
                                 "gemm_us_median": d["gemm"]["median_us"],
-                                "act_quant_us": d["act"]["mean_us"],
+                                "act_quant_us": d["act"]["batch_us"],
                                 "fired_steps": d["fired"], "gate_firings": len(d["fired"]),
                                 "outlier_channels_final": d["count"]}
     if args.all:
@@ -751,9 +773,9 @@ def main():
         r4 = run_gpu(w4, max(10, args.steps // 2), args.warmup, group=128)
         others["prefill_w4_progressive"] = {
             "step_tops": round(w4.ops / (r4["ms_step"] / 1e3) / 1e12, 1),
-            "gemm_tops": round(w4.ops / (r4["gemm"]["mean_us"] / 1e6) / 1e12, 1),
-            "gemm_us": r4["gemm"]["mean_us"],
-            "act_quant_us": r4["act"]["mean_us"],
+            "gemm_tops": round(w4.ops / (r4["gemm"]["batch_us"] / 1e6) / 1e12, 1),
+            "gemm_us": r4["gemm"]["batch_us"],
+            "act_quant_us": r4["act"]["batch_us"],
             "ms_per_step": round(r4["ms_step"], 4),
             "weights": "progressive group-wise INT4, groups of 128 (rebuilt to INT8 in the loader)"}
         sal = workloads.make_salient(w4.N)
