@@ -406,8 +406,10 @@ int mixq_gemm_ws(const int8_t *Xq, const float *s_x, const uint16_t *X_out,
  *   Y[m, j] = fp16( silu(g) * u ),  silu(g) = g / (1 + e^-g),
  * where g and u are the layer outputs (dequantized integer product plus
  * outlier product, in fp32) of gate row j and up row j -- the same values
- * MIXQ_OUT_F32 writes, taken in pairs in the epilogue.  The fp32 gate and up
- * outputs never reach memory.
+ * MIXQ_OUT_F32 writes, taken in pairs in the epilogue.  silu is evaluated in
+ * fp32 with the hardware exponential and reciprocal, whose error is far
+ * below the fp16 rounding that follows.  The fp32 gate and up outputs never
+ * reach memory.
  *
  *   Y         MIXQ_OUT_F32: fp32 [M, ldy], ldy >= N.
  *             MIXQ_OUT_F16 / MIXQ_OUT_BF16: fp16 / bf16 [M, ldy], ldy >= N.

@@ -127,6 +127,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 #define MIXQ_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt((((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8)))
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor as four dwords (base, stride 0, size in bytes, the
+// flags make_rsrc uses), for loads issued from inline assembly.
+__device__ __forceinline__ v4u rsrc_words(const void* base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const unsigned n = bytes > 0x7FFFFFFF ? 0x7FFFFFFFu : (unsigned)bytes;
+    return v4u{(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, n, 0x00020000u};
+}
+
+// One 16-byte-per-lane load straight into LDS (lane l's bytes at lds + 16 l),
+// issued from inline assembly so that the compiler's wait insertion does not
+// see it (inside a loop it cannot tell such a transfer's target from the
+// buffers the loop reads, and would wait for it before every LDS read).  The
+// caller waits for it with the vector-memory counter before reading the
+// target, and keeps every wave from leaving with it in flight.  No register
+// receives data; the offset, descriptor and LDS address (M0: one wait state
+// before the load, restored after it) are read when the instruction issues.
+__device__ __forceinline__ void lds_load16(const v4u& rsrc, uint32_t lds, int voff, int soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+
 // Scheduling pattern for one pipelined tile: the first MFMAs each followed by
 // an LDS write or a global load (so the loads issue early and have the whole
 // tile to land), the next ones each followed by LDS reads of the next tile's
@@ -208,6 +239,12 @@ void gemm_kernel(GemmArgs a) {
     const int wm = wave / WN, wn = wave % WN;
     // size of the outlier set (read once, long before the epilogue needs it)
     const int count = *a.count;
+    const int nchunks = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN;  // 32 columns each
+    const int ldb = a.ld_out * 2;  // bytes per outlier row
+    // Outlier chunks already in flight when the epilogue starts (K-pair
+    // kernels load the first two into the pair buffer the K loop frees
+    // first), and that buffer (0: stage arrays 0 and 1, 1: arrays 2 and 3).
+    int pre = 0, cf = 0;
     int64_t clk_t0 = 0, clk_r0 = 0;
     if (a.clk) {
         clk_t0 = (int64_t)__builtin_amdgcn_s_memtime();
@@ -515,6 +552,32 @@ void gemm_kernel(GemmArgs a) {
                 sched_interleave<2 * C::kFM * C::kFN, 2 * (C::kFM + C::kFN), kPI, kPI>();
             }
         }
+        // Outlier chunk j (j < 2) of both tiles into array j of pair buffer
+        // b, laid out as the epilogue's stage arrays (a 64-byte K tile: row
+        // r's 16-byte piece q at slot q ^ swz(r)).
+        auto prefetch_outliers = [&](int b, int nch) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+            const v4u wXo = rsrc_words(reinterpret_cast<const uint8_t*>(a.X_out) + (int64_t)m0 * ldb,
+                                       (int64_t)rows_a * ldb);
+            const v4u wWo = rsrc_words(reinterpret_cast<const uint8_t*>(a.w_out) + (int64_t)n0 * ldb,
+                                       (int64_t)rows_b * ldb);
+            for (int j = 0; j < nch; ++j) {
+                const uint32_t stg = (uint32_t)(uintptr_t)(lds_ptr_t)(j == 0 ? PA(b) : PB(b));
+#pragma unroll
+                for (int i = 0; i < C::kAI; ++i) {
+                    const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+                    lds_load16(wXo, stg + ((i * C::kNW + wave) * 16) * kBK,
+                               row * ldb + (((lane & 3) ^ swz(row)) << 4), j * kBK);
+                }
+#pragma unroll
+                for (int i = 0; i < C::kBI; ++i) {
+                    const int row = (i * C::kNW + wave) * 16 + (lane >> 2);
+                    lds_load16(wWo, stg + BM * kBK + ((i * C::kNW + wave) * 16) * kBK,
+                               row * ldb + (((lane & 3) ^ swz(row)) << 4), j * kBK);
+                }
+            }
+#endif
+        };
         // last pairs
         for (; p < KP; ++p) {
             const int c = p & 1, n = c ^ 1;
@@ -523,6 +586,16 @@ void gemm_kernel(GemmArgs a) {
             if (p + 1 < KP) lstore(SB, PB(n));
             if (p + 2 < KP) gload(rB, p + 2, SB);
             __syncthreads();
+            if (p == KP - 2 && a.ksplit == 1 && nchunks > 0) {
+                // Pair p's buffer is free from here on (this phase read its
+                // last fragments, and no later pair is stored into it): the
+                // first outlier chunks load into it while the last one and a
+                // half pairs multiply, instead of after the loop.  The
+                // epilogue waits for them with its other outlier loads.
+                pre = min(2, nchunks);
+                cf = c;
+                prefetch_outliers(c, pre);
+            }
             if (p + 1 < KP) lread(PA(n), PB(n), 0, fa0, fb0);
             mfmas(fa1, fb1);
             if (p + 2 < KP) lstore(SA, PA(c));
@@ -808,9 +881,12 @@ void gemm_kernel(GemmArgs a) {
     //     the last round each finished fragment is stored at once, so that its
     //     stores drain while the next fragment's MFMAs run.
     constexpr int kRC = STAGES == 4 ? 4 : 2;  // outlier chunks per round (one per stage array)
-    const int nchunks = (count + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN;
-    auto stage = [&](int c) __attribute__((always_inline)) -> uint8_t* { return c == 0 ? sS0 : c == 1 ? sS1 : c == 2 ? sS2 : sS3; };
-    const int ldb = a.ld_out * 2;  // bytes per outlier row
+    // chunk c of a round in stage array (c + 2 cf) mod 4: the prefetched
+    // chunks 0 and 1 sit in the pair buffer the K loop freed first
+    auto stage = [&](int c) __attribute__((always_inline)) -> uint8_t* {
+        const int k = (c + 2 * cf) & 3;
+        return k == 0 ? sS0 : k == 1 ? sS1 : k == 2 ? sS2 : sS3;
+    };
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t rXo =
         make_rsrc(reinterpret_cast<const uint8_t*>(a.X_out) + (int64_t)m0 * ldb,
                   nchunks > 0 ? (int64_t)rows_a * ldb : 0);
@@ -819,11 +895,11 @@ void gemm_kernel(GemmArgs a) {
                   nchunks > 0 ? (int64_t)rows_b * ldb : 0);
     // chunk c0 + c of both tiles into stage array c, laid out like a 64-byte
     // K tile: row r's 16-byte piece p at slot p ^ swz(r)
-    auto load_round = [&](int c0, int nch) __attribute__((always_inline)) {
+    auto load_round = [&](int c0, int nch, int skip) __attribute__((always_inline)) {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
         for (int c = 0; c < kRC; ++c) {
-            if (c < nch) {
+            if (c >= skip && c < nch) {
                 uint8_t* stg = stage(c);
 #pragma unroll
                 for (int i = 0; i < C::kAI; ++i) {
@@ -843,7 +919,7 @@ void gemm_kernel(GemmArgs a) {
         }
 #endif
     };
-    if (nchunks > 0) load_round(0, min(kRC, nchunks));
+    if (nchunks > 0) load_round(0, min(kRC, nchunks), pre);
 
     if constexpr (DEBUG) {
 #pragma unroll
@@ -890,7 +966,7 @@ void gemm_kernel(GemmArgs a) {
         const int nch = min(kRC, nchunks - c0);
         if (c0 > 0) {
             __syncthreads();  // every wave is done with the previous round's tiles
-            load_round(c0, nch);
+            load_round(c0, nch, 0);
         }
         MIXQ_WAIT_VMCNT(0);
         __syncthreads();
@@ -938,6 +1014,41 @@ void gemm_kernel(GemmArgs a) {
         // A gated weight interleaves 32-row blocks of gate and up rows, and
         // every wave's column range is a multiple of 64, so fragments 2jj and
         // 2jj+1 of a lane hold gate and up of the same (token, output) pairs.
+        auto swiglu16 = [&](int32_t gb, int32_t ub) __attribute__((always_inline)) -> uint32_t {
+            const float g = __int_as_float(gb);
+            const float u = __int_as_float(ub);
+            // silu(g) = g / (1 + e^-g), with the hardware reciprocal (1 ulp)
+            // in place of an IEEE division: the result is rounded to fp16
+            // (2^-11 relative) right after.  g -> -inf: e^-g = inf, rcp = 0.
+            const float y = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+            return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)y);
+        };
+        if (rows_a == BM && n0 + BN <= a.N &&
+            ((reinterpret_cast<uintptr_t>(a.Y) | (uintptr_t)ldyb) & 3) == 0) {
+            // a whole tile: two outputs per 4-byte store, as the 16-bit
+            // output modes below (adjacent lanes swap one value)
+            const bool odd = fr & 1;
+            const int voff = (4 * fh + (odd ? 1 : 0)) * ldyb +
+                             ((n0 + wn * C::kWTN) / 2 + fr - (odd ? 1 : 0)) * 2;
+#pragma unroll
+            for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < C::kFN / 2; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 16; e += 2) {
+                        const uint32_t h0 = swiglu16(acc[i][2 * jj][e], acc[i][2 * jj + 1][e]);
+                        const uint32_t h1 =
+                            swiglu16(acc[i][2 * jj][e + 1], acc[i][2 * jj + 1][e + 1]);
+                        const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp(
+                            (int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, false);
+                        const uint32_t w = odd ? (got | (h1 << 16)) : (h0 | (got << 16));
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            w, rY, voff + jj * 64,
+                            (wm * C::kWTM + i * 32 + 8 * (e >> 2) + (e & 3)) * ldyb, 0);
+                    }
+            clk_end();
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
@@ -949,13 +1060,10 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int rl = r0 + 8 * (e >> 2) + (e & 3);
-                        const float g = __int_as_float(acc[i][2 * jj][e]);
-                        const float u = __int_as_float(acc[i][2 * jj + 1][e]);
-                        const float y = g / (1.0f + __expf(-g)) * u;
                         if (rl < rows_a)
                             __builtin_amdgcn_raw_buffer_store_b16(
-                                __builtin_bit_cast(unsigned short, (_Float16)y), rY,
-                                rl * ldyb + oc * 2, 0, 0);
+                                (unsigned short)swiglu16(acc[i][2 * jj][e], acc[i][2 * jj + 1][e]),
+                                rY, rl * ldyb + oc * 2, 0, 0);
                     }
                 }
             }
@@ -979,6 +1087,44 @@ void gemm_kernel(GemmArgs a) {
         return;
     }
     const bool bf16 = a.out_mode == MIXQ_OUT_BF16;
+    // 16-bit value of an fp32 output: round to nearest, ties to even
+    auto to16 = [&](int32_t v) __attribute__((always_inline)) -> uint32_t {
+        const float y = __int_as_float(v);
+        const uint32_t u = __float_as_uint(y);
+        return bf16 ? (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16
+                    : (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)y);
+    };
+    if (!ROWS && esz == 2 && rows_a == BM && n0 + BN <= a.N &&
+        ((reinterpret_cast<uintptr_t>(a.Y) | (uintptr_t)ldyb) & 3) == 0) {
+        // A whole tile of 16-bit outputs, two per 4-byte store: 2-byte
+        // stores (one value per lane) took 15 us longer than the fp32 tile
+        // at the prefill shape, half the bytes notwithstanding.  Lanes 2k
+        // and 2k+1 hold columns 2k and 2k+1 of the same rows; for each pair
+        // of rows (r, r+1) of a fragment the even lane takes its partner's
+        // row-r value and stores row r, columns 2k..2k+1, the odd lane takes
+        // its partner's row-(r+1) value and stores row r+1 (one DPP swap of
+        // adjacent lanes per pair).  Y and its row stride 4-byte aligned.
+        const bool odd = fr & 1;
+        const int voff = (4 * fh + (odd ? 1 : 0)) * ldyb + (n0 + wn * C::kWTN + fr - (odd ? 1 : 0)) * 2;
+#pragma unroll
+        for (int i = 0; i < C::kFM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kFN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; e += 2) {
+                    const uint32_t h0 = to16(acc[i][j][e]);      // row r
+                    const uint32_t h1 = to16(acc[i][j][e + 1]);  // row r + 1
+                    // quad_perm [1, 0, 3, 2]: swap with the adjacent lane
+                    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp(
+                        (int)(odd ? h0 : h1), 0xB1, 0xF, 0xF, false);
+                    const uint32_t w = odd ? (got | (h1 << 16)) : (h0 | (got << 16));
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        w, rY, voff + j * 64,
+                        (wm * C::kWTM + i * 32 + 8 * (e >> 2) + (e & 3)) * ldyb, 0);
+                }
+        clk_end();
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < C::kFM; ++i)
 #pragma unroll
@@ -1001,14 +1147,8 @@ void gemm_kernel(GemmArgs a) {
                             __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][e], rY,
                                                                   rl * ldyb + ycol * 4, 0, 0);
                         } else {
-                            // 16-bit output: round to nearest, ties to even
-                            const float y = __int_as_float(acc[i][j][e]);
-                            const uint32_t u = __float_as_uint(y);
-                            const unsigned short h =
-                                bf16 ? (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16)
-                                     : __builtin_bit_cast(unsigned short, (_Float16)y);
-                            __builtin_amdgcn_raw_buffer_store_b16(h, rY, rl * ldyb + ycol * 2, 0,
-                                                                  0);
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                (unsigned short)to16(acc[i][j][e]), rY, rl * ldyb + ycol * 2, 0, 0);
                         }
                     }
                 }

@@ -70,6 +70,31 @@ def test_out16_llama7b_up(orc, kind):
     check16(orc, workloads.make_activation(wl), workloads.make_weight(wl), 8, kind, "llama7b_up")
 
 
+@pytest.mark.parametrize("kind", list(KINDS))
+def test_out16_prefill(orc, kind):
+    """The headline shape (256 x 256 tiles): whole tiles take the packed
+    two-values-per-store path."""
+    wl = workloads.WORKLOADS["prefill_w8"]
+    check16(orc, workloads.make_activation(wl), workloads.make_weight(wl), 8, kind, "prefill_w8")
+
+
+@pytest.mark.parametrize("kind", list(KINDS))
+def test_out16_odd_row_stride(orc, kind):
+    """A row stride of an odd number of 16-bit values: whole tiles cannot
+    take 4-byte stores and use the one-value path; the columns past N stay
+    untouched."""
+    M, K, N = 300, 1024, 256
+    mode, dt = KINDS[kind]
+    X, W, _ = workloads.random_case(seed=8, M=M, K=K, N=N, n_out=3)
+    g = GpuLayer(W, 8, 6.0, 64, M)
+    g.step(X)
+    Yw = torch.full((M, N + 41), 7.0, dtype=dt, device="cuda")
+    mixq.gemm_ex(g.Xq, g.s_x, g.X_out, g.state, g.pw, Yw[:, :N], mode, None, g.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Yw[:, :N].contiguous().view(torch.int16), g.Y.to(dt).view(torch.int16))
+    assert bool((Yw[:, N:] == 7.0).all())
+
+
 def test_out16_ldy_and_errors(orc):
     """A row stride above N leaves the columns past N untouched; a 16-bit
     output with a row-subset weight is refused."""
