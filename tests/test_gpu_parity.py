@@ -276,6 +276,25 @@ def test_split_k(orc, M, K, N, n_out):
     assert int(g.ws[:1024].abs().sum().cpu()) == 0, "tile counters not cleared"
 
 
+@pytest.mark.parametrize("tile", ["256x256_kpair", "128x128_kpair"], indirect=True)
+@pytest.mark.parametrize("M,K,N,n_out,k_cap", [
+    (300, 256, 520, 40, 64),     # two K pairs: the prefetch goes out in the first
+    (257, 384, 300, 70, 128),    # three pairs: the freed buffer is the second one
+    (130, 640, 260, 20, 64),     # five pairs, one outlier chunk
+    (96, 896, 384, 150, 256),    # seven pairs, five chunks: a second round
+])
+def test_outlier_prefetch(orc, tile, M, K, N, n_out, k_cap):
+    """The K-pair kernels load the first two outlier chunks during the last
+    K pairs into the pair buffer that frees first, which depends on the
+    parity of the pair count; the other chunks follow the loop, in later
+    rounds when there are more than four.  Unsplit launches (no workspace),
+    odd and even pair counts, one to five chunks: everything against the
+    oracle."""
+    X, W, _ = workloads.random_case(seed=K + n_out, M=M, K=K, N=N, n_out=n_out)
+    g = GpuLayer(W, 8, 6.0, k_cap, M, split=False)
+    full_compare(orc, X, W, 8, 6.0, k_cap, layer=g, tag=f"prefetch[{tile}] K={K} n_out={n_out}")
+
+
 def test_undersized_workspace_is_refused(orc):
     """A workspace that is given but smaller than the split needs is an
     explicit error (MIXQ_ERR_WORKSPACE) and enqueues nothing: Y keeps its
