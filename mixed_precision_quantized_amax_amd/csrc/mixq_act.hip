@@ -375,7 +375,11 @@ constexpr int kGateThreads = 256;
 // part must fit in registers (one segment: K <= 32768).
 // RES: before that, the residual add H = R + D (X is R), H written out; one
 // token buffer (R and D both in flight) instead of two.
-template <int CPT, int W, bool NORM, bool RES = false>
+// EXACT: K is exactly one segment (W * 64 * CPT chunks of 8 channels), so no
+// chunk of a row is out of range and no per-chunk test is compiled in (the
+// tests and their masked paths were the larger part of the pass's vector
+// instructions).
+template <int CPT, int W, bool NORM, bool RES = false, bool EXACT = false>
 __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     static_assert(!RES || NORM, "the residual add comes with the norm");
     constexpr int kRB = kGateThreads / kWave / W;  // tokens per block and round
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     const int wave = threadIdx.x / kWave;
     const int slot = wave / W, part = wave % W;
     const int seg_chunks = W * kWave * CPT;
-    const int nseg = (a.nchunks + seg_chunks - 1) / seg_chunks;
+    const int nseg = EXACT ? 1 : (a.nchunks + seg_chunks - 1) / seg_chunks;
     const int kpad = (set_size + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
     // first gather round: set member gj of each token (its channel id is
     // read once per block)
@@ -400,6 +404,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     const bool gset = a.ld_out && gj < set_size;
     const int gch = gset ? a.idx[gj] : 0;
     auto chunk = [&](int s, int i) { return s * seg_chunks + (part * CPT + i) * kWave + lane; };
+    auto in_range = [&](int c) __attribute__((always_inline)) { return EXACT || c < a.nchunks; };
     // gamma of this thread's first gather member (the rest of gamma is in LDS)
     const uint16_t ggam = (NORM && gset) ? a.gamma[gch] : 0;
     typedef uint4 XV[CPT];
@@ -411,8 +416,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = chunk(s, i);
-            xv[i] = (valid && c < a.nchunks) ? *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)
-                                             : make_uint4(0, 0, 0, 0);
+            xv[i] = (valid && in_range(c)) ? *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)
+                                           : make_uint4(0, 0, 0, 0);
         }
     };
     // the cached-set bits of the same chunks (from the bitmap staged in LDS)
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = chunk(s, i);
-            wv[i] = c < a.nchunks ? sbits[c >> 2] : 0u;
+            wv[i] = in_range(c) ? sbits[c >> 2] : 0u;
         }
     };
     auto load_seg = [&](int64_t row, int s, XV& xv, WV& wv) {
@@ -460,8 +465,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = chunk(0, i);
-            dv[i] = (valid && c < a.nchunks) ? *reinterpret_cast<const uint4*>(dr + (int64_t)c * 8)
-                                             : make_uint4(0, 0, 0, 0);
+            dv[i] = (valid && in_range(c)) ? *reinterpret_cast<const uint4*>(dr + (int64_t)c * 8)
+                                           : make_uint4(0, 0, 0, 0);
         }
         if (gset && valid) gd = dr[gch];
     };
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
             for (int i = 0; i < CPT; ++i) {
                 const int c = chunk(0, i);
                 xv[i] = hadd_chunk(xv[i], (*dv)[i]);
-                if (valid && c < a.nchunks) *reinterpret_cast<uint4*>(hr + (int64_t)c * 8) = xv[i];
+                if (valid && in_range(c)) *reinterpret_cast<uint4*>(hr + (int64_t)c * 8) = xv[i];
             }
             gval = (uint16_t)hadd2(gval, gd);
         }
@@ -504,7 +509,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 const int c = chunk(0, i);
-                if (c < a.nchunks)
+                if (in_range(c))
                     xv[i] = norm_chunk(xv[i], *reinterpret_cast<const uint4*>(sgam + c * 8), rn);
             }
             gval = norm1(gval, ggam, rn);
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
                     const int c = chunk(s, i);
-                    if (!valid || c >= a.nchunks) continue;
+                    if (!valid || !in_range(c)) continue;
                     const uint32_t cb = (wv[i] >> ((c & 3) * 8)) & 0xFFu;
                     uint32_t over = 0;
 #pragma unroll
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 const int c = chunk(s, i);
-                if (!valid || c >= a.nchunks) continue;
+                if (!valid || !in_range(c)) continue;
                 const uint4 kp = keep_of(i, c);
                 // cached channels become +0 and so get code 0
                 const uint32_t m[4] = {xv[i].x & kp.x, xv[i].y & kp.y, xv[i].z & kp.z,
@@ -811,8 +816,12 @@ int launch_act(const ActArgs& a, const GatherArgs& g, hipStream_t st) {
     const int64_t cap = RES ? 1024 : 2048;
     const int grid = (int)(g1 < cap ? g1 : cap);
     const size_t lds = (size_t)a.words * 8 + (NORM ? (size_t)a.K * 2 : 0);
-    hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES>), dim3(grid),
-                       dim3(kGateThreads), lds, st, a);
+    if (a.nchunks == CPT_G * kWave * kGateWaves)
+        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, true>), dim3(grid),
+                           dim3(kGateThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, false>), dim3(grid),
+                           dim3(kGateThreads), lds, st, a);
     int rc = launch_status();
     if (rc != MIXQ_OK) return rc;
     const int64_t rows_per_block = kReqThreads / kWave;
