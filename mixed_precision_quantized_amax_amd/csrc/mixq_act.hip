@@ -82,6 +82,16 @@ __device__ __forceinline__ void build_keep_lut(uint4* lut) {
 }
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over `bytes` bytes from base (raw, no stride): loads past
+// the end read zeros, stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes,
+                                             0x00020000);
+}
 
 // Two 16-bit unsigned maxima in one packed integer operation.
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -379,8 +389,12 @@ constexpr int kGateThreads = 256;
 // chunk of a row is out of range and no per-chunk test is compiled in (the
 // tests and their masked paths were the larger part of the pass's vector
 // instructions).
-template <int CPT, int W, bool NORM, bool RES = false, bool EXACT = false>
+// ONE: the grid has a block for every token group, so each block takes one
+// group and needs one register set, not two (fewer registers, more waves per
+// SIMD).
+template <int CPT, int W, bool NORM, bool RES = false, bool EXACT = false, bool ONE = false>
 __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
+    static_assert(!(ONE && RES), "the residual variant keeps one register set anyway");
     static_assert(!RES || NORM, "the residual add comes with the norm");
     constexpr int kRB = kGateThreads / kWave / W;  // tokens per block and round
     extern __shared__ uint32_t dyn[];  // newbits[words], sbits[words], NORM: gamma[K]
@@ -410,14 +424,17 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     typedef uint4 XV[CPT];
     typedef uint32_t WV[CPT];
     // X chunks of one segment of a token's part (global loads only)
+    // (buffer loads: a row past M or a chunk past K reads zeros through the
+    // descriptor's range, and the per-lane offsets are 32-bit)
     auto load_x = [&](int64_t row, int s, XV& xv) {
         const bool valid = row < a.M;
-        const uint16_t* xr = a.X + (valid ? row : 0) * a.ldx;
+        const __amdgpu_buffer_rsrc_t rx =
+            row_rsrc(a.X + (valid ? row : 0) * a.ldx, valid ? (int64_t)a.K * 2 : 0);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = chunk(s, i);
-            xv[i] = (valid && in_range(c)) ? *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8)
-                                           : make_uint4(0, 0, 0, 0);
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, c * 16, 0, 0);
+            xv[i] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
     // the cached-set bits of the same chunks (from the bitmap staged in LDS)
@@ -570,13 +587,15 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         }
         if (valid && part == 0 && lane == 0) a.s_x[row] = sc;
 
-        int8_t* qr = a.Xq + (valid ? row : 0) * (int64_t)a.K;
+        // codes: buffer stores, dropped past K or for a row past M
+        const __amdgpu_buffer_rsrc_t rq =
+            row_rsrc(a.Xq + (valid ? row : 0) * (int64_t)a.K, valid ? (int64_t)a.K : 0);
         for (int s = 0; s < nseg; ++s) {
             if (nseg > 1) load_seg(row, s, xv, wv);  // the part did not fit in registers
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 const int c = chunk(s, i);
-                if (!valid || !in_range(c)) continue;
+                if (!EXACT && !in_range(c)) continue;
                 const uint4 kp = keep_of(i, c);
                 // cached channels become +0 and so get code 0
                 const uint32_t m[4] = {xv[i].x & kp.x, xv[i].y & kp.y, xv[i].z & kp.z,
@@ -585,8 +604,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     u[e] = code_bits((uint16_t)(m[e >> 1] >> ((e & 1) * 16)), r);
-                *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) =
-                    make_uint2(pack4(u[0], u[1], u[2], u[3]), pack4(u[4], u[5], u[6], u[7]));
+                const v2u q = {pack4(u[0], u[1], u[2], u[3]), pack4(u[4], u[5], u[6], u[7])};
+                __builtin_amdgcn_raw_buffer_store_b64(q, rq, c * 8, 0, 0);
             }
         }
         if (orow) {
@@ -614,6 +633,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
             process(r0 + slot, xa, wa, ga, par, &da, gd);
             par ^= 1;
         }
+    } else if constexpr (ONE) {
+        if (r0 < a.M) process(r0 + slot, xa, wa, ga, 0, nullptr, 0);
     } else {
     for (; r0 < a.M; r0 += 2 * stride) {
         if (r0 + stride < a.M) load_row(r0 + stride + slot, xb, gb2);
@@ -816,12 +837,21 @@ int launch_act(const ActArgs& a, const GatherArgs& g, hipStream_t st) {
     const int64_t cap = RES ? 1024 : 2048;
     const int grid = (int)(g1 < cap ? g1 : cap);
     const size_t lds = (size_t)a.words * 8 + (NORM ? (size_t)a.K * 2 : 0);
-    if (a.nchunks == CPT_G * kWave * kGateWaves)
-        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, true>), dim3(grid),
-                           dim3(kGateThreads), lds, st, a);
+    const bool exact = a.nchunks == CPT_G * kWave * kGateWaves;
+    const bool one = !RES && g1 <= cap;  // a block per token group
+    const dim3 gd(grid), bd(kGateThreads);
+    if (exact && one)
+        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, true, !RES>), gd, bd,
+                           lds, st, a);
+    else if (exact)
+        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, true>), gd, bd, lds,
+                           st, a);
+    else if (one)
+        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, false, !RES>), gd, bd,
+                           lds, st, a);
     else
-        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, false>), dim3(grid),
-                           dim3(kGateThreads), lds, st, a);
+        hipLaunchKernelGGL((gate_quant_kernel<CPT_G, kGateWaves, NORM, RES, false>), gd, bd, lds,
+                           st, a);
     int rc = launch_status();
     if (rc != MIXQ_OK) return rc;
     const int64_t rows_per_block = kReqThreads / kWave;
