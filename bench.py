@@ -516,7 +516,9 @@ def copy_calibration(nbytes: int = 256 << 20):
     log(f"[bench] calibration copy: {nbytes} bytes, 3 times")
 
 
-COUNTER_WORKLOADS = ("prefill_w8", "prefill_w4")
+# counter passes, in this order: the GEMM dispatches of the run are
+# attributed to these workloads by dispatch order (equal consecutive blocks)
+COUNTER_WORKLOADS = ("prefill_w8", "prefill_w4", "llama7b_up", "llama70b_up", "decode_seq")
 
 
 def kernel_short_name(k: str) -> str:
@@ -529,9 +531,10 @@ def kernel_short_name(k: str) -> str:
     return head.split("::")[-1] + sep + tail
 
 
-def read_counter_csv(path: str, counter: str, n_calib: int = 3) -> dict:
-    """Mean value per dispatch of one counter, per kernel, from a rocprofv3
-    --pmc CSV (one row per dispatch and counter).  The first n_calib
+def read_counter_csv(path: str, counter: str, n_calib: int = 3):
+    """One counter from a rocprofv3 --pmc CSV (one row per dispatch and
+    counter): the mean value per dispatch of each kernel, and the GEMM
+    dispatches in dispatch order as (kernel, value).  The first n_calib
     dispatches of the run are the calibration copies, under the key 'copy'."""
     import csv
     rows = []
@@ -542,13 +545,33 @@ def read_counter_csv(path: str, counter: str, n_calib: int = 3) -> dict:
                              float(row["Counter_Value"])))
     rows.sort()
     vals = {}
+    gemms = []
     for i, (_, name, v) in enumerate(rows):
         if i < n_calib:
             if "copyBuffer" not in name:
                 raise SystemExit(f"dispatch {i} is {name}, not the calibration copy")
             name = "copy"
         vals.setdefault(name, []).append(v)
-    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+        if name.startswith("gemm_kernel"):
+            gemms.append((name, v))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}, gemms
+
+
+def gemm_blocks(gemms: list, names: tuple) -> dict:
+    """Split the GEMM dispatches of a counter run (in dispatch order) into one
+    equal block per counter workload, in the order the workloads ran; each
+    block must be one kernel (no workload here splits into two launches)."""
+    n = len(gemms) // len(names)
+    if n == 0 or n * len(names) != len(gemms):
+        raise SystemExit(f"{len(gemms)} GEMM dispatches for {len(names)} workloads")
+    out = {}
+    for i, name in enumerate(names):
+        blk = gemms[i * n:(i + 1) * n]
+        kerns = {k for k, _ in blk}
+        if len(kerns) != 1:
+            raise SystemExit(f"{name}: expected one GEMM kernel, found {sorted(kerns)}")
+        out[name] = (kerns.pop(), sum(v for _, v in blk) / n, n)
+    return out
 
 
 def traffic_summary(fetch_csv: str, write_csv: str, out_json: str, out_txt: str,
@@ -558,23 +581,24 @@ def traffic_summary(fetch_csv: str, write_csv: str, out_json: str, out_txt: str,
     are in KiB per dispatch; each is scaled so that the calibration copy
     (nbytes read, nbytes written) reads nbytes."""
     from mixed_precision_quantized_amax_amd import workloads
-    fe = read_counter_csv(fetch_csv, "FETCH_SIZE")
-    wr = read_counter_csv(write_csv, "WRITE_SIZE")
+    fe, fe_g = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    wr, wr_g = read_counter_csv(write_csv, "WRITE_SIZE")
     rs = nbytes / 1024.0 / fe["copy"][0]
     ws_ = nbytes / 1024.0 / wr["copy"][0]
-    gemms = sorted(k for k in fe if k.startswith("gemm_kernel"))
+    fb = gemm_blocks(fe_g, COUNTER_WORKLOADS)
+    wb = gemm_blocks(wr_g, COUNTER_WORKLOADS)
     lines = [f"calibration copy ({nbytes >> 20} MiB read + {nbytes >> 20} MiB written): "
              f"FETCH_SIZE {fe['copy'][0]:.0f} KiB, WRITE_SIZE {wr['copy'][0]:.0f} KiB",
              f"scale factors: read {rs:.4f}, write {ws_:.4f}"]
     res = {}
     for name in COUNTER_WORKLOADS:
         wl = workloads.WORKLOADS[name]
-        # INT8 weights: template BITS 8; INT4: 4 (the only GEMM of each pass)
-        kern = [k for k in gemms if re.match(rf"gemm_kernel<\d+, \d+, \d+, \d+, {wl.bits},", k)]
-        if len(kern) != 1:
-            raise SystemExit(f"{name}: expected one GEMM kernel, found {kern}")
-        f_kib, n = fe[kern[0]]
-        w_kib = wr[kern[0]][0]
+        kname, f_kib, n = fb[name]
+        w_kib = wb[name][1]
+        if wb[name][0] != kname or not re.match(rf"gemm_kernel<\d+, \d+, \d+, \d+, {wl.bits},",
+                                                kname):
+            raise SystemExit(f"{name}: kernels {kname} / {wb[name][0]} do not fit the workload")
+        kern = [kname]
         hbm = int(f_kib * 1024 * rs + w_kib * 1024 * ws_)
         alg = algorithmic_bytes(wl, wl.n_outliers)
         res[name] = {"hbm_bytes_per_launch": hbm, "fetch_kib": round(f_kib, 1),
@@ -758,7 +782,9 @@ def main():
                             "gemm_hot_us": r2["gemm_hot"]["batch_us"],
                             "act_quant_us": r2["act"]["batch_us"],
                             "engine_clock_ghz": r2["clock"]["ghz_median"],
-                            "ms_per_step": round(r2["ms_step"], 4)}
+                            "ms_per_step": round(r2["ms_step"], 4),
+                            "traffic": gemm_traffic(name),
+                            "algorithmic_bytes": algorithmic_bytes(w2, r2["count"])}
         dwl = workloads.WORKLOADS["decode_seq"]
         d = run_decode_sequence(dwl)
         others["decode_seq"] = {"step_tops": round(dwl.ops / (d["ms_step"] / 1e3) / 1e12, 1),
@@ -767,7 +793,9 @@ def main():
                                 "gemm_us_median": d["gemm"]["median_us"],
                                 "act_quant_us": d["act"]["batch_us"],
                                 "fired_steps": d["fired"], "gate_firings": len(d["fired"]),
-                                "outlier_channels_final": d["count"]}
+                                "outlier_channels_final": d["count"],
+                                "traffic": gemm_traffic("decode_seq"),
+                                "algorithmic_bytes": algorithmic_bytes(dwl, d["count"])}
     if args.all:
         w4 = workloads.WORKLOADS["prefill_w4"]
         r4 = run_gpu(w4, max(10, args.steps // 2), args.warmup, group=128)

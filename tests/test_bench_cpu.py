@@ -62,18 +62,26 @@ def _counter_csv(path, counter, rows):
 def test_traffic_summary_scales_by_the_copy(tmp_path):
     """Counters in KiB per dispatch, scaled so the 256 MiB calibration copy
     reads and writes 256 MiB: a copy that reads 128 Ki 'KiB' gives a read
-    scale of 2; the GEMM's bytes are averaged over its dispatches."""
+    scale of 2; the GEMM dispatches are split, in dispatch order, into one
+    equal block per counter workload, and each block's bytes are averaged."""
     ns = "void mixq::(anonymous namespace)::"
     g8 = ns + "gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>(mixq::GemmArgs)"
     g4 = ns + "gemm_kernel<256, 256, 2, 2, 4, 2, 4, false, false, false>(mixq::GemmArgs)"
+    g1 = ns + "gemm_kernel<128, 128, 2, 2, 8, 4, 5, false, false, false>(mixq::GemmArgs)"
+    gq = ns + "gate_quant_kernel<4, 4, false, false>(mixq::ActArgs)"
     cp = "__amd_rocclr_copyBuffer"
+    assert bench.COUNTER_WORKLOADS == ("prefill_w8", "prefill_w4", "llama7b_up", "llama70b_up",
+                                       "decode_seq")
+    # the workloads' GEMMs, two dispatches each, in the order they ran:
+    # llama70b_up reuses the prefill kernel, decode_seq llama7b_up's
+    f_g = [(g8, 100000), (g8, 102000), (g4, 80000), (g4, 80000), (g1, 38000), (g1, 38000),
+           (g8, 150000), (g8, 150000), (g1, 45000), (g1, 46000)]
+    w_g = [(g8, 65536), (g8, 65536), (g4, 65536), (g4, 65536), (g1, 22016), (g1, 22016),
+           (g8, 229376), (g8, 229376), (g1, 24000), (g1, 24000)]
     fe, wr = tmp_path / "f.csv", tmp_path / "w.csv"
     # three calibration copies first; a later (smaller) copy is not one of them
-    _counter_csv(fe, "FETCH_SIZE", [(cp, 131072)] * 3 + [(cp, 50), (g8, 100000), (g8, 102000),
-                                    (g4, 80000), (ns + "gate_quant_kernel<4, 4, false, false>"
-                                                  "(mixq::ActArgs)", 16000)])
-    _counter_csv(wr, "WRITE_SIZE", [(cp, 262144)] * 3 + [(cp, 9), (g8, 65536), (g8, 65536),
-                                    (g4, 65536)])
+    _counter_csv(fe, "FETCH_SIZE", [(cp, 131072)] * 3 + [(cp, 50), (gq, 16000)] + f_g)
+    _counter_csv(wr, "WRITE_SIZE", [(cp, 262144)] * 3 + [(cp, 9)] + w_g)
     oj, ot = tmp_path / "t.json", tmp_path / "t.txt"
     bench.traffic_summary(str(fe), str(wr), str(oj), str(ot))
     t = json.loads(oj.read_text())
@@ -82,5 +90,12 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert w8["read_scale"] == 2.0 and w8["write_scale"] == 1.0 and w8["dispatches"] == 2
     assert w8["hbm_bytes_per_launch"] == 101000 * 1024 * 2 + 65536 * 1024
     assert t["workloads"]["prefill_w4"]["hbm_bytes_per_launch"] == 80000 * 2048 + 65536 * 1024
+    assert t["workloads"]["llama70b_up"]["hbm_bytes_per_launch"] == 150000 * 2048 + 229376 * 1024
+    assert t["workloads"]["decode_seq"]["hbm_bytes_per_launch"] == 45500 * 2048 + 24000 * 1024
     assert "gate_quant_kernel<4, 4, false, false> (1 dispatches)" in ot.read_text()
     assert bench.kernel_short_name(g8) == "gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>"
+    # a block that mixes two kernels, or a count that does not divide, is refused
+    with pytest.raises(SystemExit):
+        bench.gemm_blocks([("a", 1), ("b", 1)], ("x",))
+    with pytest.raises(SystemExit):
+        bench.gemm_blocks([("a", 1)] * 3, ("x", "y"))
