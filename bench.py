@@ -101,6 +101,33 @@ def clock_summary(buf, event_us=None) -> dict:
     return out
 
 
+def run_mfma_probe(stream, a, b, iters: int = 128, blocks: int = 256, warmup: int = 100,
+                   n: int = 100) -> dict:
+    """The GEMM main loop's INT8 MFMA stream with no memory traffic
+    (mixq_mfma_probe) on the given operand bytes: blocks x 4 waves, iters
+    rounds of 32 MFMAs per wave.  At 256 blocks and 128 rounds it issues the
+    MFMAs of the 256 x 256 GEMM at M = 2048, K = N = 8192 (2 x 2048 x 8192 x
+    8192 ops), so its time is the GEMM's ceiling at the clock the board then
+    sustains.  Timed like the GEMM: n launches back to back, the engine clock
+    from the last one's blocks."""
+    import torch
+    from mixed_precision_quantized_amax_amd import mixq
+    a8 = a.reshape(-1).view(torch.int8)
+    b8 = b.reshape(-1).view(torch.int8)
+    out = torch.empty(256 * blocks, dtype=torch.int32, device=a.device)
+    clk = torch.zeros(4 * blocks, dtype=torch.int64, device=a.device)
+    s = stream.cuda_stream
+    for _ in range(warmup):
+        mixq.mfma_probe(a8, b8, iters, blocks, out, None, s)
+    t = launch_times(stream, n, lambda i: mixq.mfma_probe(a8, b8, iters, blocks, out, clk, s))
+    ops = blocks * 4 * iters * 32 * 2 * 32 * 32 * 32
+    tops = ops / (t["batch_us"] / 1e6) / 1e12
+    return {"tops": round(tops, 1), "pct_of_published_peak": round(100.0 * tops / PEAK_I8_TOPS, 2),
+            "us": t["batch_us"], "ops": ops, "blocks": blocks, "rounds": iters,
+            "engine_clock": clock_summary(clk, t["batch_us"]),
+            "operands": "the workload's own Xq and packed weight bytes"}
+
+
 def gemm_source_sha() -> str:
     with open(GEMM_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -128,9 +155,11 @@ def algorithmic_bytes(wl, k: int) -> int:
             + 2 * kp * (wl.M + wl.N) + 4 * wl.M * wl.N)
 
 
-def run_gpu(wl, steps: int, warmup: int, group: int = 0, counters: bool = False):
+def run_gpu(wl, steps: int, warmup: int, group: int = 0, counters: bool = False,
+            probe: bool = False):
     """group: 0, or the progressive INT4 group size (INT4 workloads).
-    counters: run the warmup and timed steps only (a byte-counter pass)."""
+    counters: run the warmup and timed steps only (a byte-counter pass).
+    probe: also run the matrix-core rate probe on the workload's operands."""
     import torch
     from mixed_precision_quantized_amax_amd import mixq, workloads
 
@@ -229,9 +258,10 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0, counters: bool = False)
     act_t = launch_times(stream, nl, lambda i: steps_c[i % copies].act())
     act_u = launch_times(stream, nl, lambda i: steps_u[i % copies].act())
     flag = int(state.flag.cpu()[0])
+    mprobe = run_mfma_probe(stream, Xq[0], packs[0].wq) if probe else None
     return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm=gemm_clean, gemm_hot=gemm_hot,
                 act=act_t, act_separate=act_u, clock=clk, count=count, flag=flag,
-                copies=copies)
+                copies=copies, probe=mprobe)
 
 
 def run_mixed(wl, steps: int, warmup: int, salient):
@@ -715,7 +745,7 @@ def main():
                           "config": {"workload": wl.description, "name": wl.name,
                                      "outlier_channels_final": d["count"]}}), flush=True)
         return
-    r = run_gpu(wl, args.steps, args.warmup)
+    r = run_gpu(wl, args.steps, args.warmup, probe=True)
     ops = wl.ops
     value = ops / (r["ms_step"] / 1e3) / 1e12
     g = r["gemm"]
@@ -768,6 +798,12 @@ def main():
                      "frac_mixed": round(t_roof_us / g["batch_us"], 4),
                      "kernel": "mixq_gemm (int8 MFMA main loop + fp16 outlier MFMAs + epilogue)"},
     }
+    if r["probe"] is not None:
+        # the same MFMA stream with no memory traffic, on the same operand
+        # bytes: the ceiling at the clock the board sustains for it
+        out["mfma_probe"] = r["probe"]
+        if r["probe"]["ops"] == ops:
+            out["roofline"]["frac_of_mfma_probe"] = round(gemm_tops / r["probe"]["tops"], 4)
     out["fused_rmsnorm_act"] = run_fused_norm(wl, args.steps, min(args.warmup, 50))
     out["swiglu_gate_up"] = run_swiglu(wl, max(20, args.steps // 2), min(args.warmup, 50))
     others = {}

@@ -492,6 +492,48 @@ int mixq_set_gemm_variant(int32_t variant);
  */
 int mixq_set_clock_record(int64_t *buf, int32_t n_blocks);
 
+/*
+ * mixq_mfma_probe -- measurement aid: the GEMM main loop's INT8 matrix-core
+ * stream with no memory traffic.  The MixQ article (section "MixQ的解决方案",
+ * Fig. 14) states its kernels' throughput against the hardware's peak; the
+ * published MI355X peak assumes the 2.4 GHz engine clock, which the board
+ * lowers under sustained matrix work by an amount that depends on the
+ * operand bits.  This call measures the matrix-core rate at the clock the
+ * board sustains, on given operand bytes (for instance a workload's own Xq
+ * and packed weight), as a ceiling the GEMM's memory traffic does not enter.
+ *
+ * Each of the blocks x 4 waves (one per SIMD) loads, per lane, eight
+ * 16-byte A operands and eight B operands once: operand q (q = 4 ks + i,
+ * ks in 0..1, i in 0..3) of wave g (g = 4 block + wave) is bytes
+ *   [((8 g + q) * 1024 + 16 lane) mod size, +16)
+ * of a (a_bytes) and of b (b_bytes).  It then runs `iters` rounds of 32
+ * v_mfma_i32_32x32x32_i8: for ks, for i, for j (0..3):
+ *   acc[i][j] += A(ks, i) B(ks, j)^T,
+ * where A(ks, i) is the 32 x 32 int8 matrix whose row r holds the operand
+ * bytes of lane r (k 0..15) then lane r + 32 (k 16..31), B(ks, j) likewise.
+ * acc[i][j] is a 32 x 32 int32 matrix; lane l holds column l % 32 and rows
+ * 8 (e / 4) + 4 (l / 32) + e % 4, e in 0..15.  out[256 b + t] receives,
+ * for thread t of block b, the sum of that lane's 256 accumulator values,
+ * in 32-bit wrapping arithmetic.
+ *
+ *   a, b      device memory, 16-byte aligned, of a_bytes / b_bytes bytes
+ *             (multiples of 16, at least 16)
+ *   iters     rounds (>= 1): 32 * iters MFMAs per wave; 128 rounds is the
+ *             MFMA count of one wave of the 256 x 256 GEMM at K = 8192
+ *   blocks    >= 1; one per compute unit (256 on MI355X) matches the GEMM
+ *   out       device int32 [256 * blocks]
+ *   clk       NULL, or device int64 [4 * blocks]: per block the shader-clock
+ *             counter (s_memtime) before and after the MFMA rounds, then the
+ *             100 MHz real-time counter (s_memrealtime) before and after
+ *   stream    hipStream_t (NULL = default stream)
+ * Errors: MIXQ_ERR_INVALID_ARG for null pointers, iters or blocks < 1, sizes
+ *         below 16 or not multiples of 16, or unaligned operands;
+ *         MIXQ_ERR_NO_DEVICE / MIXQ_ERR_UNSUPPORTED_DEVICE; MIXQ_ERR_HIP if
+ *         the launch fails.
+ */
+int mixq_mfma_probe(const int8_t *a, int64_t a_bytes, const int8_t *b, int64_t b_bytes,
+                    int32_t iters, int32_t blocks, int32_t *out, int64_t *clk, void *stream);
+
 /* Text of a status code (static storage). */
 const char *mixq_status_string(int status);
 

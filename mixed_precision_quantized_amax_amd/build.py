@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmixq.so")
-SOURCES = ["mixq_api.hip", "mixq_act.hip", "mixq_weight.hip", "mixq_gemm.hip"]
+SOURCES = ["mixq_api.hip", "mixq_act.hip", "mixq_weight.hip", "mixq_gemm.hip", "mixq_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -118,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.mixq_set_clock_record.restype = ctypes.c_int
         L.mixq_set_gemm_variant.argtypes = [I32]
         L.mixq_set_gemm_variant.restype = ctypes.c_int
+        L.mixq_mfma_probe.argtypes = [P, I64, P, I64, I32, I32, P, P, P]
+        L.mixq_mfma_probe.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -159,6 +161,24 @@ def set_gemm_variant(variant: int | str) -> None:
     the automatic choice); for tests that cover each variant."""
     v = GEMM_VARIANTS[variant] if isinstance(variant, str) else int(variant)
     _check("mixq_set_gemm_variant", lib().mixq_set_gemm_variant(v))
+
+
+def mfma_probe(a: torch.Tensor, b: torch.Tensor, iters: int, blocks: int,
+               out: torch.Tensor, clk: torch.Tensor | None = None, stream=None) -> None:
+    """Measurement aid (mixq_mfma_probe): ``blocks`` x 4 waves run ``iters``
+    rounds of the GEMM main loop's 32 INT8 MFMAs on operand bytes taken from
+    ``a`` and ``b`` (int8 device tensors, any shape), with no memory traffic
+    in the timed part.  ``out``: int32 [256 * blocks], each lane's sum of its
+    accumulators; ``clk``: int64 [4 * blocks] clock stamps, or None."""
+    assert a.dtype == torch.int8 and b.dtype == torch.int8 and a.is_contiguous() and b.is_contiguous()
+    assert out.dtype == torch.int32 and out.numel() >= 256 * blocks
+    assert clk is None or (clk.dtype == torch.int64 and clk.numel() >= 4 * blocks)
+    s = stream if stream is not None else torch.cuda.current_stream(a.device).cuda_stream
+    na = a.numel() // 16 * 16
+    nb = b.numel() // 16 * 16
+    _check("mixq_mfma_probe", lib().mixq_mfma_probe(
+        _ptr(a), na, _ptr(b), nb, iters, blocks, _ptr(out),
+        _ptr(clk), ctypes.c_void_p(s)))
 
 
 def set_clock_record(buf: torch.Tensor | None) -> None:

@@ -304,3 +304,20 @@ def test_gemm_ex_valid_arguments_need_a_device():
         assert f(ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
                  ctypes.byref(st), ctypes.byref(wm), 4, ctypes.c_void_p(0x50000), 3000, 0, None,
                  None, 0, None) == 4
+
+
+@pytest.mark.parametrize("args", [
+    (0, 64, 0x2000, 64, 1, 1, 0x3000),            # null a
+    (0x1000, 64, 0, 64, 1, 1, 0x3000),            # null b
+    (0x1000, 64, 0x2000, 64, 1, 1, 0),            # null out
+    (0x1000, 64, 0x2000, 64, 0, 1, 0x3000),       # no rounds
+    (0x1000, 64, 0x2000, 64, 1, 0, 0x3000),       # no blocks
+    (0x1000, 8, 0x2000, 64, 1, 1, 0x3000),        # fewer than 16 bytes
+    (0x1000, 64, 0x2000, 72, 1, 1, 0x3000),       # not a multiple of 16
+    (0x1008, 64, 0x2000, 64, 1, 1, 0x3000),       # unaligned operand
+])
+def test_mfma_probe_validation(args):
+    a, na, b, nb, iters, blocks, out = args
+    rc = mixq.lib().mixq_mfma_probe(ctypes.c_void_p(a), na, ctypes.c_void_p(b), nb, iters, blocks,
+                                    ctypes.c_void_p(out), None, None)
+    assert rc == 1  # MIXQ_ERR_INVALID_ARG
