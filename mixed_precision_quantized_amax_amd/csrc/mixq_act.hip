@@ -405,22 +405,16 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
     __shared__ uint32_t red[2][kRB][W];
     __shared__ double rsum[NORM ? 2 : 1][kRB][W][2];
     __shared__ int any_det;
-    const int set_size = *a.count;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform (a scalar register): the token row and its buffer
+    // descriptor are then scalar too, and each row load issues once (a
+    // descriptor in vector registers needs a loop over its distinct values)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int slot = wave / W, part = wave % W;
     const int seg_chunks = W * kWave * CPT;
     const int nseg = EXACT ? 1 : (a.nchunks + seg_chunks - 1) / seg_chunks;
-    const int kpad = (set_size + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
-    // first gather round: set member gj of each token (its channel id is
-    // read once per block)
-    const int gj = part * kWave + lane;
-    const bool gset = a.ld_out && gj < set_size;
-    const int gch = gset ? a.idx[gj] : 0;
     auto chunk = [&](int s, int i) { return s * seg_chunks + (part * CPT + i) * kWave + lane; };
     auto in_range = [&](int c) __attribute__((always_inline)) { return EXACT || c < a.nchunks; };
-    // gamma of this thread's first gather member (the rest of gamma is in LDS)
-    const uint16_t ggam = (NORM && gset) ? a.gamma[gch] : 0;
     typedef uint4 XV[CPT];
     typedef uint32_t WV[CPT];
     // X chunks of one segment of a token's part (global loads only)
@@ -437,6 +431,28 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
             xv[i] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
+    // The first token's row loads go out before anything else: before the
+    // set size is read (the wait for a scalar load holds back every later
+    // instruction), and before the cached set is staged in LDS, so that the
+    // memory latencies overlap (the set's bits are read from LDS only when
+    // the amax needs them).
+    XV xa, xb;
+    WV wa, wb;
+    uint16_t ga = 0, gb2 = 0;
+    int64_t r0 = (int64_t)blockIdx.x * kRB;
+    if (!RES && r0 < a.M) load_x(r0 + slot, 0, xa);
+    const int set_size = *a.count;
+    const int kpad = (set_size + MIXQ_OUTLIER_ALIGN - 1) / MIXQ_OUTLIER_ALIGN * MIXQ_OUTLIER_ALIGN;
+    // first gather round: set member gj of each token (its channel id is
+    // read once per block)
+    const int gj = part * kWave + lane;
+    const bool gset = a.ld_out && gj < set_size;
+    // Its channel id: a range-checked load over the committed list (lanes
+    // past the set read 0), with no branch around it, so that nothing waits
+    // for it before the row loads go out (a load inside a divergent branch
+    // is waited for where the branch ends).
+    const int gch = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        row_rsrc(a.idx, a.ld_out ? (int64_t)set_size * 4 : 0), gj * 4, 0, 0);
     // the cached-set bits of the same chunks (from the bitmap staged in LDS)
     auto load_bits = [&](int s, WV& wv) {
 #pragma unroll
@@ -449,24 +465,29 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
         load_x(row, s, xv);
         load_bits(s, wv);
     };
+    // a token's first gather value (a range-checked 2-byte load from its
+    // row: 0 for a lane that holds no set member or a row past M, values
+    // that are never stored)
+    auto load_gather = [&](int64_t row, uint16_t& gv) {
+        const bool valid = row < a.M;
+        const __amdgpu_buffer_rsrc_t rx =
+            row_rsrc(a.X + (valid ? row : 0) * a.ldx, valid ? (int64_t)a.K * 2 : 0);
+        gv = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rx, gset ? gch * 2 : a.K * 2, 0, 0);
+    };
     // the first segment of a token's part and its first gather value
     auto load_row = [&](int64_t row, XV& xv, uint16_t& gv) {
         load_x(row, 0, xv);
-        if (gset && row < a.M) gv = a.X[row * a.ldx + gch];
+        load_gather(row, gv);
     };
-    // The first token's loads go out before the cached set is staged in LDS,
-    // so that the two memory latencies overlap (the set's bits are read
-    // from LDS only when the amax needs them).
-    XV xa, xb;
-    WV wa, wb;
-    uint16_t ga = 0, gb2 = 0;
-    int64_t r0 = (int64_t)blockIdx.x * kRB;
-    if (!RES && r0 < a.M) load_row(r0 + slot, xa, ga);
     build_keep_lut(lut);
     for (int w = threadIdx.x; w < a.words; w += kGateThreads) {
         newbits[w] = 0u;
         sbits[w] = a.bitmap[w];
     }
+    // after the set's staging: the channel-id load must have landed first,
+    // and (completions in order) so have the row loads before it, whose
+    // lines then hold this value
+    if (!RES && r0 < a.M) load_gather(r0 + slot, ga);
     if constexpr (NORM) {
         uint4* const g4 = reinterpret_cast<uint4*>(dyn + 2 * a.words);
         for (int c = threadIdx.x; c < a.nchunks; c += kGateThreads)
@@ -529,7 +550,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_quant_kernel(ActArgs a) {
                 if (in_range(c))
                     xv[i] = norm_chunk(xv[i], *reinterpret_cast<const uint4*>(sgam + c * 8), rn);
             }
-            gval = norm1(gval, ggam, rn);
+            gval = norm1(gval, sgam[gch], rn);  // gamma staged in LDS
             if (valid && part == 0 && lane == 0) a.rstd[row] = rn;
         }
 
