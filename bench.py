@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the mixed-precision linear layer on one MI355X.
 
-A step is one pass of the whole layer over one batch: mixq_quantize_act
-(amax, gate, quantize, outlier split), mixq_pack_weight in its
-outlier-column mode (a device-side no-op unless the set changed) and
-mixq_gemm (INT8 x INT8 product, FP16 outlier product, fused epilogue).
+A step is one pass of the whole layer over one batch:
+mixq_quantize_act_regather (amax, gate, quantize, outlier split, and the
+weight's outlier-column regather, a device-side no-op unless the set
+changed; two launches) and mixq_gemm_ws (INT8 x INT8 product, FP16 outlier
+product, fused epilogue).
 Inputs are seeded synthetic tensors already resident in HBM; several copies
 of the inputs and packed weights are rotated so that the 256 MB Infinity
 Cache cannot serve them from one step to the next.
@@ -654,6 +655,59 @@ def traffic_summary(fetch_csv: str, write_csv: str, out_json: str, out_txt: str,
     print("\n".join(lines))
 
 
+def trace_summary(trace_csv: str, out_txt: str):
+    """Per-kernel statistics of a ``rocprofv3 --kernel-trace`` CSV of a
+    bench.py run (calls, mean, min, max, share of GPU time), and the
+    headline GEMM's windows: the default run times the INT8 256 x 256 GEMM
+    with 100 launches under per-launch events, then the same 100 back to
+    back, first rotating the copies (clean cache), then on one copy (hot);
+    each pair shows up as a run of at least 200 consecutive dispatches of
+    that kernel, whose last 100 are the back-to-back launches.  Also the
+    rate probe's back-to-back launches."""
+    import csv
+    rows = []
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            # blocks: grid work-items over workgroup size (one dimension here)
+            blk = (int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+                   if r.get("Grid_Size_X") and r.get("Workgroup_Size_X") else 0)
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                         kernel_short_name(r["Kernel_Name"]), blk))
+    rows.sort()
+    total = sum(e - b for b, e, _, _ in rows)
+    per = {}
+    for b, e, k, g in rows:
+        per.setdefault((k, g), []).append((e - b) / 1e3)
+    lines = ["# kernel | blocks | calls | avg us | min us | max us | % of GPU time"]
+    for (k, g), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k:70s} | {g:6d} | {len(v):5d} | {np.mean(v):9.2f} | {min(v):9.2f} | "
+                     f"{max(v):9.2f} | {100.0 * sum(v) * 1e3 / total:6.2f}")
+    head = "gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>"
+    runs, cur = [], []
+    for b, e, k, _ in rows:
+        if k == head:
+            cur.append((e - b) / 1e3)
+        else:
+            if cur:
+                runs.append(cur)
+            cur = []
+    if cur:
+        runs.append(cur)
+    wins = [r[-100:] for r in runs if len(r) >= 200]
+    for name, w in zip(("clean-cache", "hot-cache"), wins):
+        lines.append(f"# headline GEMM, {name} window: {len(w)} back-to-back dispatches, avg "
+                     f"{np.mean(w):.2f} us, median {np.median(w):.2f}, min {min(w):.2f}, "
+                     f"max {max(w):.2f}")
+    probe = [(e - b) / 1e3 for b, e, k, _ in rows if k.startswith("mfma_probe_kernel")]
+    if len(probe) >= 100:
+        w = probe[-100:]
+        lines.append(f"# rate probe (mixq_mfma_probe, 256 blocks x 128 rounds): last 100 dispatches, "
+                     f"avg {np.mean(w):.2f} us, median {np.median(w):.2f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def run_cpu_baseline(wl, target_s: float = 12.0):
     """The CPU oracle on a row sample of the workload: gate and quantization
     of the sampled tokens, the integer product against all N weight rows, and
@@ -705,6 +759,8 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="byte-counter pass: the calibration copy, then --steps whole steps "
                          "of each counter workload, then the fused RMSNorm passes")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "OUT_TXT"),
+                    help="summarise a rocprofv3 --kernel-trace CSV of a bench.py run")
     ap.add_argument("--traffic-summary", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON", "OUT_TXT"),
                     help="write the GEMM's HBM bytes per launch from two --counters passes")
@@ -715,6 +771,9 @@ def main():
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -99,3 +99,33 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
         bench.gemm_blocks([("a", 1), ("b", 1)], ("x",))
     with pytest.raises(SystemExit):
         bench.gemm_blocks([("a", 1)] * 3, ("x", "y"))
+
+
+def test_trace_summary_windows(tmp_path):
+    """The headline GEMM's clean- and hot-cache windows are the last 100 of
+    each run of at least 200 consecutive dispatches of that kernel; shorter
+    runs (the timed steps, where the activation kernels interleave) are not."""
+    ns = "void mixq::(anonymous namespace)::"
+    g8 = ns + "gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>(mixq::GemmArgs)"
+    gq = ns + "gate_quant_kernel<4, 4, false, false, true, true>(mixq::ActArgs)"
+    pr = ns + "mfma_probe_kernel(signed char const*, signed char const*, long, long, int, int*, long*)"
+    seq = []
+    for i in range(5):                       # steps: act and GEMM interleaved
+        seq += [(gq, 10.0), (g8, 300.0)]
+    seq += [(g8, 140.0)] * 100 + [(g8, 120.0)] * 100    # clean: per-launch events, back to back
+    seq += [(gq, 10.0)]
+    seq += [(g8, 150.0)] * 100 + [(g8, 130.0)] * 100    # hot
+    seq += [(pr, 90.0)] * 50 + [(pr, 80.0)] * 100
+    lines = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for name, us in seq:
+        lines.append(f'"{name}",{t},{t + int(us * 1000)}')
+        t += int(us * 1000) + 500
+    csvp, out = tmp_path / "t.csv", tmp_path / "s.txt"
+    csvp.write_text("\n".join(lines) + "\n")
+    bench.trace_summary(str(csvp), str(out))
+    text = out.read_text()
+    assert "clean-cache window: 100 back-to-back dispatches, avg 120.00 us" in text
+    assert "hot-cache window: 100 back-to-back dispatches, avg 130.00 us" in text
+    assert "last 100 dispatches, avg 80.00 us" in text
+    assert text.splitlines()[1].startswith("gemm_kernel<256, 256, 2, 2, 8, 4, 6, false, false, false>")
