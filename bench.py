@@ -129,6 +129,27 @@ def run_mfma_probe(stream, a, b, iters: int = 128, blocks: int = 256, warmup: in
             "operands": "the workload's own Xq and packed weight bytes"}
 
 
+def run_vendor_int8(stream, Xqs, packs, n: int = 100, warmup: int = 50) -> dict:
+    """The vendor library's plain INT8 GEMM at the same shape, for comparison
+    only: torch._int_mm (hipBLASLt on ROCm) on the same operand bytes (the
+    workload's Xq copies and their INT8 packed weights, rotated like the
+    GEMM's), int32 output, with no quantization, outlier product, scales or
+    fp32 epilogue.  Timed like the GEMM (100 launches back to back)."""
+    import torch
+    try:
+        ops = [(x, p.wq.view(torch.int8).view(p.N, p.K).t()) for x, p in zip(Xqs, packs)]
+        for i in range(warmup):
+            torch._int_mm(*ops[i % len(ops)])
+        t = launch_times(stream, n, lambda i: torch._int_mm(*ops[i % len(ops)]))
+    except Exception as e:  # reported, never fatal for the layer's numbers
+        return {"error": repr(e)}
+    M, K = Xqs[0].shape
+    N = packs[0].N
+    return {"us": t["batch_us"], "median_us": t["median_us"],
+            "tops": round(2.0 * M * N * K / (t["batch_us"] / 1e6) / 1e12, 1),
+            "call": "torch._int_mm (hipBLASLt), int8 x int8 -> int32, same operand bytes"}
+
+
 def gemm_source_sha() -> str:
     with open(GEMM_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -260,9 +281,10 @@ def run_gpu(wl, steps: int, warmup: int, group: int = 0, counters: bool = False,
     act_u = launch_times(stream, nl, lambda i: steps_u[i % copies].act())
     flag = int(state.flag.cpu()[0])
     mprobe = run_mfma_probe(stream, Xq[0], packs[0].wq) if probe else None
+    vendor = run_vendor_int8(stream, Xq, packs) if probe and wl.bits == 8 else None
     return dict(ms_step=ms_step, graph_ms_step=graph_ms_step, gemm=gemm_clean, gemm_hot=gemm_hot,
                 act=act_t, act_separate=act_u, clock=clk, count=count, flag=flag,
-                copies=copies, probe=mprobe)
+                copies=copies, probe=mprobe, vendor=vendor)
 
 
 def run_mixed(wl, steps: int, warmup: int, salient):
@@ -863,6 +885,10 @@ def main():
         out["mfma_probe"] = r["probe"]
         if r["probe"]["ops"] == ops:
             out["roofline"]["frac_of_mfma_probe"] = round(gemm_tops / r["probe"]["tops"], 4)
+    if r.get("vendor") is not None:
+        # the vendor library's plain INT8 GEMM on the same bytes (no outliers,
+        # no dequantization, int32 out): context for the fused kernel's time
+        out["vendor_int8_gemm"] = r["vendor"]
     out["fused_rmsnorm_act"] = run_fused_norm(wl, args.steps, min(args.warmup, 50))
     out["swiglu_gate_up"] = run_swiglu(wl, max(20, args.steps // 2), min(args.warmup, 50))
     others = {}
