@@ -493,11 +493,15 @@ void gemm_kernel(GemmArgs a) {
         if constexpr (PF == 6) {
             // Issue order pinned slot by slot (the scheduler may not move
             // anything across a slot): each of a phase's 32 MFMAs is followed
-            // by at most one LDS read or one LDS write + global load, reads
-            // first (their results are needed right after the phase), the
-            // write/load pairs next, the last eight MFMAs alone -- so the
-            // phase's LDS operations have completed when the barrier's wait
-            // comes and the matrix pipe never idles behind them.
+            // by at most one memory instruction.  The first 16 carry the LDS
+            // reads (their results are needed right after the phase); the
+            // other 16 alternate the 8 LDS writes and the 8 global loads, the
+            // load that refills a staging register one slot after the write
+            // that empties it.  A wave's 16-byte-per-lane LDS write moves
+            // 1 KiB; spread over 16 slots instead of 8 consecutive ones
+            // (each with its load), the writes no longer hold up the MFMA
+            // issue: 1.5-2% less time per launch at the prefill shape, three
+            // boxes, alternating builds, results identical.
             constexpr int kMF = 2 * C::kFM * C::kFN;   // 32 MFMAs per phase
             constexpr int kRD = 2 * (C::kFM + C::kFN); // 16 fragment reads
             static_assert(kMF == 32 && kRD == 16 && kPI == 8, "slot plan for 128x128 waves");
@@ -514,8 +518,11 @@ void gemm_kernel(GemmArgs a) {
                     fb[ks][q - 4] =
                         *reinterpret_cast<const v4i*>(Bb + rdB2[h][ks] + (q - 4) * 32 * kPR);
             };
-            auto wl = [&](Stg& S, uint8_t* buf, const __amdgpu_buffer_rsrc_t& r, int pl, int w) {
+            // staging register w to LDS, and its refill with pair pl's rows
+            auto wo = [&](const Stg& S, uint8_t* buf, int w) {
                 *reinterpret_cast<v4i*>(&buf[wr + w * C::kNW * 8 * kPR]) = S[w];
+            };
+            auto lo = [&](Stg& S, const __amdgpu_buffer_rsrc_t& r, int pl, int w) {
                 S[w] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[w] + (pb + pl) * kPR, 0, 0);
             };
             for (; p + 3 < KP; ++p) {
@@ -524,7 +531,8 @@ void gemm_kernel(GemmArgs a) {
                 for (int t = 0; t < kMF; ++t) {
                     mf(fa0, fb0, t);
                     if (t < kRD) rd(PA(c), PB(c), 1, fa1, fb1, t);
-                    else if (t < kRD + kPI) wl(SB, PB(n), rB, p + 2, t - kRD);
+                    else if (t % 2 == 0) wo(SB, PB(n), (t - kRD) / 2);
+                    else lo(SB, rB, p + 2, (t - kRD) / 2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 __syncthreads();
@@ -532,7 +540,8 @@ void gemm_kernel(GemmArgs a) {
                 for (int t = 0; t < kMF; ++t) {
                     mf(fa1, fb1, t);
                     if (t < kRD) rd(PA(n), PB(n), 0, fa0, fb0, t);
-                    else if (t < kRD + kPI) wl(SA, PA(c), rA, p + 3, t - kRD);
+                    else if (t % 2 == 0) wo(SA, PA(c), (t - kRD) / 2);
+                    else lo(SA, rA, p + 3, (t - kRD) / 2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
